@@ -1,0 +1,221 @@
+"""Block-pool allocator replica (oracle; test infrastructure only).
+
+What the pages fix: blocks of a fixed number of tokens come from one shared
+pool as tokens arrive («¿Cómo gestiona Paged Attention la caché KV…?» "PagedAttention divide el estado KV en bloques
+de tamaño fijo"); each sequence keeps a block table mapping logical order to
+physical blocks («¿Cómo gestiona Paged Attention la caché KV…?»; «PagedAttention e vLLM» "Approfondimento tecnico"; «Paged Attention optimiza el uso de memoria»); the
+runtime keeps reference counts («¿Cómo gestiona Paged Attention la caché KV…?» "La gestión de bloques…"); finished
+requests return their unshared blocks to the pool at once («¿Cómo gestiona Paged Attention la caché KV…?» "Los
+bloques liberados…", «Paged Attention optimiza el uso de memoria»); identical prefixes point at the same blocks
+and a writer copies only the page it would change («PagedAttention e vLLM»; «Paged Attention optimiza el uso de memoria» on
+copy-on-write); release must not free blocks still in use and no request may
+see another's private continuation («Servicio…presupuesto de memoria» §8).
+
+Readings where the pages are silent (each is one of several correct
+choices; the library follows the same ones so allocator state can be
+compared bit for bit):
+
+* free list is a stack: ``init`` pushes the initial order reversed, so pops
+  return ``perm[0], perm[1], ...``; freed blocks are pushed on top;
+* sequence ids start at 0 and are never reused;
+* a batched append serves ids in the order given; a duplicate id in one
+  batch is invalid;
+* the token at position ``pos`` needs a fresh block when ``pos % B == 0``;
+  otherwise, if its block is shared (refcount > 1), the writer takes a fresh
+  block, the shared block loses one reference, and the pair (old, new) is
+  recorded so the whole block's contents can be copied;
+* slot number = block id · B + pos % B;
+* release walks the table in logical order and pushes each block whose
+  count drops to zero;
+* every call is all-or-nothing: on pool exhaustion nothing changes.
+"""
+from __future__ import annotations
+
+import copy
+from typing import Dict, List, Sequence, Tuple
+
+
+class AllocError(Exception):
+    pass
+
+
+class NoBlocks(AllocError):
+    pass
+
+
+class BadSeq(AllocError):
+    pass
+
+
+class Invalid(AllocError):
+    pass
+
+
+class Allocator:
+    def __init__(self, num_blocks: int, block: int = 16, perm: Sequence[int] = None):
+        if num_blocks < 1 or block < 1:
+            raise Invalid("num_blocks and block must be positive")
+        if perm is None:
+            perm = list(range(num_blocks))
+        perm = [int(x) for x in perm]
+        if sorted(perm) != list(range(num_blocks)):
+            raise Invalid("perm must be a permutation of 0..num_blocks-1")
+        self.N = num_blocks
+        self.B = block
+        self.free: List[int] = list(reversed(perm))
+        self.ref: List[int] = [0] * num_blocks
+        self.seqs: Dict[int, Tuple[int, List[int]]] = {}
+        self.next_id = 0
+
+    # -- sequences ---------------------------------------------------------
+    def create(self) -> int:
+        sid = self.next_id
+        self.next_id += 1
+        self.seqs[sid] = (0, [])
+        return sid
+
+    def fork(self, parent: int) -> int:
+        if parent not in self.seqs:
+            raise BadSeq(parent)
+        n, table = self.seqs[parent]
+        for b in table:
+            self.ref[b] += 1
+        sid = self.next_id
+        self.next_id += 1
+        self.seqs[sid] = (n, list(table))
+        return sid
+
+    def free_seq(self, sid: int) -> None:
+        if sid not in self.seqs:
+            raise BadSeq(sid)
+        _, table = self.seqs.pop(sid)
+        for b in table:
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.append(b)
+
+    # -- slot reservation ----------------------------------------------------
+    def _append_one(self, sid: int, cow: List[Tuple[int, int]]) -> int:
+        n, table = self.seqs[sid]
+        pos = n
+        if pos % self.B == 0:
+            if not self.free:
+                raise NoBlocks()
+            b = self.free.pop()
+            self.ref[b] = 1
+            table.append(b)
+        else:
+            last = table[-1]
+            if self.ref[last] > 1:
+                if not self.free:
+                    raise NoBlocks()
+                nb = self.free.pop()
+                self.ref[last] -= 1
+                self.ref[nb] = 1
+                cow.append((last, nb))
+                table[-1] = nb
+        slot = table[pos // self.B] * self.B + pos % self.B
+        self.seqs[sid] = (n + 1, table)
+        return slot
+
+    def _transaction(self, fn):
+        saved = (list(self.free), list(self.ref),
+                 {k: (v[0], list(v[1])) for k, v in self.seqs.items()}, self.next_id)
+        try:
+            return fn()
+        except AllocError:
+            self.free, self.ref, self.seqs, self.next_id = saved
+            raise
+
+    def append(self, ids: Sequence[int]):
+        """One token for each id, in order.  Returns (slots, cow_pairs)."""
+        ids = [int(i) for i in ids]
+        if len(set(ids)) != len(ids):
+            raise Invalid("duplicate id in batch")
+        for i in ids:
+            if i not in self.seqs:
+                raise BadSeq(i)
+
+        def run():
+            cow: List[Tuple[int, int]] = []
+            slots = [self._append_one(i, cow) for i in ids]
+            return slots, cow
+        return self._transaction(run)
+
+    def extend(self, sid: int, k: int):
+        """k successive one-token appends of ``sid``; all-or-nothing."""
+        if sid not in self.seqs:
+            raise BadSeq(sid)
+        if k < 0:
+            raise Invalid("negative count")
+
+        def run():
+            cow: List[Tuple[int, int]] = []
+            slots = [self._append_one(sid, cow) for _ in range(k)]
+            return slots, cow
+        return self._transaction(run)
+
+    # -- inspection ----------------------------------------------------------
+    def length(self, sid: int) -> int:
+        return self.seqs[sid][0]
+
+    def table(self, sid: int) -> List[int]:
+        return list(self.seqs[sid][1])
+
+    def snapshot(self):
+        """(free stack bottom..top, refcounts, [(id, len, table)] by id, next_id)."""
+        return (list(self.free), list(self.ref),
+                [(k, v[0], list(v[1])) for k, v in sorted(self.seqs.items())],
+                self.next_id)
+
+    def stats(self):
+        used = self.N - len(self.free)
+        sum_len = sum(v[0] for v in self.seqs.values())
+        tail = sum(self.B * len(v[1]) - v[0] for v in self.seqs.values())
+        return {"free": len(self.free), "used": used, "sum_len": sum_len,
+                "sum_ref": sum(self.ref), "tail_waste": tail, "num_seqs": len(self.seqs)}
+
+    def check_invariants(self) -> None:
+        """Raise AssertionError if the state breaks a pool invariant."""
+        assert sum(self.ref) == sum(len(t) for _, t in self.seqs.values())
+        live = {b for b in range(self.N) if self.ref[b] > 0}
+        assert len(set(self.free)) == len(self.free)
+        assert live.isdisjoint(self.free)
+        assert live | set(self.free) == set(range(self.N))
+        for b in range(self.N):
+            assert self.ref[b] >= 0
+        counts = [0] * self.N
+        for n, t in self.seqs.values():
+            assert len(t) == -(-n // self.B)
+            assert 0 <= self.B * len(t) - n <= self.B - 1 or n == 0
+            for b in t:
+                counts[b] += 1
+        assert counts == self.ref
+
+    def clone(self) -> "Allocator":
+        return copy.deepcopy(self)
+
+
+def run_script(alloc: Allocator, ops, on_slots=None):
+    """Execute a workload script.  ``on_slots(op, sid_or_ids, slots, cow)`` is
+    called after each extend/append so a caller can write values.  Errors
+    from the allocator propagate."""
+    for op in ops:
+        kind = op[0]
+        if kind == "create":
+            alloc.create()
+        elif kind == "fork":
+            alloc.fork(op[1])
+        elif kind == "free":
+            alloc.free_seq(op[1])
+        elif kind == "extend":
+            slots, cow = alloc.extend(op[1], op[2])
+            if on_slots:
+                on_slots(op, op[1], slots, cow)
+        elif kind == "append":
+            ids = [e[0] for e in op[1]]
+            slots, cow = alloc.append(ids)
+            if on_slots:
+                on_slots(op, ids, slots, cow)
+        else:
+            raise ValueError(kind)

@@ -1,0 +1,106 @@
+"""Exact decode attention in fp64 (oracle; test infrastructure only).
+
+«Servicio…presupuesto de memoria» §6 ("La atención exacta sigue teniendo un contrato numérico"): dense
+attention forms scaled query-key scores, applies softmax and weights the
+values; an IO-aware implementation may process blocks while carrying running
+normalisation statistics, which changes the evaluation order, not the
+operation.  «¿Cuánta memoria reservar para la caché KV?» ("Emplear las cabezas KV, en particular con GQA"): with
+grouped-query attention several query heads share one KV head (e.g. 40 query
+heads over 8 KV heads, five per group); the cache stores KV heads only.
+
+Readings (where the pages are silent):
+* score scale: 1/sqrt(d) by default, passed in explicitly;
+* query head h uses KV head floor(h / G), G = Hq / Hkv (contiguous groups,
+  the repeat-interleave convention);
+* decode attends over every stored token of the sequence, the one just
+  appended included; a sequence needs at least one token.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .pool import Pool, to_f64
+
+
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """softmax(q Kᵀ · scale) V for query rows q [G][d], keys/values [n][d]."""
+    X = (q @ K.T) * scale
+    X = X - X.max(axis=1, keepdims=True)
+    P = np.exp(X)
+    return (P @ V) / P.sum(axis=1, keepdims=True)
+
+
+def attend_online(q, K, V, scale: float, chunk: int) -> np.ndarray:
+    """The same result computed chunk by chunk with running statistics:
+    per query row a running maximum m, running sum l and an unnormalised
+    accumulator, rescaled whenever the maximum grows («Servicio…presupuesto de memoria» §6, §9)."""
+    G, d = q.shape
+    m = np.full((G, 1), -np.inf)
+    l = np.zeros((G, 1))
+    acc = np.zeros((G, V.shape[1]))
+    for lo in range(0, K.shape[0], chunk):
+        X = (q @ K[lo:lo + chunk].T) * scale
+        m_new = np.maximum(m, X.max(axis=1, keepdims=True))
+        alpha = np.exp(m - m_new)
+        P = np.exp(X - m_new)
+        l = l * alpha + P.sum(axis=1, keepdims=True)
+        acc = acc * alpha + P @ V[lo:lo + chunk]
+        m = m_new
+    return acc / l
+
+
+def partial_stats(q, K, V, scale: float):
+    """(m, l, acc) of one partition: max score, sum of exp(score - m) and the
+    unnormalised exp-weighted value sum."""
+    X = (q @ K.T) * scale
+    m = X.max(axis=1, keepdims=True)
+    P = np.exp(X - m)
+    return m, P.sum(axis=1, keepdims=True), P @ V
+
+
+def merge_stats(parts) -> np.ndarray:
+    """Combine per-partition (m, l, acc): rescale every partition to the
+    common maximum, then divide the summed accumulators by the summed sums."""
+    M = np.max(np.concatenate([p[0] for p in parts], axis=1), axis=1, keepdims=True)
+    L = sum(p[1] * np.exp(p[0] - M) for p in parts)
+    A = sum(p[2] * np.exp(p[0] - M) for p in parts)
+    return A / L
+
+
+def attend_split(q, K, V, scale: float, part: int) -> np.ndarray:
+    """Split the keys into partitions of ``part`` tokens, summarise each
+    independently and merge the summaries."""
+    parts = [partial_stats(q, K[lo:lo + part], V[lo:lo + part], scale)
+             for lo in range(0, K.shape[0], part)]
+    return merge_stats(parts)
+
+
+def decode(pool: Pool, layer: int, tables, lengths, q: np.ndarray, Hq: int,
+           scale: float = None, heads=None) -> np.ndarray:
+    """out[s][h] = attention of query head h of sequence s over the sequence's
+    gathered keys/values of KV head floor(h/G).
+
+    ``q`` is float64 [S][Hq][d] (already upcast).  ``heads`` optionally limits
+    the (s, h) pairs computed; others are left NaN.
+    """
+    S = len(lengths)
+    d = pool.d
+    G = Hq // pool.Hkv
+    if Hq % pool.Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = np.full((S, Hq, d), np.nan)
+    for s in range(S):
+        n = int(lengths[s])
+        if n < 1:
+            raise ValueError("a sequence needs at least one token")
+        for g in range(pool.Hkv):
+            hs = [h for h in range(g * G, (g + 1) * G) if heads is None or (s, h) in heads]
+            if not hs:
+                continue
+            Kc, Vc = pool.gather(layer, tables[s], n, g)
+            out[s, hs] = attend(q[s, hs], Kc, Vc, scale)
+    return out

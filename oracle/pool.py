@@ -1,0 +1,97 @@
+"""Physical K/V pool in the library's byte layout (oracle; test infrastructure).
+
+«¿Cómo gestiona Paged Attention la caché KV…?» ("PagedAttention divide el estado KV…"): K/V blocks may sit anywhere
+in physical memory; a per-sequence block table maps the request's logical
+token order onto them, and the model still attends over the right sequence —
+the indirection moves data, it does not change its meaning.  «PagedAttention e vLLM»
+("Approfondimento tecnico"): each page holds the keys and values of a fixed
+number of tokens.
+
+Layout (the library's documented format, restated here with NumPy indexing;
+B = tokens per block, x = 16 bytes / element size, so x = 4 for fp32 and 8
+for bf16):
+
+* K of layer l: ``K[l][block][head][d // x][B][x]`` — element ``j`` of
+  token slot ``o`` sits at ``[block][head][j // x][o][j % x]``;
+* V of layer l: ``V[l][block][head][d][B]`` — element ``j`` of slot ``o``
+  sits at ``[block][head][j][o]``.
+
+Values are stored as raw bit patterns (uint32 for fp32, uint16 for bf16) so
+that the pool can be compared bit for bit.  Slots nothing has written hold a
+quiet-NaN poison pattern.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+POISON = {"f32": np.uint32(0x7FC00000), "bf16": np.uint16(0x7FC0)}
+BITS = {"f32": np.uint32, "bf16": np.uint16}
+
+
+def to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact upcast of stored bit patterns to float64."""
+    if dtype == "f32":
+        return np.ascontiguousarray(bits, dtype=np.uint32).view(np.float32).astype(np.float64)
+    if dtype == "bf16":
+        wide = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return wide.view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+class Pool:
+    def __init__(self, num_blocks: int, Hkv: int, d: int, dtype: str, block: int = 16,
+                 layers: int = 1, lazy_layers: bool = False):
+        self.N, self.Hkv, self.d, self.dtype, self.B = num_blocks, Hkv, d, dtype, block
+        self.itemsize = 4 if dtype == "f32" else 2
+        self.x = 16 // self.itemsize
+        if d % self.x:
+            raise ValueError("head dim must be a multiple of 16 bytes")
+        self.layers = layers
+        self.K = [None] * layers
+        self.V = [None] * layers
+        if not lazy_layers:
+            for l in range(layers):
+                self._materialize(l)
+
+    def _materialize(self, l: int) -> None:
+        if self.K[l] is None:
+            self.K[l] = np.full((self.N, self.Hkv, self.d // self.x, self.B, self.x),
+                                POISON[self.dtype], dtype=BITS[self.dtype])
+            self.V[l] = np.full((self.N, self.Hkv, self.d, self.B),
+                                POISON[self.dtype], dtype=BITS[self.dtype])
+
+    def scatter(self, layer: int, slots, k_bits: np.ndarray, v_bits: np.ndarray) -> None:
+        """Write token i's K/V ([Hkv][d] bit patterns) into ``slots[i]``."""
+        self._materialize(layer)
+        K, V = self.K[layer], self.V[layer]
+        for i, slot in enumerate(slots):
+            b, o = divmod(int(slot), self.B)
+            K[b, :, :, o, :] = k_bits[i].reshape(self.Hkv, self.d // self.x, self.x)
+            V[b, :, :, o] = v_bits[i]
+
+    def copy_block(self, src: int, dst: int) -> None:
+        """Copy-on-write: block ``dst`` becomes a copy of ``src`` in every layer."""
+        for l in range(self.layers):
+            if self.K[l] is not None:
+                self.K[l][dst] = self.K[l][src]
+                self.V[l][dst] = self.V[l][src]
+
+    def gather(self, layer: int, table, n: int, head: int):
+        """Contiguous fp64 (K [n][d], V [n][d]) of one sequence and KV head:
+        logical token t comes from block ``table[t // B]``, slot ``t % B``."""
+        self._materialize(layer)
+        nblk = -(-n // self.B)
+        blocks = np.asarray(table[:nblk], dtype=np.int64)
+        kb = self.K[layer][blocks, head]                 # [nblk][d/x][B][x]
+        kb = kb.transpose(0, 2, 1, 3).reshape(nblk * self.B, self.d)
+        vb = self.V[layer][blocks, head]                 # [nblk][d][B]
+        vb = vb.transpose(0, 2, 1).reshape(nblk * self.B, self.d)
+        return to_f64(kb[:n], self.dtype), to_f64(vb[:n], self.dtype)
+
+    def valid_mask(self, tables, lengths) -> np.ndarray:
+        """Boolean [N][B]: slots that hold a token of some listed sequence."""
+        m = np.zeros((self.N, self.B), dtype=bool)
+        for table, n in zip(tables, lengths):
+            for t in range(int(n)):
+                m[table[t // self.B], t % self.B] = True
+        return m

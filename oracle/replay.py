@@ -1,0 +1,59 @@
+"""Run a workload script through the oracle allocator and pool (test infra).
+
+The workload object only supplies inputs (script, initial free order, shapes,
+logical per-sequence K/V values).  Here the oracle's own allocator decides
+every slot, its own pool receives the values, copy-on-write pairs are copied
+before the new token is written, and the decode inputs (tables, lengths)
+are read back from the oracle's own state.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .allocator import Allocator, run_script
+from .pool import Pool
+
+
+class Replay:
+    def __init__(self, wl, layers=None):
+        self.wl = wl
+        self.alloc = Allocator(wl.num_blocks, wl.block, wl.perm)
+        n_layers = wl.layers if layers is None else layers
+        self.pool = Pool(wl.num_blocks, wl.Hkv, wl.d, wl.dtype, wl.block, layers=n_layers,
+                         lazy_layers=True)
+        self.log = []          # (op kind, ids, slots, cow pairs) per extend/append
+
+    def run(self, ops, values=None):
+        """Execute ``ops``; ``values`` maps layer -> (k_bits, v_bits) logical
+        arrays [sum n][Hkv][d]; every listed layer receives the tokens."""
+        offs = self.wl.offsets
+        values = values or {}
+
+        def on_slots(op, ids, slots, cow):
+            self.log.append((op[0], ids, list(slots), list(cow)))
+            for a, b in cow:
+                self.pool.copy_block(a, b)
+            if op[0] == "extend":
+                _, sid, k, src, pos = op
+                rows = np.arange(offs[src] + pos, offs[src] + pos + k)
+            else:
+                rows = np.array([offs[src] + pos for (_, src, pos) in op[1]], dtype=np.int64)
+            for layer, (kb, vb) in values.items():
+                self.pool.scatter(layer, slots, kb[rows], vb[rows])
+
+        run_script(self.alloc, ops, on_slots)
+        return self
+
+    def tables(self):
+        return [self.alloc.table(sid) for sid in self.wl.seq_ids]
+
+    def lengths(self):
+        return [self.alloc.length(sid) for sid in self.wl.seq_ids]
+
+    def padded_tables(self, max_blocks=None, pad=-1):
+        t = self.tables()
+        mb = max_blocks or max(len(x) for x in t)
+        arr = np.full((len(t), mb), pad, dtype=np.int32)
+        for i, row in enumerate(t):
+            arr[i, :len(row)] = row
+        return arr
