@@ -1,0 +1,220 @@
+/*
+ * pkv — paged KV cache and paged decode attention for AMD MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes only.  Every function returns an int
+ * status (PKV_OK = 0, negative on failure); no C++ exception crosses this
+ * boundary.  pkv_last_error() gives a thread-local message for the last
+ * failure on the calling thread.
+ *
+ * Sources of the operations (page titles; sections as printed on them):
+ *  - «¿Cómo gestiona Paged Attention la caché KV…?», "PagedAttention divide
+ *    el estado KV en bloques de tamaño fijo": blocks come from one shared
+ *    pool as tokens arrive; a block table maps logical token order to
+ *    physical blocks; the indirection moves data without changing meaning.
+ *    "Los bloques liberados regresan…": finished requests return unshared
+ *    blocks to the pool at once.  "La gestión de bloques…": the runtime keeps
+ *    block tables, reference counts and attention kernels for paged layouts.
+ *  - «PagedAttention e vLLM», "Approfondimento tecnico": fixed-size pages
+ *    holding keys and values of a fixed number of tokens; one block table per
+ *    sequence; identical prefixes share pages by copy-on-write.
+ *  - «Paged Attention optimiza el uso de memoria»: 16-token pages allocated
+ *    on demand; copy-on-write copies only the diverging page.
+ *  - «Servicio…presupuesto de memoria» §6: exact attention = scaled
+ *    query-key scores, softmax, weighted values, computable blockwise with
+ *    running normalisation statistics.  §8: release must not free pages in
+ *    use; no request may see another's private continuation.
+ *  - «¿Cuánta memoria reservar para la caché KV?», "Emplear las cabezas KV":
+ *    grouped-query attention, several query heads per KV head.
+ *
+ * Ownership: all device memory (per-layer K/V pools, q, out, block tables,
+ * sequence lengths, slot mappings, workspace) belongs to the caller; the
+ * library keeps raw pointers and never frees them.  Host allocator state is
+ * owned by the opaque pkv_pool.  Device work is enqueued on the caller's HIP
+ * stream (a hipStream_t passed as void*, NULL = the null stream); no call
+ * waits for the device except where stated.  A pkv_pool is not thread-safe:
+ * the caller serialises calls on one pool.
+ *
+ * Pool byte layout of one layer (B = block_size tokens, x = 16 / element
+ * size, i.e. 4 for fp32 and 8 for bf16; d must be a multiple of x):
+ *   K: [num_blocks][num_kv_heads][d / x][B][x]
+ *   V: [num_blocks][num_kv_heads][d][B]
+ * Slot number s names block s / B, token offset s % B.  One block id
+ * addresses the same token range in every layer's pool.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define PKV_OK               0
+#define PKV_ERR_INVALID     -1  /* bad argument or shape                      */
+#define PKV_ERR_NO_BLOCKS   -2  /* pool exhausted; nothing was changed        */
+#define PKV_ERR_BAD_SEQ     -3  /* unknown or already freed sequence id       */
+#define PKV_ERR_HIP         -4  /* a HIP runtime call failed                  */
+#define PKV_ERR_UNSUPPORTED -5  /* valid, but no kernel for this shape        */
+
+/* ---- element types ----------------------------------------------------- */
+#define PKV_F32  0
+#define PKV_BF16 1
+
+/* Name of a status code (static string). */
+const char* pkv_status_string(int status);
+/* Message describing the last failure on this thread ("" if none). */
+const char* pkv_last_error(void);
+/* Library version, major * 10000 + minor * 100 + patch. */
+int pkv_version(void);
+
+/* ---- pool and allocator ------------------------------------------------ */
+typedef struct pkv_pool pkv_pool;
+
+typedef struct pkv_pool_desc {
+  int32_t num_layers;      /* >= 1                                          */
+  int32_t num_kv_heads;    /* Hkv >= 1                                      */
+  int32_t head_dim;        /* d, multiple of 16 bytes / element size        */
+  int32_t block_size;      /* B tokens per block (16 for the kernels)       */
+  int32_t num_blocks;      /* pool capacity in blocks, >= 1                 */
+  int32_t dtype;           /* PKV_F32 or PKV_BF16                           */
+  void* const* k_cache;    /* [num_layers] device pointers, or NULL for an  */
+  void* const* v_cache;    /*   allocator-only pool (no device calls)       */
+  const int32_t* init_perm;/* optional host [num_blocks] permutation: the   */
+                           /*   free list hands out init_perm[0], [1], ...  */
+} pkv_pool_desc;
+
+/* Create a pool.  The descriptor's arrays are copied.  Free list starts with
+ * every block (in init_perm order, or 0, 1, 2, ...); reference counts 0.    */
+int pkv_pool_create(const pkv_pool_desc* desc, pkv_pool** out);
+/* Destroy a pool (waits for its last table upload to finish).  NULL is ok. */
+int pkv_pool_destroy(pkv_pool* pool);
+
+/* New empty sequence.  Ids start at 0, increase by one, are never reused. */
+int pkv_seq_create(pkv_pool* pool, int64_t* seq_id);
+/* New sequence sharing every block of `parent` (each block's reference count
+ * +1), with the parent's length.                                            */
+int pkv_seq_fork(pkv_pool* pool, int64_t parent, int64_t* child);
+/* Release a sequence: walk its table in logical order, decrement each
+ * block's count and push blocks that reach 0 onto the free list.           */
+int pkv_seq_free(pkv_pool* pool, int64_t seq_id);
+
+/* Reserve `ntok` >= 0 consecutive slots for one sequence (bulk prefill).
+ * slots_out: host int32[ntok].  cow_pairs_out: host int32[2] receiving at
+ * most one (src, dst) block pair; *n_cow gets the count (0 or 1).
+ * All-or-nothing: PKV_ERR_NO_BLOCKS leaves the pool unchanged.             */
+int pkv_seq_extend(pkv_pool* pool, int64_t seq_id, int32_t ntok, int32_t* slots_out,
+                   int32_t* cow_pairs_out, int32_t* n_cow);
+
+/* Reserve one slot for each of `n` distinct ids, in array order (the decode
+ * step).  For the token at position pos = current length:
+ *   pos % B == 0            -> pop a free block, count 1, append to table;
+ *   else, last block count>1 -> pop a free block (count 1), the shared block
+ *                              loses one reference, (old, new) is recorded
+ *                              and replaces the table's last entry;
+ *   slot = table[pos / B] * B + pos % B; length += 1.
+ * slots_out: host int32[n].  cow_pairs_out: host int32[2 * n] receiving
+ * (src, dst) pairs in order; *n_cow their count.  Recorded pairs must be
+ * copied (pkv_copy_blocks) before the new tokens are written.  Duplicate ids
+ * are PKV_ERR_INVALID.  All-or-nothing.                                    */
+int pkv_append_slots(pkv_pool* pool, const int64_t* ids, int32_t n, int32_t* slots_out,
+                     int32_t* cow_pairs_out, int32_t* n_cow);
+
+/* Current length of a sequence. */
+int pkv_seq_length(const pkv_pool* pool, int64_t seq_id, int32_t* len);
+/* Host copy of a sequence's block table: writes min(cap, nblocks) entries to
+ * table_out and the table length to *nblocks.                              */
+int pkv_seq_table(const pkv_pool* pool, int64_t seq_id, int32_t* table_out, int32_t cap,
+                  int32_t* nblocks);
+
+/* Upload the block tables and lengths of `n` sequences to caller-owned
+ * device arrays: dev_block_tables int32[n][max_blocks] (row i = ids[i],
+ * unused entries -1) and dev_seq_lens int32[n].  Asynchronous on `stream`
+ * through a pinned staging buffer owned by the pool; the next call waits
+ * for the previous upload before reusing it.  PKV_ERR_INVALID if a
+ * sequence holds more than max_blocks blocks.                              */
+int pkv_sync_tables(pkv_pool* pool, const int64_t* ids, int32_t n, int32_t* dev_block_tables,
+                    int32_t max_blocks, int32_t* dev_seq_lens, void* stream);
+
+/* Copy-on-write copy: for each host pair (src, dst) in pairs[2 * n_pairs],
+ * block dst := block src in K and V of every layer (all heads, all slots).
+ * Runs one kernel on `stream`.                                             */
+int pkv_copy_blocks(pkv_pool* pool, const int32_t* pairs, int32_t n_pairs, void* stream);
+
+/* Write new tokens of one layer: token i's K and V (device, contiguous
+ * [n][num_kv_heads][head_dim] in the pool dtype) go to slot
+ * dev_slot_mapping[i] (device int32[n]).  Slots outside the pool are
+ * skipped.  Runs one kernel on `stream`.                                   */
+int pkv_kv_append(pkv_pool* pool, int32_t layer, const void* k_new, const void* v_new,
+                  const int32_t* dev_slot_mapping, int32_t n, void* stream);
+
+typedef struct pkv_stats {
+  int64_t num_blocks, free_blocks, used_blocks;
+  int64_t num_seqs, sum_len, sum_ref, tail_waste;
+} pkv_stats;
+int pkv_pool_stats(const pkv_pool* pool, pkv_stats* out);
+
+/* Allocator state for exact comparison.  First call with NULL arrays to get
+ * the sizes (*n_free, *n_seqs, *n_entries = total table entries), then with
+ * arrays of those sizes: free_out[n_free] (stack, bottom to top),
+ * ref_out[num_blocks], ids_out[n_seqs] (ascending), lens_out[n_seqs],
+ * table_off_out[n_seqs + 1] (row i = tables_out[off[i] .. off[i+1])),
+ * tables_out[n_entries], *next_id.  Host only.                             */
+int pkv_pool_snapshot(const pkv_pool* pool, int32_t* free_out, int32_t* ref_out,
+                      int64_t* ids_out, int32_t* lens_out, int64_t* table_off_out,
+                      int32_t* tables_out, int64_t* n_free, int64_t* n_seqs,
+                      int64_t* n_entries, int64_t* next_id);
+
+/* ---- paged decode attention --------------------------------------------
+ * For each sequence s (length n = seq_lens[s]) and query head h, with
+ * G = Hq / Hkv and KV head g = h / G:
+ *   out[s][h] = sum_t softmax_t(scale * q[s][h] . K_s[t]) V_s[t],
+ *   K_s[t] = K[block_tables[s][t / B]][g][token t % B], same for V,
+ * accumulated in fp32, rounded to the q/out dtype (nearest even).
+ * Tokens are split into partitions of `partition` tokens (split-K); a
+ * sequence with more than one partition writes fp32 partial results
+ * (running max, running sum, unnormalised accumulator) to the workspace and
+ * a reduce kernel merges them.  Sequences with n < 1, n > max_seq_len or a
+ * block id outside [0, num_blocks) get NaN rows (the kernels read nothing
+ * outside the pool).  Supported: block_size 16, head_dim 64 or 128, any
+ * Hq multiple of Hkv.                                                      */
+typedef struct pkv_decode_args {
+  const void* q;              /* device [S][Hq][d], pool dtype              */
+  void* out;                  /* device [S][Hq][d], pool dtype              */
+  const void* k_cache;        /* device, one layer, layout above            */
+  const void* v_cache;
+  const int32_t* block_tables;/* device [S][max_blocks]                     */
+  const int32_t* seq_lens;    /* device [S]                                 */
+  void* workspace;            /* device, >= pkv_decode_workspace_bytes(...) */
+  size_t workspace_bytes;
+  int32_t num_seqs;           /* S >= 1                                     */
+  int32_t num_q_heads;        /* Hq                                         */
+  int32_t num_kv_heads;       /* Hkv, divides Hq                            */
+  int32_t head_dim;           /* d                                          */
+  int32_t block_size;         /* B                                          */
+  int32_t num_blocks;         /* pool capacity (bounds check)               */
+  int32_t max_blocks;         /* row stride of block_tables                 */
+  int32_t max_seq_len;        /* upper bound of seq_lens (sizes the grid)   */
+  int32_t partition;          /* tokens per split-K partition, multiple of  */
+                              /*   32; 0 = 512                              */
+  int32_t dtype;              /* PKV_F32 or PKV_BF16                        */
+  float scale;                /* score scale, e.g. 1/sqrt(d)                */
+} pkv_decode_args;
+
+/* Workspace bytes the decode call needs (0 when one partition suffices). */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_seq_len, int32_t partition);
+/* Partial kernel followed, when max_seq_len exceeds one partition, by the
+ * reduce kernel; both on `stream`.                                        */
+int pkv_paged_attention_decode(const pkv_decode_args* args, void* stream);
+/* The partial kernel alone (single-partition sequences are finished here). */
+int pkv_paged_decode_partial(const pkv_decode_args* args, void* stream);
+/* The reduce kernel alone (no-op when one partition suffices). */
+int pkv_paged_decode_reduce(const pkv_decode_args* args, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PKV_H */

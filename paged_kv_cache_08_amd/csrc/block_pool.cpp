@@ -1,0 +1,171 @@
+// Host-side block allocator (see block_pool.hpp for the sources and choices).
+#include "block_pool.hpp"
+
+#include <algorithm>
+#include <unordered_set>
+
+namespace pkv {
+
+BlockPool::BlockPool(int32_t num_blocks, int32_t block_size, const int32_t* init_perm)
+    : num_blocks_(num_blocks), block_(block_size), ref_(num_blocks, 0) {
+  free_.resize(num_blocks);
+  // The stack's top (back) is handed out first, so store the order reversed.
+  for (int32_t i = 0; i < num_blocks; ++i) {
+    const int32_t b = init_perm ? init_perm[i] : i;
+    free_[num_blocks - 1 - i] = b;
+  }
+}
+
+Status BlockPool::create(int64_t* id) {
+  const int64_t sid = next_id_++;
+  seqs_.emplace(sid, Sequence{});
+  *id = sid;
+  return Status::Ok;
+}
+
+Status BlockPool::fork(int64_t parent, int64_t* child) {
+  auto it = seqs_.find(parent);
+  if (it == seqs_.end()) {
+    err_ = "fork: unknown sequence id " + std::to_string(parent);
+    return Status::BadSeq;
+  }
+  Sequence copy = it->second;
+  for (int32_t b : copy.table) ref_[b] += 1;
+  const int64_t sid = next_id_++;
+  seqs_.emplace(sid, std::move(copy));
+  *child = sid;
+  return Status::Ok;
+}
+
+Status BlockPool::release(int64_t id) {
+  auto it = seqs_.find(id);
+  if (it == seqs_.end()) {
+    err_ = "free: unknown sequence id " + std::to_string(id);
+    return Status::BadSeq;
+  }
+  for (int32_t b : it->second.table) {
+    if (--ref_[b] == 0) free_.push_back(b);
+  }
+  seqs_.erase(it);
+  return Status::Ok;
+}
+
+int32_t BlockPool::pop_free() {
+  const int32_t b = free_.back();
+  free_.pop_back();
+  return b;
+}
+
+int32_t BlockPool::take_slot(Sequence& seq, int32_t* cow, int32_t* n_cow) {
+  const int32_t pos = seq.len;
+  const int32_t off = pos % block_;
+  if (off == 0) {
+    const int32_t b = pop_free();
+    ref_[b] = 1;
+    seq.table.push_back(b);
+  } else {
+    const int32_t shared = seq.table.back();
+    if (ref_[shared] > 1) {
+      const int32_t b = pop_free();
+      ref_[shared] -= 1;
+      ref_[b] = 1;
+      cow[2 * *n_cow] = shared;
+      cow[2 * *n_cow + 1] = b;
+      *n_cow += 1;
+      seq.table.back() = b;
+    }
+  }
+  seq.len = pos + 1;
+  return seq.table[pos / block_] * block_ + off;
+}
+
+Status BlockPool::extend(int64_t id, int32_t k, int32_t* slots, int32_t* cow, int32_t* n_cow) {
+  *n_cow = 0;
+  if (k < 0) {
+    err_ = "extend: negative token count";
+    return Status::Invalid;
+  }
+  auto it = seqs_.find(id);
+  if (it == seqs_.end()) {
+    err_ = "extend: unknown sequence id " + std::to_string(id);
+    return Status::BadSeq;
+  }
+  Sequence& seq = it->second;
+  if (static_cast<int64_t>(seq.len) + k > INT32_MAX / 2) {
+    err_ = "extend: sequence length overflow";
+    return Status::Invalid;
+  }
+  // Blocks needed: one per block boundary crossed, plus one copy if the
+  // first token lands in a shared partial block.
+  int64_t need = 0;
+  const int32_t first = seq.len;
+  if (k > 0) {
+    if (first % block_ != 0 && ref_[seq.table.back()] > 1) need += 1;
+    const int32_t last = first + k - 1;
+    // positions p in [first, last] with p % B == 0
+    need += last / block_ - (first + block_ - 1) / block_ + 1;
+  }
+  if (need > static_cast<int64_t>(free_.size())) {
+    err_ = "extend: pool exhausted (need " + std::to_string(need) + " blocks, " +
+           std::to_string(free_.size()) + " free)";
+    return Status::NoBlocks;
+  }
+  for (int32_t i = 0; i < k; ++i) slots[i] = take_slot(seq, cow, n_cow);
+  return Status::Ok;
+}
+
+Status BlockPool::append(const int64_t* ids, int32_t n, int32_t* slots, int32_t* cow,
+                         int32_t* n_cow) {
+  *n_cow = 0;
+  if (n < 0) {
+    err_ = "append: negative batch size";
+    return Status::Invalid;
+  }
+  std::unordered_set<int64_t> seen;
+  seen.reserve(static_cast<size_t>(n) * 2);
+  std::vector<Sequence*> seq(n);
+  for (int32_t i = 0; i < n; ++i) {
+    if (!seen.insert(ids[i]).second) {
+      err_ = "append: duplicate id " + std::to_string(ids[i]) + " in batch";
+      return Status::Invalid;
+    }
+    auto it = seqs_.find(ids[i]);
+    if (it == seqs_.end()) {
+      err_ = "append: unknown sequence id " + std::to_string(ids[i]);
+      return Status::BadSeq;
+    }
+    seq[i] = &it->second;
+  }
+  // Dry run over reference counts: the batch's copy-on-write decisions can
+  // depend on earlier entries of the same batch (two sharers of one block).
+  std::unordered_map<int32_t, int32_t> dec;
+  int64_t need = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const Sequence& s = *seq[i];
+    if (s.len % block_ == 0) {
+      need += 1;
+    } else {
+      const int32_t b = s.table.back();
+      auto d = dec.find(b);
+      const int32_t r = ref_[b] - (d == dec.end() ? 0 : d->second);
+      if (r > 1) {
+        need += 1;
+        dec[b] += 1;
+      }
+    }
+  }
+  if (need > static_cast<int64_t>(free_.size())) {
+    err_ = "append: pool exhausted (need " + std::to_string(need) + " blocks, " +
+           std::to_string(free_.size()) + " free)";
+    return Status::NoBlocks;
+  }
+  for (int32_t i = 0; i < n; ++i) slots[i] = take_slot(*seq[i], cow, n_cow);
+  return Status::Ok;
+}
+
+const Sequence* BlockPool::find(int64_t id) const {
+  auto it = seqs_.find(id);
+  return it == seqs_.end() ? nullptr : &it->second;
+}
+
+}  // namespace pkv

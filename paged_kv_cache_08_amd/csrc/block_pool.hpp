@@ -1,0 +1,73 @@
+// Host-side block allocator of the paged KV cache (no HIP dependency).
+//
+// «¿Cómo gestiona Paged Attention la caché KV…?», "PagedAttention divide el
+// estado KV en bloques de tamaño fijo": fixed-size blocks come from one
+// shared pool as a request's tokens arrive, and a per-request table maps
+// logical order onto them.  "Los bloques liberados regresan…": a finished
+// request's unshared blocks go back to the pool at once.  «PagedAttention e
+// vLLM», "Approfondimento tecnico", and «Paged Attention optimiza el uso de
+// memoria» (copy-on-write paragraph): identical prefixes point at the same
+// pages; a writer copies only the page it would change.  «Servicio…
+// presupuesto de memoria» §8: release drops references without freeing
+// pages still in use.
+//
+// Choices where the pages leave freedom (any free block is a correct pick):
+// the free list is a stack (initial order handed out first, freed blocks
+// reused first); ids count up from 0; a batch is served in array order; a
+// release walks the table in logical order; every mutating call is
+// all-or-nothing, checked before anything changes.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+namespace pkv {
+
+enum class Status : int { Ok = 0, Invalid = -1, NoBlocks = -2, BadSeq = -3 };
+
+struct Sequence {
+  int32_t len = 0;
+  std::vector<int32_t> table;
+};
+
+class BlockPool {
+ public:
+  BlockPool(int32_t num_blocks, int32_t block_size, const int32_t* init_perm);
+
+  int32_t num_blocks() const { return num_blocks_; }
+  int32_t block_size() const { return block_; }
+
+  Status create(int64_t* id);
+  Status fork(int64_t parent, int64_t* child);
+  Status release(int64_t id);
+  // k slots for one sequence; at most one copy-on-write pair.
+  Status extend(int64_t id, int32_t k, int32_t* slots, int32_t* cow, int32_t* n_cow);
+  // one slot per id, in order.
+  Status append(const int64_t* ids, int32_t n, int32_t* slots, int32_t* cow, int32_t* n_cow);
+
+  const Sequence* find(int64_t id) const;
+  const std::vector<int32_t>& free_stack() const { return free_; }
+  const std::vector<int32_t>& refcounts() const { return ref_; }
+  const std::unordered_map<int64_t, Sequence>& sequences() const { return seqs_; }
+  int64_t next_id() const { return next_id_; }
+  const std::string& error() const { return err_; }
+
+ private:
+  // Takes the next block for `seq`'s token at its current length, copying a
+  // shared partial block when needed; returns the slot.  Callers have
+  // already checked that enough free blocks exist.
+  int32_t take_slot(Sequence& seq, int32_t* cow, int32_t* n_cow);
+  int32_t pop_free();
+
+  int32_t num_blocks_;
+  int32_t block_;
+  std::vector<int32_t> free_;    // stack: back() is the next block handed out
+  std::vector<int32_t> ref_;
+  std::unordered_map<int64_t, Sequence> seqs_;
+  int64_t next_id_ = 0;
+  std::string err_;
+};
+
+}  // namespace pkv

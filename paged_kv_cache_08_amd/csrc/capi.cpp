@@ -1,0 +1,446 @@
+// C ABI of the paged KV cache library (declared in include/pkv.h).
+//
+// Argument checking, allocator calls and kernel launches.  No C++ exception
+// leaves this file: every entry point catches and returns a status.
+#include "pkv.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstring>
+#include <exception>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "block_pool.hpp"
+#include "kernels.hpp"
+
+struct pkv_pool {
+  pkv::BlockPool alloc;
+  int32_t num_layers, num_kv_heads, head_dim, dtype;
+  std::vector<void*> k_cache, v_cache;    // empty for an allocator-only pool
+  // pinned staging for table uploads, reused once the previous upload ends
+  void* staging = nullptr;
+  size_t staging_bytes = 0;
+  hipEvent_t upload_done = nullptr;
+  bool upload_pending = false;
+
+  pkv_pool(int32_t nb, int32_t bs, const int32_t* perm) : alloc(nb, bs, perm) {}
+};
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int status, const std::string& msg) {
+  g_error = msg;
+  return status;
+}
+
+int from_alloc(pkv::Status st, const pkv_pool* pool) {
+  if (st == pkv::Status::Ok) return PKV_OK;
+  g_error = pool->alloc.error();
+  return static_cast<int>(st);
+}
+
+int from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PKV_OK;
+  return fail(PKV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int elem_bytes(int32_t dtype) { return dtype == PKV_F32 ? 4 : 2; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+template <typename F>
+int guarded(F&& f) {
+  try {
+    return f();
+  } catch (const std::bad_alloc&) {
+    return fail(PKV_ERR_INVALID, "host allocation failed");
+  } catch (const std::exception& e) {
+    return fail(PKV_ERR_INVALID, e.what());
+  } catch (...) {
+    return fail(PKV_ERR_INVALID, "unknown error");
+  }
+}
+
+int32_t effective_partition(int32_t partition) { return partition == 0 ? 512 : partition; }
+
+// Checks the decode arguments and fills the kernel parameter block.
+int prepare_decode(const pkv_decode_args* a, pkv::DecodeParams* p) {
+  if (!a) return fail(PKV_ERR_INVALID, "decode: null args");
+  if (a->dtype != PKV_F32 && a->dtype != PKV_BF16) return fail(PKV_ERR_INVALID, "decode: bad dtype");
+  if (a->num_seqs < 1 || a->num_kv_heads < 1 || a->num_q_heads < 1 || a->head_dim < 1 ||
+      a->block_size < 1 || a->num_blocks < 1 || a->max_blocks < 1 || a->max_seq_len < 1)
+    return fail(PKV_ERR_INVALID, "decode: sizes must be positive");
+  if (a->num_q_heads % a->num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "decode: num_q_heads must be a multiple of num_kv_heads");
+  const int32_t part = effective_partition(a->partition);
+  if (part < 32 || part > 1024 || part % 32 != 0)
+    return fail(PKV_ERR_INVALID, "decode: partition must be a multiple of 32 in [32, 1024]");
+  if (!pkv::decode_shape_supported(a->dtype == PKV_BF16 ? 1 : 0, a->head_dim, a->block_size))
+    return fail(PKV_ERR_UNSUPPORTED, "decode: supported shapes are block_size 16, head_dim 64 or 128");
+  if (!a->q || !a->out || !a->k_cache || !a->v_cache || !a->block_tables || !a->seq_lens)
+    return fail(PKV_ERR_INVALID, "decode: null device pointer");
+  if (!aligned16(a->q) || !aligned16(a->out) || !aligned16(a->k_cache) || !aligned16(a->v_cache))
+    return fail(PKV_ERR_INVALID, "decode: q, out and caches must be 16-byte aligned");
+  const int64_t pmax = (static_cast<int64_t>(a->max_seq_len) + part - 1) / part;
+  const int64_t gx = pmax * a->num_seqs * a->num_kv_heads;
+  if (gx > 0x7fffffffLL || static_cast<int64_t>(a->num_seqs) * a->num_q_heads > 0x7fffffffLL)
+    return fail(PKV_ERR_INVALID, "decode: grid too large");
+  const size_t need = pkv_decode_workspace_bytes(a->num_seqs, a->num_q_heads, a->head_dim,
+                                                 a->max_seq_len, a->partition);
+  if (need > 0 && (!a->workspace || a->workspace_bytes < need))
+    return fail(PKV_ERR_INVALID, "decode: workspace missing or smaller than pkv_decode_workspace_bytes()");
+  if (need > 0 && !aligned16(a->workspace))
+    return fail(PKV_ERR_INVALID, "decode: workspace must be 16-byte aligned");
+  p->q = a->q;
+  p->out = a->out;
+  p->k_cache = a->k_cache;
+  p->v_cache = a->v_cache;
+  p->block_tables = a->block_tables;
+  p->seq_lens = a->seq_lens;
+  p->S = a->num_seqs;
+  p->Hq = a->num_q_heads;
+  p->Hkv = a->num_kv_heads;
+  p->G = a->num_q_heads / a->num_kv_heads;
+  p->d = a->head_dim;
+  p->num_blocks = a->num_blocks;
+  p->max_blocks = a->max_blocks;
+  p->max_seq_len = a->max_seq_len;
+  p->partition = part;
+  p->pmax = static_cast<int32_t>(pmax);
+  p->scale_log2 = a->scale * 1.4426950408889634f;
+  if (need > 0) {
+    const size_t rows = static_cast<size_t>(a->num_seqs) * a->num_q_heads * pmax;
+    const size_t ml_bytes = (rows * 2 * sizeof(float) + 255) & ~size_t(255);
+    p->part_ml = static_cast<float*>(a->workspace);
+    p->part_acc = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + ml_bytes);
+  } else {
+    p->part_ml = nullptr;
+    p->part_acc = nullptr;
+  }
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_ERR_INVALID: return "PKV_ERR_INVALID";
+    case PKV_ERR_NO_BLOCKS: return "PKV_ERR_NO_BLOCKS";
+    case PKV_ERR_BAD_SEQ: return "PKV_ERR_BAD_SEQ";
+    case PKV_ERR_HIP: return "PKV_ERR_HIP";
+    case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED";
+    default: return "PKV_ERR_UNKNOWN";
+  }
+}
+
+const char* pkv_last_error(void) { return g_error.c_str(); }
+
+int pkv_version(void) { return 100; }
+
+int pkv_pool_create(const pkv_pool_desc* d, pkv_pool** out) {
+  return guarded([&]() -> int {
+    if (!d || !out) return fail(PKV_ERR_INVALID, "pool_create: null argument");
+    *out = nullptr;
+    if (d->num_layers < 1 || d->num_kv_heads < 1 || d->head_dim < 1 || d->block_size < 1 ||
+        d->num_blocks < 1)
+      return fail(PKV_ERR_INVALID, "pool_create: sizes must be positive");
+    if (d->dtype != PKV_F32 && d->dtype != PKV_BF16) return fail(PKV_ERR_INVALID, "pool_create: bad dtype");
+    if ((d->head_dim * elem_bytes(d->dtype)) % 16 != 0)
+      return fail(PKV_ERR_INVALID, "pool_create: head_dim must be a multiple of 16 bytes");
+    if (static_cast<int64_t>(d->num_blocks) * d->block_size > 0x7fffffffLL)
+      return fail(PKV_ERR_INVALID, "pool_create: num_blocks * block_size must fit in int32 slots");
+    if ((d->k_cache == nullptr) != (d->v_cache == nullptr))
+      return fail(PKV_ERR_INVALID, "pool_create: give both k_cache and v_cache, or neither");
+    if (d->init_perm) {
+      std::vector<char> seen(d->num_blocks, 0);
+      for (int32_t i = 0; i < d->num_blocks; ++i) {
+        const int32_t b = d->init_perm[i];
+        if (b < 0 || b >= d->num_blocks || seen[b])
+          return fail(PKV_ERR_INVALID, "pool_create: init_perm is not a permutation");
+        seen[b] = 1;
+      }
+    }
+    auto* pool = new pkv_pool(d->num_blocks, d->block_size, d->init_perm);
+    pool->num_layers = d->num_layers;
+    pool->num_kv_heads = d->num_kv_heads;
+    pool->head_dim = d->head_dim;
+    pool->dtype = d->dtype;
+    if (d->k_cache) {
+      for (int32_t l = 0; l < d->num_layers; ++l) {
+        if (!d->k_cache[l] || !d->v_cache[l] || !aligned16(d->k_cache[l]) || !aligned16(d->v_cache[l])) {
+          delete pool;
+          return fail(PKV_ERR_INVALID, "pool_create: layer caches must be non-null and 16-byte aligned");
+        }
+        pool->k_cache.push_back(d->k_cache[l]);
+        pool->v_cache.push_back(d->v_cache[l]);
+      }
+    }
+    *out = pool;
+    return PKV_OK;
+  });
+}
+
+int pkv_pool_destroy(pkv_pool* pool) {
+  if (!pool) return PKV_OK;
+  int st = PKV_OK;
+  if (pool->upload_done) {
+    if (pool->upload_pending) st = from_hip(hipEventSynchronize(pool->upload_done), "pool_destroy");
+    (void)hipEventDestroy(pool->upload_done);
+  }
+  if (pool->staging) (void)hipHostFree(pool->staging);
+  delete pool;
+  return st;
+}
+
+int pkv_seq_create(pkv_pool* pool, int64_t* id) {
+  if (!pool || !id) return fail(PKV_ERR_INVALID, "seq_create: null argument");
+  return guarded([&] { return from_alloc(pool->alloc.create(id), pool); });
+}
+
+int pkv_seq_fork(pkv_pool* pool, int64_t parent, int64_t* child) {
+  if (!pool || !child) return fail(PKV_ERR_INVALID, "seq_fork: null argument");
+  return guarded([&] { return from_alloc(pool->alloc.fork(parent, child), pool); });
+}
+
+int pkv_seq_free(pkv_pool* pool, int64_t id) {
+  if (!pool) return fail(PKV_ERR_INVALID, "seq_free: null pool");
+  return guarded([&] { return from_alloc(pool->alloc.release(id), pool); });
+}
+
+int pkv_seq_extend(pkv_pool* pool, int64_t id, int32_t ntok, int32_t* slots, int32_t* cow,
+                   int32_t* n_cow) {
+  if (!pool || !n_cow || !cow || (ntok > 0 && !slots)) return fail(PKV_ERR_INVALID, "seq_extend: null argument");
+  return guarded([&] { return from_alloc(pool->alloc.extend(id, ntok, slots, cow, n_cow), pool); });
+}
+
+int pkv_append_slots(pkv_pool* pool, const int64_t* ids, int32_t n, int32_t* slots, int32_t* cow,
+                     int32_t* n_cow) {
+  if (!pool || !n_cow || (n > 0 && (!ids || !slots || !cow)))
+    return fail(PKV_ERR_INVALID, "append_slots: null argument");
+  return guarded([&] { return from_alloc(pool->alloc.append(ids, n, slots, cow, n_cow), pool); });
+}
+
+int pkv_seq_length(const pkv_pool* pool, int64_t id, int32_t* len) {
+  if (!pool || !len) return fail(PKV_ERR_INVALID, "seq_length: null argument");
+  const pkv::Sequence* s = pool->alloc.find(id);
+  if (!s) return fail(PKV_ERR_BAD_SEQ, "seq_length: unknown sequence id " + std::to_string(id));
+  *len = s->len;
+  return PKV_OK;
+}
+
+int pkv_seq_table(const pkv_pool* pool, int64_t id, int32_t* table, int32_t cap, int32_t* nblocks) {
+  if (!pool || !nblocks || (cap > 0 && !table)) return fail(PKV_ERR_INVALID, "seq_table: null argument");
+  const pkv::Sequence* s = pool->alloc.find(id);
+  if (!s) return fail(PKV_ERR_BAD_SEQ, "seq_table: unknown sequence id " + std::to_string(id));
+  const int32_t nb = static_cast<int32_t>(s->table.size());
+  *nblocks = nb;
+  std::copy_n(s->table.begin(), std::min(std::max(cap, 0), nb), table);
+  return PKV_OK;
+}
+
+int pkv_sync_tables(pkv_pool* pool, const int64_t* ids, int32_t n, int32_t* dev_tables,
+                    int32_t max_blocks, int32_t* dev_lens, void* stream) {
+  return guarded([&]() -> int {
+    if (!pool || n < 0 || max_blocks < 1) return fail(PKV_ERR_INVALID, "sync_tables: bad argument");
+    if (n == 0) return PKV_OK;
+    if (!ids || !dev_tables || !dev_lens) return fail(PKV_ERR_INVALID, "sync_tables: null pointer");
+    std::vector<const pkv::Sequence*> seqs(n);
+    for (int32_t i = 0; i < n; ++i) {
+      seqs[i] = pool->alloc.find(ids[i]);
+      if (!seqs[i]) return fail(PKV_ERR_BAD_SEQ, "sync_tables: unknown sequence id " + std::to_string(ids[i]));
+      if (static_cast<int32_t>(seqs[i]->table.size()) > max_blocks)
+        return fail(PKV_ERR_INVALID, "sync_tables: sequence " + std::to_string(ids[i]) +
+                                         " holds more than max_blocks blocks");
+    }
+    const size_t table_bytes = static_cast<size_t>(n) * max_blocks * sizeof(int32_t);
+    const size_t need = table_bytes + static_cast<size_t>(n) * sizeof(int32_t);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int rc;
+    if (!pool->upload_done) {
+      rc = from_hip(hipEventCreateWithFlags(&pool->upload_done, hipEventDisableTiming), "sync_tables");
+      if (rc) return rc;
+    }
+    if (pool->upload_pending) {
+      rc = from_hip(hipEventSynchronize(pool->upload_done), "sync_tables: wait for previous upload");
+      if (rc) return rc;
+      pool->upload_pending = false;
+    }
+    if (pool->staging_bytes < need) {
+      if (pool->staging) (void)hipHostFree(pool->staging);
+      pool->staging = nullptr;
+      pool->staging_bytes = 0;
+      const size_t cap = std::max(need, static_cast<size_t>(1) << 20);
+      rc = from_hip(hipHostMalloc(&pool->staging, cap, hipHostMallocDefault), "sync_tables: pinned staging");
+      if (rc) return rc;
+      pool->staging_bytes = cap;
+    }
+    int32_t* tab = static_cast<int32_t*>(pool->staging);
+    int32_t* lens = tab + static_cast<size_t>(n) * max_blocks;
+    for (int32_t i = 0; i < n; ++i) {
+      int32_t* row = tab + static_cast<size_t>(i) * max_blocks;
+      const auto& t = seqs[i]->table;
+      std::copy(t.begin(), t.end(), row);
+      std::fill(row + t.size(), row + max_blocks, -1);
+      lens[i] = seqs[i]->len;
+    }
+    rc = from_hip(hipMemcpyAsync(dev_tables, tab, table_bytes, hipMemcpyHostToDevice, st), "sync_tables: tables");
+    if (rc) return rc;
+    rc = from_hip(hipMemcpyAsync(dev_lens, lens, n * sizeof(int32_t), hipMemcpyHostToDevice, st),
+                  "sync_tables: lengths");
+    if (rc) return rc;
+    rc = from_hip(hipEventRecord(pool->upload_done, st), "sync_tables: record");
+    if (rc) return rc;
+    pool->upload_pending = true;
+    return PKV_OK;
+  });
+}
+
+int pkv_copy_blocks(pkv_pool* pool, const int32_t* pairs, int32_t n_pairs, void* stream) {
+  if (!pool || n_pairs < 0 || (n_pairs > 0 && !pairs)) return fail(PKV_ERR_INVALID, "copy_blocks: bad argument");
+  if (n_pairs == 0) return PKV_OK;
+  if (pool->k_cache.empty()) return fail(PKV_ERR_INVALID, "copy_blocks: pool has no device caches");
+  const int32_t nb = pool->alloc.num_blocks();
+  for (int32_t i = 0; i < 2 * n_pairs; ++i)
+    if (pairs[i] < 0 || pairs[i] >= nb) return fail(PKV_ERR_INVALID, "copy_blocks: block id out of range");
+  const int64_t block_bytes = static_cast<int64_t>(pool->num_kv_heads) * pool->head_dim *
+                              pool->alloc.block_size() * elem_bytes(pool->dtype);
+  for (int32_t l0 = 0; l0 < pool->num_layers; l0 += pkv::kCopyMaxLayers) {
+    for (int32_t p0 = 0; p0 < n_pairs; p0 += pkv::kCopyMaxPairs) {
+      pkv::CopyBlocksParams p{};
+      p.n_layers = std::min(pkv::kCopyMaxLayers, pool->num_layers - l0);
+      p.n_pairs = std::min(pkv::kCopyMaxPairs, n_pairs - p0);
+      p.block_bytes = block_bytes;
+      for (int32_t l = 0; l < p.n_layers; ++l) {
+        p.k[l] = pool->k_cache[l0 + l];
+        p.v[l] = pool->v_cache[l0 + l];
+      }
+      std::memcpy(p.pairs, pairs + 2 * p0, sizeof(int32_t) * 2 * p.n_pairs);
+      const int rc = from_hip(pkv::launch_copy_blocks(p, static_cast<hipStream_t>(stream)), "copy_blocks");
+      if (rc) return rc;
+    }
+  }
+  return PKV_OK;
+}
+
+int pkv_kv_append(pkv_pool* pool, int32_t layer, const void* k_new, const void* v_new,
+                  const int32_t* dev_slots, int32_t n, void* stream) {
+  if (!pool || n < 0) return fail(PKV_ERR_INVALID, "kv_append: bad argument");
+  if (n == 0) return PKV_OK;
+  if (pool->k_cache.empty()) return fail(PKV_ERR_INVALID, "kv_append: pool has no device caches");
+  if (layer < 0 || layer >= pool->num_layers) return fail(PKV_ERR_INVALID, "kv_append: layer out of range");
+  if (!k_new || !v_new || !dev_slots) return fail(PKV_ERR_INVALID, "kv_append: null pointer");
+  if (!aligned16(k_new) || !aligned16(v_new)) return fail(PKV_ERR_INVALID, "kv_append: inputs must be 16-byte aligned");
+  pkv::AppendParams p{};
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.slots = dev_slots;
+  p.k_cache = pool->k_cache[layer];
+  p.v_cache = pool->v_cache[layer];
+  p.num_slots = static_cast<int64_t>(pool->alloc.num_blocks()) * pool->alloc.block_size();
+  p.n = n;
+  p.num_kv_heads = pool->num_kv_heads;
+  p.head_dim = pool->head_dim;
+  p.block_size = pool->alloc.block_size();
+  p.elem_bytes = elem_bytes(pool->dtype);
+  return from_hip(pkv::launch_kv_append(p, static_cast<hipStream_t>(stream)), "kv_append");
+}
+
+int pkv_pool_stats(const pkv_pool* pool, pkv_stats* out) {
+  if (!pool || !out) return fail(PKV_ERR_INVALID, "pool_stats: null argument");
+  const auto& a = pool->alloc;
+  pkv_stats s{};
+  s.num_blocks = a.num_blocks();
+  s.free_blocks = static_cast<int64_t>(a.free_stack().size());
+  s.used_blocks = s.num_blocks - s.free_blocks;
+  s.num_seqs = static_cast<int64_t>(a.sequences().size());
+  for (int32_t r : a.refcounts()) s.sum_ref += r;
+  for (const auto& kv : a.sequences()) {
+    s.sum_len += kv.second.len;
+    s.tail_waste += static_cast<int64_t>(kv.second.table.size()) * a.block_size() - kv.second.len;
+  }
+  *out = s;
+  return PKV_OK;
+}
+
+int pkv_pool_snapshot(const pkv_pool* pool, int32_t* free_out, int32_t* ref_out, int64_t* ids_out,
+                      int32_t* lens_out, int64_t* table_off_out, int32_t* tables_out, int64_t* n_free,
+                      int64_t* n_seqs, int64_t* n_entries, int64_t* next_id) {
+  return guarded([&]() -> int {
+    if (!pool || !n_free || !n_seqs || !n_entries || !next_id)
+      return fail(PKV_ERR_INVALID, "pool_snapshot: null size pointer");
+    const auto& a = pool->alloc;
+    std::vector<int64_t> ids;
+    ids.reserve(a.sequences().size());
+    int64_t entries = 0;
+    for (const auto& kv : a.sequences()) {
+      ids.push_back(kv.first);
+      entries += static_cast<int64_t>(kv.second.table.size());
+    }
+    std::sort(ids.begin(), ids.end());
+    *n_free = static_cast<int64_t>(a.free_stack().size());
+    *n_seqs = static_cast<int64_t>(ids.size());
+    *n_entries = entries;
+    *next_id = a.next_id();
+    if (free_out) std::copy(a.free_stack().begin(), a.free_stack().end(), free_out);
+    if (ref_out) std::copy(a.refcounts().begin(), a.refcounts().end(), ref_out);
+    int64_t off = 0;
+    for (size_t i = 0; i < ids.size(); ++i) {
+      const pkv::Sequence* s = a.find(ids[i]);
+      if (ids_out) ids_out[i] = ids[i];
+      if (lens_out) lens_out[i] = s->len;
+      if (table_off_out) table_off_out[i] = off;
+      if (tables_out) std::copy(s->table.begin(), s->table.end(), tables_out + off);
+      off += static_cast<int64_t>(s->table.size());
+    }
+    if (table_off_out) table_off_out[ids.size()] = off;
+    return PKV_OK;
+  });
+}
+
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t max_seq_len, int32_t partition) {
+  const int32_t part = effective_partition(partition);
+  if (num_seqs < 1 || num_q_heads < 1 || head_dim < 1 || max_seq_len < 1 || part < 1) return 0;
+  const int64_t pmax = (static_cast<int64_t>(max_seq_len) + part - 1) / part;
+  if (pmax <= 1) return 0;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * pmax;
+  const size_t ml_bytes = (rows * 2 * sizeof(float) + 255) & ~size_t(255);
+  return ml_bytes + rows * head_dim * sizeof(float);
+}
+
+int pkv_paged_decode_partial(const pkv_decode_args* a, void* stream) {
+  pkv::DecodeParams p{};
+  const int rc = prepare_decode(a, &p);
+  if (rc) return rc;
+  return from_hip(pkv::launch_decode_partial(p, a->dtype == PKV_BF16 ? 1 : 0, static_cast<hipStream_t>(stream)),
+                  "decode_partial");
+}
+
+int pkv_paged_decode_reduce(const pkv_decode_args* a, void* stream) {
+  pkv::DecodeParams p{};
+  const int rc = prepare_decode(a, &p);
+  if (rc) return rc;
+  return from_hip(pkv::launch_decode_reduce(p, a->dtype == PKV_BF16 ? 1 : 0, static_cast<hipStream_t>(stream)),
+                  "decode_reduce");
+}
+
+int pkv_paged_attention_decode(const pkv_decode_args* a, void* stream) {
+  pkv::DecodeParams p{};
+  int rc = prepare_decode(a, &p);
+  if (rc) return rc;
+  const int dt = a->dtype == PKV_BF16 ? 1 : 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = from_hip(pkv::launch_decode_partial(p, dt, st), "decode_partial");
+  if (rc) return rc;
+  return from_hip(pkv::launch_decode_reduce(p, dt, st), "decode_reduce");
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Host-side launchers of the HIP kernels (defined in kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace pkv {
+
+// Copy-on-write block copies for up to kCopyMaxLayers layers and
+// kCopyMaxPairs pairs per launch (the caller chunks larger requests).
+constexpr int kCopyMaxLayers = 32;
+constexpr int kCopyMaxPairs = 64;
+
+struct CopyBlocksParams {
+  void* k[kCopyMaxLayers];
+  void* v[kCopyMaxLayers];
+  int32_t pairs[2 * kCopyMaxPairs];
+  int32_t n_layers;
+  int32_t n_pairs;
+  int64_t block_bytes;   // bytes of one block (all heads) in one layer's K or V
+};
+
+struct AppendParams {
+  const void* k_new;
+  const void* v_new;
+  const int32_t* slots;
+  void* k_cache;
+  void* v_cache;
+  int64_t num_slots;     // num_blocks * block_size
+  int32_t n;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t elem_bytes;    // 4 (fp32) or 2 (bf16)
+};
+
+struct DecodeParams {
+  const void* q;
+  void* out;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  float* part_ml;        // [S][Hq][Pmax][2]   (running max in log2 units, sum)
+  float* part_acc;       // [S][Hq][Pmax][d]   unnormalised accumulators
+  int32_t S, Hq, Hkv, G, d;
+  int32_t num_blocks, max_blocks, max_seq_len;
+  int32_t partition, pmax;
+  float scale_log2;      // scale * log2(e): scores are kept in base-2 units
+};
+
+hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t stream);
+hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream);
+// dtype: 0 = fp32, 1 = bf16.  Returns hipErrorInvalidValue for shapes
+// without a kernel (checked by the caller first).
+hipError_t launch_decode_partial(const DecodeParams& p, int dtype, hipStream_t stream);
+hipError_t launch_decode_reduce(const DecodeParams& p, int dtype, hipStream_t stream);
+bool decode_shape_supported(int dtype, int head_dim, int block_size);
+
+}  // namespace pkv

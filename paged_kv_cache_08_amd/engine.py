@@ -1,0 +1,139 @@
+"""A decode-step driver over the C ABI: device pools as torch tensors, the
+host allocator, copy-on-write copies, kv_append and paged decode attention.
+
+torch provides device memory and streams only; every step of the path is a
+libpkv call (host allocator or HIP kernel).
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+from . import pkv as P
+
+_DT = {"f32": (torch.float32, P.PKV_F32), "bf16": (torch.bfloat16, P.PKV_BF16)}
+
+
+class PagedDecodeEngine:
+    def __init__(self, num_layers: int, num_kv_heads: int, head_dim: int, num_blocks: int,
+                 dtype: str = "bf16", block_size: int = 16, init_perm=None, device="cuda",
+                 poison: bool = True, partition: int = 0):
+        self.L, self.Hkv, self.d, self.N, self.B = num_layers, num_kv_heads, head_dim, num_blocks, block_size
+        self.dtype = dtype
+        self.tdtype, self.cdtype = _DT[dtype]
+        self.device = torch.device(device)
+        self.partition = partition
+        numel = num_blocks * num_kv_heads * head_dim * block_size
+        fill = float("nan") if poison else 0.0
+        self.k = [torch.full((numel,), fill, dtype=self.tdtype, device=self.device) for _ in range(num_layers)]
+        self.v = [torch.full((numel,), fill, dtype=self.tdtype, device=self.device) for _ in range(num_layers)]
+        self.pool = P.pkv_pool_create(num_layers, num_kv_heads, head_dim, block_size, num_blocks,
+                                      self.cdtype, self.k, self.v, init_perm)
+        self.tables = None
+        self.lens = None
+        self.workspace = None
+
+    # -- allocator + writes ------------------------------------------------
+    def create(self) -> int:
+        return P.pkv_seq_create(self.pool)
+
+    def fork(self, parent: int) -> int:
+        return P.pkv_seq_fork(self.pool, parent)
+
+    def free(self, sid: int) -> None:
+        P.pkv_seq_free(self.pool, sid)
+
+    def _write(self, slots: np.ndarray, cow, values: Optional[Dict[int, Tuple[torch.Tensor, torch.Tensor]]],
+               stream=None):
+        if cow:
+            P.pkv_copy_blocks(self.pool, cow, stream)
+        if values:
+            dev_slots = torch.from_numpy(np.ascontiguousarray(slots)).to(self.device, non_blocking=False)
+            for layer, (kk, vv) in values.items():
+                P.pkv_kv_append(self.pool, layer, kk.contiguous(), vv.contiguous(), dev_slots, stream)
+
+    def extend(self, sid: int, ntok: int, values=None, stream=None):
+        """Reserve ntok slots; values: {layer: (k [ntok][Hkv][d], v)} device tensors."""
+        slots, cow = P.pkv_seq_extend(self.pool, sid, ntok)
+        self._write(slots, cow, values, stream)
+        return slots, cow
+
+    def append(self, ids: Sequence[int], values=None, stream=None):
+        """One token per id; values: {layer: (k [n][Hkv][d], v)} device tensors."""
+        slots, cow = P.pkv_append_slots(self.pool, ids)
+        self._write(slots, cow, values, stream)
+        return slots, cow
+
+    def run_script(self, ops, wl=None, k_log=None, v_log=None, layers: Sequence[int] = (0,), stream=None):
+        """Execute a workload script; token values are rows of the logical
+        tensors (dict layer -> tensor [sum n][Hkv][d]) selected by the ops."""
+        offs = None if wl is None else wl.offsets
+        log = []
+        for op in ops:
+            kind = op[0]
+            if kind == "create":
+                self.create()
+            elif kind == "fork":
+                self.fork(op[1])
+            elif kind == "free":
+                self.free(op[1])
+            elif kind in ("extend", "append"):
+                if kind == "extend":
+                    _, sid, k, src, pos = op
+                    rows = torch.arange(offs[src] + pos, offs[src] + pos + k) if offs is not None else None
+                else:
+                    rows = (torch.tensor([offs[src] + pos for (_, src, pos) in op[1]])
+                            if offs is not None else None)
+                vals = None
+                if k_log is not None and rows is not None:
+                    rd = rows.to(self.device)
+                    vals = {l: (k_log[l].index_select(0, rd), v_log[l].index_select(0, rd)) for l in layers}
+                if kind == "extend":
+                    slots, cow = self.extend(op[1], op[2], vals, stream)
+                    log.append(("extend", op[1], slots, cow))
+                else:
+                    ids = [e[0] for e in op[1]]
+                    slots, cow = self.append(ids, vals, stream)
+                    log.append(("append", ids, slots, cow))
+            else:
+                raise ValueError(kind)
+        return log
+
+    # -- decode ------------------------------------------------------------
+    def sync(self, ids: Sequence[int], max_blocks: Optional[int] = None, stream=None):
+        n = len(ids)
+        if max_blocks is None:
+            max_blocks = max(1, max(len(P.pkv_seq_table(self.pool, i)) for i in ids))
+        if self.tables is None or self.tables.shape != (n, max_blocks):
+            self.tables = torch.empty((n, max_blocks), dtype=torch.int32, device=self.device)
+            self.lens = torch.empty((n,), dtype=torch.int32, device=self.device)
+        P.pkv_sync_tables(self.pool, ids, self.tables, self.lens, stream)
+        return self.tables, self.lens
+
+    def decode_args(self, layer: int, q: torch.Tensor, out: torch.Tensor, max_seq_len: int,
+                    scale: Optional[float] = None):
+        need = P.pkv_decode_workspace_bytes(q.shape[0], q.shape[1], self.d, max_seq_len, self.partition)
+        if need and (self.workspace is None or self.workspace.numel() < need):
+            self.workspace = torch.empty((need,), dtype=torch.uint8, device=self.device)
+        return P.decode_args(q, out, self.k[layer], self.v[layer], self.tables, self.lens, self.Hkv, self.N,
+                             max_seq_len, scale, self.partition, self.workspace if need else None, self.B)
+
+    def decode(self, layer: int, q: torch.Tensor, max_seq_len: int, out: Optional[torch.Tensor] = None,
+               scale: Optional[float] = None, stream=None) -> torch.Tensor:
+        if out is None:
+            out = torch.empty_like(q)
+        a = self.decode_args(layer, q, out, max_seq_len, scale)
+        P.pkv_paged_attention_decode(a, stream)
+        return out
+
+    def snapshot(self):
+        return P.pkv_pool_snapshot(self.pool)
+
+    def length(self, sid: int) -> int:
+        return P.pkv_seq_length(self.pool, sid)
+
+    def table(self, sid: int):
+        return P.pkv_seq_table(self.pool, sid)

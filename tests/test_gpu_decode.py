@@ -1,0 +1,170 @@
+"""GPU parity: the library (allocator, kv_append, copy_blocks, decode
+kernels) against the CPU oracle on the same seeded inputs.
+
+Allocator state, slot mappings and the pool contents are compared bit for
+bit (free and tail slots hold NaN poison on both sides); attention outputs
+within max |err| <= 2e-2 and row-normwise relative error <= 1e-2.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_common import (check_allocator, check_pool, compare_out, need_gpu, note, oracle_out,
+                        oracle_replay, run_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_case(wl, partition=0, scale=None, q_scale=1.0):
+    need_gpu()
+    note(f"case: {wl.description} partition={partition} q_scale={q_scale}")
+    q, k, v = wl.tensors(device="cuda")
+    if q_scale != 1.0:
+        q = (q.float() * q_scale).to(q.dtype)
+    eng, log, out = run_gpu(wl, {0: k}, {0: v}, q, partition=partition, scale=scale)
+    rp = oracle_replay(wl, {0: k}, {0: v})
+    check_allocator(eng, rp, log)
+    check_pool(eng, rp)
+    ref = oracle_out(rp, wl, q, scale=scale)
+    err = compare_out(out[0], ref)
+    note(f"  max_abs={err[0]:.3e} row_rel={err[1]:.3e}")
+    return eng, log, out[0], ref
+
+
+def test_tiny():
+    _full_case(workloads.tiny())
+
+
+SHAPES = [
+    # S, Hq, Hkv, d, dtype, max_len
+    (5, 8, 2, 128, "bf16", 300),
+    (4, 40, 8, 128, "bf16", 1100),
+    (3, 40, 2, 128, "bf16", 700),       # 20 query heads per KV head: two head groups
+    (6, 8, 1, 64, "bf16", 200),         # one KV head, d = 64
+    (3, 4, 4, 128, "f32", 900),         # MHA fp32, several partitions
+    (4, 12, 3, 64, "f32", 600),
+    (4, 64, 8, 128, "bf16", 2100),
+    (2, 64, 1, 128, "bf16", 150),       # 64 query heads on one KV head
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_shapes(shape):
+    S, Hq, Hkv, d, dt, ml = shape
+    _full_case(workloads.random_small(40 + len(str(shape)), S=S, Hq=Hq, Hkv=Hkv, d=d, dtype=dt, max_len=ml))
+
+
+EDGE = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 511, 512, 513, 1023, 1024, 1025, 1535]
+
+
+@pytest.mark.parametrize("partition", [0, 32, 64, 1024])
+def test_edge_lengths(partition):
+    wl = workloads.with_lengths(EDGE, Hq=16, Hkv=4, d=128, dtype="bf16", seed=partition + 1)
+    _full_case(wl, partition=partition)
+
+
+def test_edge_lengths_fp32():
+    wl = workloads.with_lengths(EDGE, Hq=4, Hkv=1, d=64, dtype="f32", seed=5)
+    _full_case(wl)
+
+
+def test_extreme_logits():
+    wl = workloads.random_small(61, S=4, Hq=8, Hkv=2, d=128, dtype="bf16", max_len=700)
+    _full_case(wl, q_scale=3000.0)
+
+
+def test_custom_scale():
+    wl = workloads.random_small(62, S=3, Hq=8, Hkv=2, d=128, dtype="bf16", max_len=600)
+    _full_case(wl, scale=0.37)
+
+
+def test_permutation_gives_identical_bits():
+    need_gpu()
+    wl = workloads.random_small(70, S=6, Hq=16, Hkv=4, d=128, dtype="bf16", max_len=1500)
+    q, k, v = wl.tensors(device="cuda")
+    _, _, out1 = run_gpu(wl, {0: k}, {0: v}, q)
+    wl2 = dataclasses.replace(wl, perm=np.random.default_rng(123).permutation(wl.num_blocks).astype(np.int32))
+    _, _, out2 = run_gpu(wl2, {0: k}, {0: v}, q)
+    assert torch.equal(out1[0].view(torch.int16), out2[0].view(torch.int16))
+
+
+def test_shared_prefix_equals_private_copies_bits():
+    need_gpu()
+    kw = dict(seed=9, S=12, prefix=256, lo=16, hi=200)
+    sh = workloads.shared_prefix(**kw)
+    pr = workloads.shared_prefix(private_copies=True, **kw)
+    q, k, v = sh.tensors(device="cuda")
+    offs = sh.offsets
+    for s in range(1, sh.S):       # every logical sequence carries sequence 0's prefix
+        k[offs[s]:offs[s] + 256] = k[0:256]
+        v[offs[s]:offs[s] + 256] = v[0:256]
+    eng, log, out_s = run_gpu(sh, {0: k}, {0: v}, q)
+    _, _, out_p = run_gpu(pr, {0: k}, {0: v}, q)
+    assert torch.equal(out_s[0].view(torch.int16), out_p[0].view(torch.int16))
+    rp = oracle_replay(sh, {0: k}, {0: v})
+    check_allocator(eng, rp, log)
+    check_pool(eng, rp)
+    compare_out(out_s[0], oracle_out(rp, sh, q))
+
+
+def _cow_workload(dtype="bf16", d=128):
+    lengths = np.array([21, 21, 21, 37])
+    ops = [("create",), ("extend", 0, 20, 0, 0), ("fork", 0), ("fork", 0),
+           ("append", [(1, 1, 20), (2, 2, 20), (0, 0, 20)]),
+           ("fork", 1), ("extend", 3, 15, 3, 21)]
+    # seq 3 forks seq 1 at length 21 (inside a block), extends 15 tokens and
+    # appends its 37th in the checked step
+    step = [("append", [(3, 3, 36)])]
+    return workloads.Workload("cow", 1, 8, 2, d, dtype, lengths, 12, np.arange(12, dtype=np.int32)[::-1].copy(),
+                              ops, step, [0, 1, 2, 3], 77, description="fork/copy-on-write script")
+
+
+def test_copy_on_write():
+    wl = _cow_workload()
+    eng, log, out, ref = _full_case(wl)
+    # the batch append copied the shared partial block for seqs 1 and 2, not 0;
+    # the extend of seq 3 copied the block it shared with seq 1
+    assert [len(c) for _, _, _, c in log] == [0, 2, 1, 0]
+
+
+def test_copy_on_write_fp32_two_layers():
+    need_gpu()
+    wl = _cow_workload("f32", 64)
+    wl = dataclasses.replace(wl, layers=2)
+    t0 = wl.tensors(0, device="cuda")
+    t1 = wl.tensors(1, device="cuda")
+    k = {0: t0[1], 1: t1[1]}
+    v = {0: t0[2], 1: t1[2]}
+    eng, log, out = run_gpu(wl, k, v, {0: t0[0], 1: t1[0]}, layers=(0, 1))
+    assert any(c for _, _, _, c in log), "script should copy on write"
+    rp = oracle_replay(wl, k, v, layers=(0, 1))
+    check_allocator(eng, rp, log)
+    for layer, q in ((0, t0[0]), (1, t1[0])):
+        check_pool(eng, rp, layer)
+        compare_out(out[layer], oracle_out(rp, wl, q, layer=layer))
+
+
+def test_invalid_rows_become_nan():
+    need_gpu()
+    import paged_kv_cache_08_amd.pkv as P
+    wl = workloads.random_small(80, S=5, Hq=8, Hkv=2, d=128, dtype="bf16", max_len=900, min_len=600)
+    q, k, v = wl.tensors(device="cuda")
+    eng, _, out = run_gpu(wl, {0: k}, {0: v}, q)
+    good = out[0].clone()
+    tables, lens = eng.tables.clone(), eng.lens.clone()
+    lens[1] = 0                          # empty sequence
+    lens[2] = wl.max_len + 1             # beyond the declared bound
+    tables[3, 1] = wl.num_blocks         # block id outside the pool
+    out2 = torch.empty_like(q)
+    a = P.decode_args(q, out2, eng.k[0], eng.v[0], tables, lens, wl.Hkv, wl.num_blocks, wl.max_len)
+    ws = torch.empty(P.pkv_decode_workspace_bytes(wl.S, wl.Hq, wl.d, wl.max_len), dtype=torch.uint8, device="cuda")
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    P.pkv_paged_attention_decode(a)
+    torch.cuda.synchronize()
+    for s in (1, 2, 3):
+        assert torch.isnan(out2[s].float()).all(), s
+    for s in (0, 4):
+        assert torch.equal(out2[s].view(torch.int16), good[s].view(torch.int16))
