@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Paged decode benchmark on one MI355X.
+
+A step is one pass of the whole decode hot path over the batch: reserve one
+slot per sequence on the host allocator (copy-on-write copies if any),
+upload block tables and lengths, then for every layer write the new token's
+K/V (kv_append) and run paged decode attention (partial + reduce).  Steps
+are successive decode steps: every sequence grows by one token per step, and
+bytes are counted from the lengths of each step.
+
+Default workload: 16 sequences of 32768 tokens, 64 query / 8 KV heads,
+d = 128, bf16, 16-token blocks in random physical order, 512-token split-K
+partitions (the long-context configuration).  `value` is KV bytes read by
+attention per second (decimal GB/s) over the timed steps.
+
+Prints one JSON line.  Options: --gpus N (only 1 is supported), --steps K,
+--warmup W, --config NAME, --no-cpu-baseline, --cpu-seconds S.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: KV GB/s read and % of HBM peak; decode tokens/s"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_08_amd", "csrc", "kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="long_context")
+    ap.add_argument("--partition", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain 1 GiB device copies (known bytes) for counter scaling")
+    return ap.parse_args()
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def copy_calibration(reps: int = 5, nbytes: int = 1 << 30) -> None:
+    """Plain device-to-device copies of a known size: each launch reads and
+    writes exactly `nbytes`, so counter readings for it give the scale from
+    counter units to bytes."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": reps}), flush=True)
+
+
+class DecodeBench:
+    """Builds the batch through the library, then runs timed decode steps."""
+
+    def __init__(self, wl, steps_total: int, partition: int = 0, device="cuda"):
+        import numpy as np
+        import torch
+        from paged_kv_cache_08_amd import pkv as P
+        from paged_kv_cache_08_amd.engine import PagedDecodeEngine
+
+        self.P, self.torch, self.np = P, torch, np
+        self.wl = wl
+        self.dev = torch.device(device)
+        self.layers = wl.layers
+        self.eng = PagedDecodeEngine(wl.layers, wl.Hkv, wl.d, wl.num_blocks, wl.dtype, init_perm=wl.perm,
+                                     device=device, partition=partition)
+        # prefill every sequence to n - 1 tokens, layer by layer so the logical
+        # tensors of one layer at a time are resident
+        setup_log = self.eng.run_script(wl.setup_ops, None)    # allocator only
+        for layer in range(wl.layers):
+            _, k, v = wl.tensors(layer, device=device)
+            offs = wl.offsets
+            for (kind, sid, slots, cow), op in zip(setup_log, [o for o in wl.setup_ops if o[0] == "extend"]):
+                assert not cow
+                _, _, cnt, src, pos = op
+                rows = torch.arange(offs[src] + pos, offs[src] + pos + cnt, device=self.dev)
+                dslots = torch.from_numpy(np.ascontiguousarray(slots)).to(self.dev)
+                P.pkv_kv_append(self.eng.pool, layer, k.index_select(0, rows), v.index_select(0, rows), dslots)
+            del k, v
+        torch.cuda.synchronize()
+        self.ids = list(wl.seq_ids)
+        self.lengths = [int(n) - 1 for n in wl.lengths]        # current lengths
+        self.max_len = max(self.lengths) + steps_total
+        self.max_blocks = -(-self.max_len // wl.block)
+        self.eng.tables = torch.empty((len(self.ids), self.max_blocks), dtype=torch.int32, device=self.dev)
+        self.eng.lens = torch.empty((len(self.ids),), dtype=torch.int32, device=self.dev)
+        self.eng.host_lens = np.zeros(len(self.ids), dtype=np.int32)
+        # per-step inputs: new K/V per layer and the step's queries
+        g = torch.Generator(device=self.dev)
+        g.manual_seed(wl.seed * 7919 + 1)
+        dt = self.eng.tdtype
+        S = len(self.ids)
+        self.knew = [torch.randn((steps_total, S, wl.Hkv, wl.d), generator=g, device=self.dev).to(dt)
+                     for _ in range(wl.layers)]
+        self.vnew = [torch.randn((steps_total, S, wl.Hkv, wl.d), generator=g, device=self.dev).to(dt)
+                     for _ in range(wl.layers)]
+        self.q = [torch.randn((S, wl.Hq, wl.d), generator=g, device=self.dev).to(dt) for _ in range(wl.layers)]
+        self.out = [torch.empty_like(self.q[l]) for l in range(wl.layers)]
+        self.args = [self.eng.decode_args(l, self.q[l], self.out[l], self.max_len) for l in range(wl.layers)]
+        self.step_idx = 0
+        self.kv_bytes = []            # attention KV bytes of each step (all layers)
+        self.events = []              # (k3 start, k3 end) per layer per step
+
+    def step(self, record_events: bool):
+        P, torch = self.P, self.torch
+        j = self.step_idx
+        slots, cow = P.pkv_append_slots(self.eng.pool, self.ids)
+        if cow:
+            P.pkv_copy_blocks(self.eng.pool, cow)
+        dslots = torch.from_numpy(slots).pin_memory().to(self.dev, non_blocking=True)
+        P.pkv_sync_tables(self.eng.pool, self.ids, self.eng.tables, self.eng.lens, self.eng.host_lens)
+        for i in range(len(self.lengths)):
+            self.lengths[i] += 1
+        for l in range(self.layers):
+            P.pkv_kv_append(self.eng.pool, l, self.knew[l][j], self.vnew[l][j], dslots)
+            if record_events:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+            P.pkv_paged_decode_partial(self.args[l])
+            if record_events:
+                e1.record()
+                self.events.append((e0, e1))
+            P.pkv_paged_decode_reduce(self.args[l])
+        wl = self.wl
+        self.kv_bytes.append(2 * sum(self.lengths) * wl.Hkv * wl.d * self.eng.tdtype.itemsize * self.layers)
+        self.step_idx += 1
+
+
+def cpu_baseline(wl_name: str, seconds: float):
+    """The oracle (unchanged) on a bounded sample of the same workload:
+    a few of its sequences, one decode step at a time (allocator append,
+    scatter of the new token, gather + fp64 attention), on host cores."""
+    import numpy as np
+    import torch
+    import workloads
+    from oracle import attention as OA
+    from oracle.pool import to_f64
+    from oracle.replay import Replay
+
+    def bits(t):
+        t = t.contiguous()
+        return (t.view(torch.int32).numpy().view(np.uint32) if t.dtype == torch.float32
+                else t.view(torch.int16).numpy().view(np.uint16))
+
+    if wl_name == "long_context":
+        wl = workloads.long_context(S=2)
+        sample = "2 of the 16 sequences (32768 tokens, all 8 KV / 64 query heads), one layer"
+    elif wl_name == "full_step":
+        wl = workloads.full_step(S=16, layers=1)
+        sample = "16 sequences of the same length distribution, 1 of 32 layers"
+    else:
+        wl = workloads.CONFIGS[wl_name]()
+        sample = "whole batch, one layer"
+    q, k, v = wl.tensors(0, device="cpu")
+    rp = Replay(wl, layers=1).run(wl.setup_ops, {0: (bits(k), bits(v))})
+    g = torch.Generator().manual_seed(5)
+    lengths = [int(n) - 1 for n in wl.lengths]
+    q64 = to_f64(bits(q), wl.dtype)
+    steps, kv, t = 0, 0, 0.0
+    while t < seconds or steps == 0:
+        kn = torch.randn((wl.S, wl.Hkv, wl.d), generator=g).to(q.dtype)
+        vn = torch.randn((wl.S, wl.Hkv, wl.d), generator=g).to(q.dtype)
+        t0 = time.perf_counter()
+        slots, cow = rp.alloc.append(list(wl.seq_ids))
+        for a, b in cow:
+            rp.pool.copy_block(a, b)
+        rp.pool.scatter(0, slots, bits(kn), bits(vn))
+        lengths = [n + 1 for n in lengths]
+        OA.decode(rp.pool, 0, rp.tables(), lengths, q64, wl.Hq)
+        t += time.perf_counter() - t0
+        kv += 2 * sum(lengths) * wl.Hkv * wl.d * wl.itemsize
+        steps += 1
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    return {"value": kv / t / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{sample}; {steps} decode steps, {t:.1f} s", "tokens_per_s": wl.S * steps / t}
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch of the partial kernel from committed counter runs,
+    if they were taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_sha") != kernel_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the decode path has no multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    from paged_kv_cache_08_amd import pkv
+    if not os.path.exists(pkv.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+
+    wl = workloads.CONFIGS[args.config]()
+    total = args.warmup + args.steps
+    log(f"setup {wl.description}")
+    bench = DecodeBench(wl, total, partition=args.partition)
+    log("setup done; warmup")
+    for _ in range(args.warmup):
+        bench.step(record_events=False)
+    torch.cuda.synchronize()
+    log("timed steps")
+    bench.kv_bytes.clear()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        bench.step(record_events=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    kv_total = sum(bench.kv_bytes)
+    value = kv_total / elapsed / 1e9
+    k3_ms = [a.elapsed_time(b) for a, b in bench.events]
+    k3_avg_s = sum(k3_ms) / len(k3_ms) / 1e3
+    kv_per_launch = kv_total / len(k3_ms)
+    achieved = kv_per_launch / k3_avg_s / 1e9
+    traffic = load_traffic(args.config)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "description": wl.description, "layers": wl.layers,
+                   "S": wl.S, "Hq": wl.Hq, "Hkv": wl.Hkv, "d": wl.d, "block": wl.block,
+                   "partition": args.partition or 512, "start_lengths_mean": float(wl.lengths.mean())},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s": round(wl.S * args.steps / elapsed, 1),
+        "roofline": {"bound": "hbm", "kernel": "decode_partial", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "avg_launch_us": round(k3_avg_s * 1e6, 2),
+                     "algorithmic_bytes_per_launch": int(kv_per_launch)},
+    }
+    log(f"timed {args.steps} steps: {value:.1f} GB/s; partial kernel {k3_avg_s * 1e6:.1f} us")
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

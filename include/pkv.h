@@ -132,11 +132,14 @@ int pkv_seq_table(const pkv_pool* pool, int64_t seq_id, int32_t* table_out, int3
 /* Upload the block tables and lengths of `n` sequences to caller-owned
  * device arrays: dev_block_tables int32[n][max_blocks] (row i = ids[i],
  * unused entries -1) and dev_seq_lens int32[n].  Asynchronous on `stream`
- * through a pinned staging buffer owned by the pool; the next call waits
- * for the previous upload before reusing it.  PKV_ERR_INVALID if a
+ * through two pinned staging buffers owned by the pool, used alternately: a
+ * call waits only for the upload issued two calls earlier.  If
+ * host_seq_lens_out is not NULL it also receives the lengths (host int32[n]),
+ * e.g. to pass as pkv_decode_args.host_seq_lens.  PKV_ERR_INVALID if a
  * sequence holds more than max_blocks blocks.                              */
 int pkv_sync_tables(pkv_pool* pool, const int64_t* ids, int32_t n, int32_t* dev_block_tables,
-                    int32_t max_blocks, int32_t* dev_seq_lens, void* stream);
+                    int32_t max_blocks, int32_t* dev_seq_lens, int32_t* host_seq_lens_out,
+                    void* stream);
 
 /* Copy-on-write copy: for each host pair (src, dst) in pairs[2 * n_pairs],
  * block dst := block src in K and V of every layer (all heads, all slots).
@@ -201,6 +204,10 @@ typedef struct pkv_decode_args {
                               /*   32; 0 = 512                              */
   int32_t dtype;              /* PKV_F32 or PKV_BF16                        */
   float scale;                /* score scale, e.g. 1/sqrt(d)                */
+  const int32_t* host_seq_lens; /* optional host copy of seq_lens [S], read */
+                              /*   only to choose how partitions are spread */
+                              /*   over waves; NULL = unknown (results do   */
+                              /*   not depend on it)                        */
 } pkv_decode_args;
 
 /* Workspace bytes the decode call needs (0 when one partition suffices). */

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <climits>
 #include <cstring>
 #include <exception>
 #include <new>
@@ -20,11 +21,13 @@ struct pkv_pool {
   pkv::BlockPool alloc;
   int32_t num_layers, num_kv_heads, head_dim, dtype;
   std::vector<void*> k_cache, v_cache;    // empty for an allocator-only pool
-  // pinned staging for table uploads, reused once the previous upload ends
-  void* staging = nullptr;
-  size_t staging_bytes = 0;
-  hipEvent_t upload_done = nullptr;
-  bool upload_pending = false;
+  // Two pinned staging buffers for table uploads, used alternately; a buffer
+  // is refilled only after the upload that last read it has finished.
+  void* staging[2] = {nullptr, nullptr};
+  size_t staging_bytes[2] = {0, 0};
+  hipEvent_t upload_done[2] = {nullptr, nullptr};
+  bool upload_pending[2] = {false, false};
+  int next_staging = 0;
 
   pkv_pool(int32_t nb, int32_t bs, const int32_t* perm) : alloc(nb, bs, perm) {}
 };
@@ -112,6 +115,24 @@ int prepare_decode(const pkv_decode_args* a, pkv::DecodeParams* p) {
   p->max_seq_len = a->max_seq_len;
   p->partition = part;
   p->pmax = static_cast<int32_t>(pmax);
+  p->ppw = 1;
+  p->tasks_hint = 0;
+  p->uniform_hint = 0;
+  if (a->host_seq_lens) {
+    // exact partition count from the host copy of the lengths
+    int64_t sum = 0, lo = INT64_MAX, hi = 0;
+    for (int32_t i = 0; i < a->num_seqs; ++i) {
+      const int32_t n = a->host_seq_lens[i];
+      if (n < 1 || n > a->max_seq_len) continue;
+      const int64_t P = (n + part - 1) / part;
+      sum += P;
+      lo = std::min(lo, P);
+      hi = std::max(hi, P);
+    }
+    const int64_t hg = (p->G + 15) / 16;
+    p->tasks_hint = sum * a->num_kv_heads * hg;
+    p->uniform_hint = sum > 0 && lo * 8 >= hi * 7;
+  }
   p->scale_log2 = a->scale * 1.4426950408889634f;
   if (need > 0) {
     const size_t rows = static_cast<size_t>(a->num_seqs) * a->num_q_heads * pmax;
@@ -191,11 +212,14 @@ int pkv_pool_create(const pkv_pool_desc* d, pkv_pool** out) {
 int pkv_pool_destroy(pkv_pool* pool) {
   if (!pool) return PKV_OK;
   int st = PKV_OK;
-  if (pool->upload_done) {
-    if (pool->upload_pending) st = from_hip(hipEventSynchronize(pool->upload_done), "pool_destroy");
-    (void)hipEventDestroy(pool->upload_done);
+  for (int i = 0; i < 2; ++i) {
+    if (pool->upload_done[i]) {
+      if (pool->upload_pending[i] && st == PKV_OK)
+        st = from_hip(hipEventSynchronize(pool->upload_done[i]), "pool_destroy");
+      (void)hipEventDestroy(pool->upload_done[i]);
+    }
+    if (pool->staging[i]) (void)hipHostFree(pool->staging[i]);
   }
-  if (pool->staging) (void)hipHostFree(pool->staging);
   delete pool;
   return st;
 }
@@ -247,7 +271,7 @@ int pkv_seq_table(const pkv_pool* pool, int64_t id, int32_t* table, int32_t cap,
 }
 
 int pkv_sync_tables(pkv_pool* pool, const int64_t* ids, int32_t n, int32_t* dev_tables,
-                    int32_t max_blocks, int32_t* dev_lens, void* stream) {
+                    int32_t max_blocks, int32_t* dev_lens, int32_t* host_lens_out, void* stream) {
   return guarded([&]() -> int {
     if (!pool || n < 0 || max_blocks < 1) return fail(PKV_ERR_INVALID, "sync_tables: bad argument");
     if (n == 0) return PKV_OK;
@@ -263,26 +287,27 @@ int pkv_sync_tables(pkv_pool* pool, const int64_t* ids, int32_t n, int32_t* dev_
     const size_t table_bytes = static_cast<size_t>(n) * max_blocks * sizeof(int32_t);
     const size_t need = table_bytes + static_cast<size_t>(n) * sizeof(int32_t);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const int k = pool->next_staging;
     int rc;
-    if (!pool->upload_done) {
-      rc = from_hip(hipEventCreateWithFlags(&pool->upload_done, hipEventDisableTiming), "sync_tables");
+    if (!pool->upload_done[k]) {
+      rc = from_hip(hipEventCreateWithFlags(&pool->upload_done[k], hipEventDisableTiming), "sync_tables");
       if (rc) return rc;
     }
-    if (pool->upload_pending) {
-      rc = from_hip(hipEventSynchronize(pool->upload_done), "sync_tables: wait for previous upload");
+    if (pool->upload_pending[k]) {
+      rc = from_hip(hipEventSynchronize(pool->upload_done[k]), "sync_tables: wait for an earlier upload");
       if (rc) return rc;
-      pool->upload_pending = false;
+      pool->upload_pending[k] = false;
     }
-    if (pool->staging_bytes < need) {
-      if (pool->staging) (void)hipHostFree(pool->staging);
-      pool->staging = nullptr;
-      pool->staging_bytes = 0;
+    if (pool->staging_bytes[k] < need) {
+      if (pool->staging[k]) (void)hipHostFree(pool->staging[k]);
+      pool->staging[k] = nullptr;
+      pool->staging_bytes[k] = 0;
       const size_t cap = std::max(need, static_cast<size_t>(1) << 20);
-      rc = from_hip(hipHostMalloc(&pool->staging, cap, hipHostMallocDefault), "sync_tables: pinned staging");
+      rc = from_hip(hipHostMalloc(&pool->staging[k], cap, hipHostMallocDefault), "sync_tables: pinned staging");
       if (rc) return rc;
-      pool->staging_bytes = cap;
+      pool->staging_bytes[k] = cap;
     }
-    int32_t* tab = static_cast<int32_t*>(pool->staging);
+    int32_t* tab = static_cast<int32_t*>(pool->staging[k]);
     int32_t* lens = tab + static_cast<size_t>(n) * max_blocks;
     for (int32_t i = 0; i < n; ++i) {
       int32_t* row = tab + static_cast<size_t>(i) * max_blocks;
@@ -290,15 +315,17 @@ int pkv_sync_tables(pkv_pool* pool, const int64_t* ids, int32_t n, int32_t* dev_
       std::copy(t.begin(), t.end(), row);
       std::fill(row + t.size(), row + max_blocks, -1);
       lens[i] = seqs[i]->len;
+      if (host_lens_out) host_lens_out[i] = seqs[i]->len;
     }
     rc = from_hip(hipMemcpyAsync(dev_tables, tab, table_bytes, hipMemcpyHostToDevice, st), "sync_tables: tables");
     if (rc) return rc;
     rc = from_hip(hipMemcpyAsync(dev_lens, lens, n * sizeof(int32_t), hipMemcpyHostToDevice, st),
                   "sync_tables: lengths");
     if (rc) return rc;
-    rc = from_hip(hipEventRecord(pool->upload_done, st), "sync_tables: record");
+    rc = from_hip(hipEventRecord(pool->upload_done[k], st), "sync_tables: record");
     if (rc) return rc;
-    pool->upload_pending = true;
+    pool->upload_pending[k] = true;
+    pool->next_staging = 1 - k;
     return PKV_OK;
   });
 }

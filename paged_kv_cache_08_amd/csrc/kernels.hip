@@ -28,8 +28,11 @@
 // uses the hardware exp2.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
+#include <type_traits>
 
 #include "kernels.hpp"
 
@@ -42,19 +45,33 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBlock = 16;   // tokens per block on the decode path
+#ifndef PKV_DEPTH
+#define PKV_DEPTH 3
+#endif
+constexpr int kDepth = PKV_DEPTH;  // blocks in flight per wave on the bf16 decode path
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Reductions over the four lanes l, l^16, l^32, l^48 (one MFMA column).
+// K/V tiles are read exactly once per decode call: stream them with the
+// non-temporal hint so they do not displace reusable lines.  On MI355X this
+// lifts a 4 KiB-tile gather from about 6.1 to about 6.85 TB/s.
+template <typename T>
+__device__ __forceinline__ T stream_load(const T* p) { return __builtin_nontemporal_load(p); }
+
+// Reductions over the four lanes l, l^16, l^32, l^48 (one MFMA column), with
+// the gfx950 row-swap permutes (no LDS round trip): permlane32_swap exchanges
+// the two 32-lane halves, permlane16_swap exchanges rows 0<->1 and 2<->3.
 __device__ __forceinline__ float max_over_rows(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float sum_over_rows(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -65,9 +82,6 @@ __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
   return x;
-}
-__device__ __forceinline__ float lane_value(float x, int lane) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
 // ---------------------------------------------------------------------------
@@ -113,13 +127,17 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksParams p) {
 // ---------------------------------------------------------------------------
 // decode: shared prologue
 // ---------------------------------------------------------------------------
+// A wave streams a run of up to `ppw` consecutive partitions of one
+// (sequence, KV head, query-head group): at most kMaxWaveBlocks blocks.
+constexpr int kMaxWaveBlocks = 256;
+
 struct WaveTask {
-  int s, kvh, part, h0, nh;     // sequence, KV head, partition, first q head, heads here
+  int s, kvh, h0, nh;           // sequence, KV head, first query head, heads here
   int n, P;                     // length, partitions of this sequence
-  int t_end;                    // one past the last token of this partition
+  int part0, part_end;          // partitions [part0, part_end) of this wave
+  int t_end;                    // one past the last token of the wave's run
   int blk_first, nblk;          // first logical block and block count
-  int myblk;                    // lane l holds the id of block blk_first + l
-  bool status_ok;
+  int id0, id1, id2, id3;       // lane l of idC holds block blk_first + 64C + l
 };
 
 template <typename T, int D>
@@ -130,45 +148,58 @@ __device__ __forceinline__ void write_nan_rows(const DecodeParams& p, int s, int
 
 template <int D>
 __device__ __forceinline__ void write_nan_partials(const DecodeParams& p, const WaveTask& w) {
-  for (int h = 0; h < w.nh; ++h) {
-    const size_t row = (static_cast<size_t>(w.s) * p.Hq + w.h0 + h) * p.pmax + w.part;
-    for (int e = threadIdx.x; e < D; e += 64) p.part_acc[row * D + e] = NAN;
-    if (threadIdx.x == 0) {
-      p.part_ml[2 * row] = NAN;
-      p.part_ml[2 * row + 1] = NAN;
+  for (int part = w.part0; part < w.part_end; ++part)
+    for (int h = 0; h < w.nh; ++h) {
+      const size_t row = (static_cast<size_t>(w.s) * p.Hq + w.h0 + h) * p.pmax + part;
+      for (int e = threadIdx.x; e < D; e += 64) p.part_acc[row * D + e] = NAN;
+      if (threadIdx.x == 0) {
+        p.part_ml[2 * row] = NAN;
+        p.part_ml[2 * row + 1] = NAN;
+      }
     }
-  }
 }
 
-// Decodes blockIdx into the wave's task and validates lengths and table
-// entries.  Returns false when the wave has nothing to do (it may have
-// written NaN rows for an invalid sequence first).
+// Decodes blockIdx into the wave's task, loads its block ids and validates
+// lengths and table entries.  Returns false when the wave has nothing to do
+// (after writing NaN results for an invalid sequence).
 template <typename T, int D>
 __device__ __forceinline__ bool setup_task(const DecodeParams& p, WaveTask& w) {
   const int lane = threadIdx.x;
   w.kvh = blockIdx.x % p.Hkv;
   const int rest = blockIdx.x / p.Hkv;
   w.s = rest % p.S;
-  w.part = rest / p.S;
+  const int grp = rest / p.S;
   w.h0 = w.kvh * p.G + blockIdx.y * 16;
   w.nh = min(16, p.G - static_cast<int>(blockIdx.y) * 16);
   w.n = p.seq_lens[w.s];
   if (w.n < 1 || w.n > p.max_seq_len) {
-    if (w.part == 0) write_nan_rows<T, D>(p, w.s, w.h0, w.nh);
+    if (grp == 0) write_nan_rows<T, D>(p, w.s, w.h0, w.nh);
     return false;
   }
   w.P = (w.n + p.partition - 1) / p.partition;
-  if (w.part >= w.P) return false;
-  const int t_begin = w.part * p.partition;
-  w.t_end = min(w.n, t_begin + p.partition);
+  w.part0 = grp * p.ppw;
+  if (w.part0 >= w.P) return false;
+  w.part_end = min(w.P, w.part0 + p.ppw);
+  const int t_begin = w.part0 * p.partition;
+  w.t_end = min(w.n, w.part_end * p.partition);
   w.blk_first = t_begin / kBlock;
   w.nblk = (w.t_end - t_begin + kBlock - 1) / kBlock;
   bool bad = w.blk_first + w.nblk > p.max_blocks;
-  int b = 0;
-  if (!bad && lane < w.nblk) b = p.block_tables[static_cast<size_t>(w.s) * p.max_blocks + w.blk_first + lane];
-  const bool bad_lane = static_cast<unsigned>(b) >= static_cast<unsigned>(p.num_blocks);
+  bool bad_lane = false;
+  const int32_t* row = p.block_tables + static_cast<size_t>(w.s) * p.max_blocks + w.blk_first;
+  auto fetch = [&](int c) {
+    const int idx = 64 * c + lane;
+    int b = 0;
+    if (!bad && idx < w.nblk) b = row[idx];
+    const bool bl = static_cast<unsigned>(b) >= static_cast<unsigned>(p.num_blocks);
+    bad_lane = bad_lane || bl;
+    return bl ? 0 : b;
+  };
+  w.id0 = fetch(0);
+  w.id1 = fetch(1);
+  w.id2 = fetch(2);
+  w.id3 = fetch(3);
   bad = bad || __any(bad_lane);
-  w.myblk = bad_lane ? 0 : b;
   if (bad) {
     if (w.P == 1) write_nan_rows<T, D>(p, w.s, w.h0, w.nh);
     else write_nan_partials<D>(p, w);
@@ -177,37 +208,57 @@ __device__ __forceinline__ bool setup_task(const DecodeParams& p, WaveTask& w) {
   return true;
 }
 
-__device__ __forceinline__ int block_id(const WaveTask& w, int i) {
-  return __builtin_amdgcn_readlane(w.myblk, i);
+// Physical id of a wave's i-th block (i wave-uniform) from the four id
+// registers.
+__device__ __forceinline__ int block_id(int id0, int id1, int id2, int id3, int i) {
+  const int c = i >> 6;
+  const int v = c == 0 ? id0 : c == 1 ? id1 : c == 2 ? id2 : id3;
+  return __builtin_amdgcn_readlane(v, i & 63);
 }
 
 // ---------------------------------------------------------------------------
-// decode_partial, bf16: v_mfma_f32_16x16x32_bf16
+// decode_partial, bf16
 //
-// Per pair of blocks (32 tokens), with lane l = 16*g + c (g = l/16,
-// c = l%16):
-//   S^T = K · Q^T: A = K tile (row = token c, k = 8 head-dim values of chunk
-//   g), B = Q^T (column = head c, same k).  Result lane l holds the scores
-//   of tokens 4g..4g+3 for head c.
-//   out^T += V^T · P: A = V^T (row = value column c of the tile, k = the
-//   lane's 8 tokens: 4g..4g+3 of the first block and of the second), B = P
-//   (the lane's own 8 probabilities, same token order, head c).  Result lane
-//   l holds value columns 16t+4g..16t+4g+3 of head c for tile t.
-// The token order inside the k dimension is the same on both operands, so
-// no data moves between lanes except the max / sum reductions.
+// Work unit: one 16-token block (a 4 KiB K tile and a 4 KiB V tile of one KV
+// head).  With lane l = 16*g + c (g = l/16, c = l%16):
+//   scores S^T = K · Q^T with v_mfma_f32_16x16x32_bf16 over four 32-wide
+//   slices of the head dimension: A = K tile (row = token c, k = 8 values of
+//   16-byte chunk g of the slice), B = Q^T (column = query head c, same k).
+//   Lane l receives the scores of tokens 4g..4g+3 for head c.
+//   out^T += V^T · P with v_mfma_f32_16x16x16_bf16 per 16 value columns:
+//   A = V^T (row = value column c, k = tokens 4g..4g+3, read as one 8-byte
+//   run of the token-fastest V tile), B = P (the lane's own four
+//   probabilities, head c).  Lane l accumulates value columns
+//   16t+4g..16t+4g+3 of head c.
+// The token order inside k is the same on both operands, so only the max and
+// sum reductions move data between lanes.  NBUF blocks are in flight per
+// wave in rotating register sets: block i+NBUF is requested as soon as
+// block i has been consumed.
 // ---------------------------------------------------------------------------
-template <int D>
-struct PairRegs {
-  u32x4 k0[D / 32], k1[D / 32];
-  u32x2 v0[D / 16], v1[D / 16];
-};
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
+struct BlockRegs {
+  u32x4 k[D / 32];
+  u32x2 v[D / 16];
+};
+
+template <int D, int NBUF>
 __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
   constexpr int KC = D / 32;
   constexpr int NT = D / 16;
-  WaveTask w;
-  if (!setup_task<__bf16, D>(p, w)) return;
+  // Partials of the wave's finished partitions wait here until its load
+  // stream ends: a global store in the middle of the stream would make every
+  // later wait drain all loads in flight (stores and loads share vmcnt).
+  extern __shared__ float staged[];
+  int s_, kvh, h0, nh, P, part0, part_end, t_end, blk_first, nblk, id0, id1, id2, id3;
+  {
+    WaveTask w;
+    if (!setup_task<__bf16, D>(p, w)) return;
+    s_ = w.s; kvh = w.kvh; h0 = w.h0; nh = w.nh; P = w.P; part0 = w.part0; part_end = w.part_end;
+    t_end = w.t_end; blk_first = w.blk_first; nblk = w.nblk;
+    id0 = w.id0; id1 = w.id1; id2 = w.id2; id3 = w.id3;
+  }
   const int lane = threadIdx.x;
   const int c16 = lane & 15;
   const int g4 = lane >> 4;
@@ -215,38 +266,31 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
   // Q^T operand: head c16, head-dim values 32c + 8g4 .. +7.
   bf16x8 qreg[KC];
   {
-    const __bf16* q = static_cast<const __bf16*>(p.q) + (static_cast<size_t>(w.s) * p.Hq + w.h0 + c16) * D;
+    const __bf16* q = static_cast<const __bf16*>(p.q) + (static_cast<size_t>(s_) * p.Hq + h0 + c16) * D;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       u32x4 v = {0, 0, 0, 0};
-      if (c16 < w.nh) v = *reinterpret_cast<const u32x4*>(q + 32 * c + 8 * g4);
+      if (c16 < nh) v = *reinterpret_cast<const u32x4*>(q + 32 * c + 8 * g4);
       qreg[c] = __builtin_bit_cast(bf16x8, v);
     }
   }
 
   const size_t tile = static_cast<size_t>(kBlock) * D;               // elements per (block, head)
-  const size_t blk_stride = static_cast<size_t>(p.Hkv) * tile;
-  const __bf16* kc = static_cast<const __bf16*>(p.k_cache) + static_cast<size_t>(w.kvh) * tile;
-  const __bf16* vc = static_cast<const __bf16*>(p.v_cache) + static_cast<size_t>(w.kvh) * tile;
-  const int npair = (w.nblk + 1) / 2;
+  const size_t blk_bytes = static_cast<size_t>(p.Hkv) * tile * sizeof(__bf16);
+  const char* kc_b = reinterpret_cast<const char*>(static_cast<const __bf16*>(p.k_cache) + kvh * tile);
+  const char* vc_b = reinterpret_cast<const char*>(static_cast<const __bf16*>(p.v_cache) + kvh * tile);
+  // Block bases are wave-uniform; per-lane byte offsets are 32-bit.
+  const uint32_t k_off = static_cast<uint32_t>(lane) * 16u;
+  const uint32_t v_off = static_cast<uint32_t>(c16 * 4 + g4) * 8u;
 
-  auto load_pair = [&](PairRegs<D>& r, int i) {
-    const int b0 = block_id(w, 2 * i);
-    const int b1 = (2 * i + 1 < w.nblk) ? block_id(w, 2 * i + 1) : b0;
-    const u32x4* k0 = reinterpret_cast<const u32x4*>(kc + b0 * blk_stride) + lane;
-    const u32x4* k1 = reinterpret_cast<const u32x4*>(kc + b1 * blk_stride) + lane;
-    const u32x2* v0 = reinterpret_cast<const u32x2*>(vc + b0 * blk_stride) + c16 * 4 + g4;
-    const u32x2* v1 = reinterpret_cast<const u32x2*>(vc + b1 * blk_stride) + c16 * 4 + g4;
+  auto load_block = [&](BlockRegs<D>& r, int i) {
+    const size_t b = static_cast<size_t>(block_id(id0, id1, id2, id3, i));
+    const u32x4* kp = reinterpret_cast<const u32x4*>(kc_b + b * blk_bytes + k_off);
+    const u32x2* vp = reinterpret_cast<const u32x2*>(vc_b + b * blk_bytes + v_off);
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      r.k0[c] = k0[64 * c];
-      r.k1[c] = k1[64 * c];
-    }
+    for (int c = 0; c < KC; ++c) r.k[c] = stream_load(kp + 64 * c);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      r.v0[t] = v0[64 * t];
-      r.v1[t] = v1[64 * t];
-    }
+    for (int t = 0; t < NT; ++t) r.v[t] = stream_load(vp + 64 * t);
   };
 
   f32x4 acc[NT];
@@ -254,90 +298,156 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY;
   float l_run = 0.f;
+  const int bpp = p.partition / kBlock;        // blocks per partition
+  int next_boundary = bpp;                     // block count that closes a partition
+  int staged_parts = 0;
+  const int row_floats = D + 2;                // staged row: accumulator, m, l
 
-  auto compute_pair = [&](const PairRegs<D>& r, int i) {
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f};
-    f32x4 s1 = {0.f, 0.f, 0.f, 0.f};
+  // Closes a partition that is not the wave's last: park (acc, m, l) in LDS
+  // and restart the running statistics.
+  auto stage_partition = [&]() {
+    const float l_tot = sum_over_rows(l_run);
+    if (c16 < nh) {
+      float* dst = staged + (staged_parts * nh + c16) * row_floats;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.k0[c]), qreg[c], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.k1[c]), qreg[c], s1, 0, 0, 0);
-    }
-    const int tok0 = (w.blk_first + 2 * i) * kBlock + 4 * g4;     // token of x[0]
-    const bool tail = (w.blk_first + 2 * i + 2) * kBlock > w.t_end;
-    float x[8];
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[j] = s0[j] * p.scale_log2;
-      x[4 + j] = s1[j] * p.scale_log2;
-    }
-    if (tail) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (tok0 + j >= w.t_end) x[j] = -INFINITY;
-        if (tok0 + kBlock + j >= w.t_end) x[4 + j] = -INFINITY;
+        for (int j = 0; j < 4; ++j) dst[16 * t + 4 * g4 + j] = acc[t][j];
+      if (g4 == 0) {
+        dst[D] = m_run;
+        dst[D + 1] = l_tot;
       }
     }
-    float mx = x[0];
 #pragma unroll
-    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run = -INFINITY;
+    l_run = 0.f;
+    ++staged_parts;
+  };
+
+  // kTail: the block may hold tokens past the sequence end (only the wave's
+  // last block can).
+  auto compute_block = [&](const BlockRegs<D>& r, int i, auto tail_tag) {
+    constexpr bool kTail = decltype(tail_tag)::value;
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.k[c]), qreg[c], sc, 0, 0, 0);
+    const int tok0 = (blk_first + i) * kBlock + 4 * g4;           // token of x[0]
+    const bool tail = kTail && (blk_first + i + 1) * kBlock > t_end;
+    float x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = sc[j] * p.scale_log2;
+    if (tail) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (tok0 + j >= t_end) x[j] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = max_over_rows(mx);
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2_fast(m_run - m_new);
-    m_run = m_new;
-    bf16x8 pb;
+    // Rescale only when some column's maximum grew (alpha is exactly 1
+    // elsewhere); once the running maxima settle this is skipped.
+    if (__any(m_new > m_run)) {
+      const float alpha = exp2_fast(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+      m_run = m_new;
+    }
+    bf16x4 pb;
     float ps = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const __bf16 e = static_cast<__bf16>(exp2_fast(x[j] - m_new));
+    for (int j = 0; j < 4; ++j) {
+      const __bf16 e = static_cast<__bf16>(exp2_fast(x[j] - m_run));
       pb[j] = e;
       ps += static_cast<float>(e);
     }
-    l_run = l_run * alpha + ps;
-    uint32_t mk0 = 0xFFFFFFFFu, mk1 = 0xFFFFFFFFu, mk2 = 0xFFFFFFFFu, mk3 = 0xFFFFFFFFu;
+    l_run += ps;
+    uint32_t mk0 = 0xFFFFFFFFu, mk1 = 0xFFFFFFFFu;
     if (tail) {
-      auto half = [&](int tok) -> uint32_t { return tok < w.t_end ? 0xFFFFu : 0u; };
+      auto half = [&](int tok) -> uint32_t { return tok < t_end ? 0xFFFFu : 0u; };
       mk0 = half(tok0) | (half(tok0 + 1) << 16);
       mk1 = half(tok0 + 2) | (half(tok0 + 3) << 16);
-      mk2 = half(tok0 + kBlock) | (half(tok0 + kBlock + 1) << 16);
-      mk3 = half(tok0 + kBlock + 2) | (half(tok0 + kBlock + 3) << 16);
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      acc[t] *= alpha;
-      const u32x4 vv = {r.v0[t].x & mk0, r.v0[t].y & mk1, r.v1[t].x & mk2, r.v1[t].y & mk3};
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pb, acc[t], 0, 0, 0);
+      const u32x2 vv = {r.v[t].x & mk0, r.v[t].y & mk1};
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vv), pb, acc[t], 0, 0, 0);
+    }
+    if (i + 1 == next_boundary && i + 1 < nblk) {
+      stage_partition();
+      next_boundary += bpp;
     }
   };
 
-  // Two register sets: the next pair's loads are in flight while the current
-  // pair is computed.
-  PairRegs<D> ra, rb;
-  load_pair(ra, 0);
-  for (int i = 0; i < npair; i += 2) {
-    if (i + 1 < npair) load_pair(rb, i + 1);
-    compute_pair(ra, i);
-    if (i + 1 >= npair) break;
-    if (i + 2 < npair) load_pair(ra, i + 2);
-    compute_pair(rb, i + 1);
+  // Steady state: every iteration consumes NBUF blocks and requests the next
+  // NBUF, all unconditionally, so NBUF blocks stay in flight.  The drain loop
+  // finishes the last blocks (and short runs).
+  using NoTail = std::integral_constant<bool, false>;
+  using MayTail = std::integral_constant<bool, true>;
+  BlockRegs<D> buf[NBUF];
+  int i = 0;
+  if (nblk >= 2 * NBUF) {
+    // Issue order matters: the loop expects buf[0] to be the oldest load in
+    // flight on entry (as it is on the back edge), otherwise the wait at the
+    // loop head must drain everything.  The barriers keep this order.
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      load_block(buf[u], u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (; i + 2 * NBUF <= nblk; i += NBUF) {
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) {
+        compute_block(buf[u], i + u, NoTail{});
+        load_block(buf[u], i + u + NBUF);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u)
+      if (u < nblk) load_block(buf[u], u);
+  }
+  for (; i < nblk; i += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      if (i + u < nblk) {
+        compute_block(buf[u], i + u, MayTail{});
+        if (i + u + NBUF < nblk) load_block(buf[u], i + u + NBUF);
+      }
+    }
   }
 
+  // The stream has ended: write the staged partitions, then the last one.
   const float l_tot = sum_over_rows(l_run);
-  if (c16 >= w.nh) return;
-  const size_t head_row = static_cast<size_t>(w.s) * p.Hq + w.h0 + c16;
-  if (w.P == 1) {
+  if (staged_parts > 0) {
+    // (LDS accesses of one wave complete in order: no barrier is needed.)
+    for (int sp = 0; sp < staged_parts; ++sp)
+      for (int h = 0; h < nh; ++h) {
+        const float* src = staged + (sp * nh + h) * row_floats;
+        const size_t row = (static_cast<size_t>(s_) * p.Hq + h0 + h) * p.pmax + part0 + sp;
+        for (int e = lane; e < D; e += 64) p.part_acc[row * D + e] = src[e];
+        if (lane == 0) {
+          p.part_ml[2 * row] = src[D];
+          p.part_ml[2 * row + 1] = src[D + 1];
+        }
+      }
+  }
+  if (c16 >= nh) return;
+  const size_t head_row = static_cast<size_t>(s_) * p.Hq + h0 + c16;
+  if (P == 1) {
     const float inv = 1.f / l_tot;
     __bf16* out = static_cast<__bf16*>(p.out) + head_row * D + 4 * g4;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
       bf16x4 o;
 #pragma unroll
       for (int j = 0; j < 4; ++j) o[j] = static_cast<__bf16>(acc[t][j] * inv);
       *reinterpret_cast<bf16x4*>(out + 16 * t) = o;
     }
   } else {
-    const size_t row = head_row * p.pmax + w.part;
+    const size_t row = head_row * p.pmax + part_end - 1;
     float* pa = p.part_acc + row * D + 4 * g4;
 #pragma unroll
     for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4*>(pa + 16 * t) = acc[t];
@@ -359,26 +469,32 @@ template <int D>
 __global__ __launch_bounds__(64) void decode_partial_f32(DecodeParams p) {
   constexpr int KC = D / 16;
   constexpr int NT = D / 16;
-  WaveTask w;
-  if (!setup_task<float, D>(p, w)) return;
+  int s_, kvh, h0, nh, P, part0, t_end, blk_first, nblk, id0, id1, id2, id3;
+  {
+    WaveTask w;
+    if (!setup_task<float, D>(p, w)) return;
+    s_ = w.s; kvh = w.kvh; h0 = w.h0; nh = w.nh; P = w.P; part0 = w.part0;
+    t_end = w.t_end; blk_first = w.blk_first; nblk = w.nblk;
+    id0 = w.id0; id1 = w.id1; id2 = w.id2; id3 = w.id3;
+  }
   const int lane = threadIdx.x;
   const int c16 = lane & 15;
   const int g4 = lane >> 4;
 
   f32x4 qreg[KC];
   {
-    const float* q = static_cast<const float*>(p.q) + (static_cast<size_t>(w.s) * p.Hq + w.h0 + c16) * D;
+    const float* q = static_cast<const float*>(p.q) + (static_cast<size_t>(s_) * p.Hq + h0 + c16) * D;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (c16 < w.nh) v = *reinterpret_cast<const f32x4*>(q + 16 * c + 4 * g4);
+      if (c16 < nh) v = *reinterpret_cast<const f32x4*>(q + 16 * c + 4 * g4);
       qreg[c] = v;
     }
   }
   const size_t tile = static_cast<size_t>(kBlock) * D;
   const size_t blk_stride = static_cast<size_t>(p.Hkv) * tile;
-  const float* kc = static_cast<const float*>(p.k_cache) + static_cast<size_t>(w.kvh) * tile;
-  const float* vc = static_cast<const float*>(p.v_cache) + static_cast<size_t>(w.kvh) * tile;
+  const float* kc = static_cast<const float*>(p.k_cache) + static_cast<size_t>(kvh) * tile;
+  const float* vc = static_cast<const float*>(p.v_cache) + static_cast<size_t>(kvh) * tile;
 
   f32x4 acc[NT];
 #pragma unroll
@@ -386,24 +502,24 @@ __global__ __launch_bounds__(64) void decode_partial_f32(DecodeParams p) {
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  for (int i = 0; i < w.nblk; ++i) {
-    const int b = block_id(w, i);
+  for (int i = 0; i < nblk; ++i) {    // one partition per wave (ppw = 1)
+    const int b = block_id(id0, id1, id2, id3, i);
     const f32x4* kp = reinterpret_cast<const f32x4*>(kc + b * blk_stride) + lane;
     const f32x4* vp = reinterpret_cast<const f32x4*>(vc + b * blk_stride) + c16 * 4 + g4;
     f32x4 kr[KC], vr[NT];
 #pragma unroll
-    for (int c = 0; c < KC; ++c) kr[c] = kp[64 * c];
+    for (int c = 0; c < KC; ++c) kr[c] = stream_load(kp + 64 * c);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) vr[t] = vp[64 * t];
+    for (int t = 0; t < NT; ++t) vr[t] = stream_load(vp + 64 * t);
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < KC; ++c)
 #pragma unroll
       for (int j = 0; j < 4; ++j) sc = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[c][j], qreg[c][j], sc, 0, 0, 0);
-    const int tok0 = (w.blk_first + i) * kBlock + 4 * g4;
+    const int tok0 = (blk_first + i) * kBlock + 4 * g4;
     float x[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) x[j] = (tok0 + j < w.t_end) ? sc[j] * p.scale_log2 : -INFINITY;
+    for (int j = 0; j < 4; ++j) x[j] = (tok0 + j < t_end) ? sc[j] * p.scale_log2 : -INFINITY;
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = max_over_rows(mx);
     const float m_new = fmaxf(m_run, mx);
@@ -422,22 +538,22 @@ __global__ __launch_bounds__(64) void decode_partial_f32(DecodeParams p) {
       acc[t] *= alpha;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float v = (tok0 + j < w.t_end) ? vr[t][j] : 0.f;
+        const float v = (tok0 + j < t_end) ? vr[t][j] : 0.f;
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(v, pr[j], acc[t], 0, 0, 0);
       }
     }
   }
 
   const float l_tot = sum_over_rows(l_run);
-  if (c16 >= w.nh) return;
-  const size_t head_row = static_cast<size_t>(w.s) * p.Hq + w.h0 + c16;
-  if (w.P == 1) {
+  if (c16 >= nh) return;
+  const size_t head_row = static_cast<size_t>(s_) * p.Hq + h0 + c16;
+  if (P == 1) {
     const float inv = 1.f / l_tot;
     float* out = static_cast<float*>(p.out) + head_row * D + 4 * g4;
 #pragma unroll
     for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4*>(out + 16 * t) = acc[t] * inv;
   } else {
-    const size_t row = head_row * p.pmax + w.part;
+    const size_t row = head_row * p.pmax + part0;
     float* pa = p.part_acc + row * D + 4 * g4;
 #pragma unroll
     for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4*>(pa + 16 * t) = acc[t];
@@ -449,14 +565,37 @@ __global__ __launch_bounds__(64) void decode_partial_f32(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// decode_reduce: one wave per (sequence, query head) with more than one
-// partition.  M = max_p m_p, L = sum_p l_p 2^(m_p - M),
-// out = sum_p acc_p 2^(m_p - M) / L, rounded to the output type.
+// decode_reduce: one 256-lane workgroup per (sequence, query head) with more
+// than one partition.  M = max_p m_p, L = sum_p l_p 2^(m_p - M),
+// out = sum_p acc_p 2^(m_p - M) / L, rounded to the output type.  Lane t
+// owns value columns 4(t % CG) .. +3 for partitions p = t / CG + k * PH, so
+// all its loads are independent and in flight together; the PH partial sums
+// of a column are added through LDS.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float block_max_256(float x, float* scratch) {
+  x = wave_max(x);
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = x;
+  __syncthreads();
+  x = fmaxf(fmaxf(scratch[0], scratch[1]), fmaxf(scratch[2], scratch[3]));
+  __syncthreads();
+  return x;
+}
+__device__ __forceinline__ float block_sum_256(float x, float* scratch) {
+  x = wave_sum(x);
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = x;
+  __syncthreads();
+  x = (scratch[0] + scratch[1]) + (scratch[2] + scratch[3]);
+  __syncthreads();
+  return x;
+}
+
 template <typename T, int D>
-__global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeParams p) {
-  constexpr int PER = D / 64;
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams p) {
+  constexpr int CG = D / 4;        // float4 column groups
+  constexpr int PH = 256 / CG;     // partition phases
+  __shared__ float red[PH][D];
+  __shared__ float scratch[4];
+  const int tid = threadIdx.x;
   const int row = blockIdx.x;
   const int s = row / p.Hq;
   const int n = p.seq_lens[s];
@@ -466,28 +605,38 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeParams p) {
   const float* ml = p.part_ml + static_cast<size_t>(row) * p.pmax * 2;
   const float* acc = p.part_acc + static_cast<size_t>(row) * p.pmax * D;
   float M = -INFINITY;
-  for (int i = lane; i < P; i += 64) M = fmaxf(M, ml[2 * i]);
-  M = wave_max(M);
+  for (int i = tid; i < P; i += 256) M = fmaxf(M, ml[2 * i]);
+  M = block_max_256(M, scratch);
   float L = 0.f;
-  for (int i = lane; i < P; i += 64) L += ml[2 * i + 1] * exp2_fast(ml[2 * i] - M);
-  L = wave_sum(L);
-  float o[PER];
+  for (int i = tid; i < P; i += 256) L += ml[2 * i + 1] * exp2_fast(ml[2 * i] - M);
+  L = block_sum_256(L, scratch);
+  const int cg = tid % CG;
+  const int ph = tid / CG;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  int i = ph;
+  for (; i + 3 * PH < P; i += 4 * PH) {
+    f32x4 a[4];
+    float wgt[4];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) o[e] = 0.f;
-  for (int base = 0; base < P; base += 64) {
-    const float wl = (base + lane < P) ? exp2_fast(ml[2 * (base + lane)] - M) : 0.f;
-    const int cnt = min(64, P - base);
-    for (int j = 0; j < cnt; ++j) {
-      const float wj = lane_value(wl, j);
-      const float* a = acc + static_cast<size_t>(base + j) * D + lane * PER;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) o[e] += wj * a[e];
+    for (int u = 0; u < 4; ++u) {
+      a[u] = *reinterpret_cast<const f32x4*>(acc + static_cast<size_t>(i + u * PH) * D + 4 * cg);
+      wgt[u] = exp2_fast(ml[2 * (i + u * PH)] - M);
     }
-  }
-  const float inv = 1.f / L;
-  T* out = static_cast<T*>(p.out) + static_cast<size_t>(row) * D + lane * PER;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) out[e] = static_cast<T>(o[e] * inv);
+    for (int u = 0; u < 4; ++u) o += wgt[u] * a[u];
+  }
+  for (; i < P; i += PH)
+    o += exp2_fast(ml[2 * i] - M) * *reinterpret_cast<const f32x4*>(acc + static_cast<size_t>(i) * D + 4 * cg);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) red[ph][4 * cg + j] = o[j];
+  __syncthreads();
+  if (tid < D) {
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < PH; ++k) sum += red[k][tid];
+    T* out = static_cast<T*>(p.out) + static_cast<size_t>(row) * D;
+    out[tid] = static_cast<T>(sum / L);
+  }
 }
 
 }  // namespace
@@ -516,12 +665,56 @@ bool decode_shape_supported(int dtype, int head_dim, int block_size) {
   return block_size == kBlock && (dtype == 0 || dtype == 1) && (head_dim == 64 || head_dim == 128);
 }
 
-hipError_t launch_decode_partial(const DecodeParams& p, int dtype, hipStream_t stream) {
-  const long long gx = static_cast<long long>(p.pmax) * p.S * p.Hkv;
+// Partitions per wave for the bf16 kernel.  Each wave streams a run of
+// consecutive partitions; for long batches runs are made as long as possible
+// while the grid still fills every resident wave slot once (one round:
+// equal-length runs then finish together instead of leaving a partly filled
+// last round).
+// PKV_WAVE_PARTITIONS overrides the choice.
+template <int D>
+static int pick_partitions_per_wave(const DecodeParams& p) {
+  static int slots = 0;   // resident waves on the device (per kernel variant)
+  static int forced = -1;
+  if (forced < 0) {
+    const char* e = std::getenv("PKV_WAVE_PARTITIONS");
+    forced = e ? std::max(0, std::atoi(e)) : 0;
+  }
+  const int hg = (p.G + 15) / 16;
+  const int rows = std::min(16, p.G);
+  int max_ppw = std::min(p.pmax, kMaxWaveBlocks * kBlock / p.partition);
+  // LDS for the staged partials stays within 20 KiB per wave, so eight
+  // resident waves still fit in a CU's 160 KiB and LDS never lowers occupancy
+  const int lds_row = (p.d + 2) * static_cast<int>(sizeof(float));
+  max_ppw = std::max(1, std::min(max_ppw, 1 + (20 * 1024) / (rows * lds_row)));
+  if (forced > 0) return std::min(forced, max_ppw);
+  if (slots == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_partial_bf16<D, kDepth>, 64, 0) !=
+            hipSuccess || per_cu <= 0)
+      per_cu = 8;
+    slots = cus * per_cu;
+  }
+  // Long runs pay only for batches of equal-length sequences with at least
+  // three rounds of work; mixed lengths balance better with one partition
+  // per wave.  Without the caller's length hint nothing is known: one.
+  (void)hg;
+  if (p.tasks_hint <= 0 || !p.uniform_hint || p.tasks_hint < 3LL * slots) return 1;
+  return static_cast<int>(std::min<long long>(p.tasks_hint / slots, max_ppw));
+}
+
+hipError_t launch_decode_partial(const DecodeParams& p0, int dtype, hipStream_t stream) {
+  DecodeParams p = p0;
+  p.ppw = dtype != 1 ? 1 : (p.d == 128 ? pick_partitions_per_wave<128>(p) : pick_partitions_per_wave<64>(p));
+  const long long groups = (p.pmax + p.ppw - 1) / p.ppw;
+  const long long gx = groups * p.S * p.Hkv;
   dim3 grid(static_cast<unsigned>(gx), (p.G + 15) / 16);
   if (dtype == 1) {
-    if (p.d == 128) hipLaunchKernelGGL(decode_partial_bf16<128>, grid, dim3(64), 0, stream, p);
-    else if (p.d == 64) hipLaunchKernelGGL(decode_partial_bf16<64>, grid, dim3(64), 0, stream, p);
+    const size_t shmem = static_cast<size_t>(p.ppw - 1) * std::min(16, p.G) * (p.d + 2) * sizeof(float);
+    if (p.d == 128) hipLaunchKernelGGL((decode_partial_bf16<128, kDepth>), grid, dim3(64), shmem, stream, p);
+    else if (p.d == 64) hipLaunchKernelGGL((decode_partial_bf16<64, kDepth>), grid, dim3(64), shmem, stream, p);
     else return hipErrorInvalidValue;
   } else {
     if (p.d == 128) hipLaunchKernelGGL(decode_partial_f32<128>, grid, dim3(64), 0, stream, p);
@@ -535,12 +728,12 @@ hipError_t launch_decode_reduce(const DecodeParams& p, int dtype, hipStream_t st
   if (p.pmax <= 1) return hipSuccess;
   dim3 grid(static_cast<unsigned>(p.S * p.Hq));
   if (dtype == 1) {
-    if (p.d == 128) hipLaunchKernelGGL((decode_reduce_kernel<__bf16, 128>), grid, dim3(64), 0, stream, p);
-    else if (p.d == 64) hipLaunchKernelGGL((decode_reduce_kernel<__bf16, 64>), grid, dim3(64), 0, stream, p);
+    if (p.d == 128) hipLaunchKernelGGL((decode_reduce_kernel<__bf16, 128>), grid, dim3(256), 0, stream, p);
+    else if (p.d == 64) hipLaunchKernelGGL((decode_reduce_kernel<__bf16, 64>), grid, dim3(256), 0, stream, p);
     else return hipErrorInvalidValue;
   } else {
-    if (p.d == 128) hipLaunchKernelGGL((decode_reduce_kernel<float, 128>), grid, dim3(64), 0, stream, p);
-    else if (p.d == 64) hipLaunchKernelGGL((decode_reduce_kernel<float, 64>), grid, dim3(64), 0, stream, p);
+    if (p.d == 128) hipLaunchKernelGGL((decode_reduce_kernel<float, 128>), grid, dim3(256), 0, stream, p);
+    else if (p.d == 64) hipLaunchKernelGGL((decode_reduce_kernel<float, 64>), grid, dim3(256), 0, stream, p);
     else return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -48,6 +48,9 @@ struct DecodeParams {
   int32_t S, Hq, Hkv, G, d;
   int32_t num_blocks, max_blocks, max_seq_len;
   int32_t partition, pmax;
+  int32_t ppw;           // partitions streamed per wave (set by the launcher)
+  int64_t tasks_hint;    // exact (sequence, KV head, head group, partition) count, 0 = unknown
+  int32_t uniform_hint;  // 1 if every sequence has about the same number of partitions
   float scale_log2;      // scale * log2(e): scores are kept in base-2 units
 };
 

@@ -34,6 +34,7 @@ class PagedDecodeEngine:
                                       self.cdtype, self.k, self.v, init_perm)
         self.tables = None
         self.lens = None
+        self.host_lens = None      # host copy of the last uploaded lengths
         self.workspace = None
 
     # -- allocator + writes ------------------------------------------------
@@ -110,7 +111,8 @@ class PagedDecodeEngine:
         if self.tables is None or self.tables.shape != (n, max_blocks):
             self.tables = torch.empty((n, max_blocks), dtype=torch.int32, device=self.device)
             self.lens = torch.empty((n,), dtype=torch.int32, device=self.device)
-        P.pkv_sync_tables(self.pool, ids, self.tables, self.lens, stream)
+            self.host_lens = np.zeros(n, dtype=np.int32)
+        P.pkv_sync_tables(self.pool, ids, self.tables, self.lens, self.host_lens, stream)
         return self.tables, self.lens
 
     def decode_args(self, layer: int, q: torch.Tensor, out: torch.Tensor, max_seq_len: int,
@@ -119,7 +121,8 @@ class PagedDecodeEngine:
         if need and (self.workspace is None or self.workspace.numel() < need):
             self.workspace = torch.empty((need,), dtype=torch.uint8, device=self.device)
         return P.decode_args(q, out, self.k[layer], self.v[layer], self.tables, self.lens, self.Hkv, self.N,
-                             max_seq_len, scale, self.partition, self.workspace if need else None, self.B)
+                             max_seq_len, scale, self.partition, self.workspace if need else None, self.B,
+                             host_seq_lens=self.host_lens)
 
     def decode(self, layer: int, q: torch.Tensor, max_seq_len: int, out: Optional[torch.Tensor] = None,
                scale: Optional[float] = None, stream=None) -> torch.Tensor:

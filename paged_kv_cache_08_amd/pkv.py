@@ -14,7 +14,8 @@ from typing import List, Optional, Sequence, Tuple
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpkv.so")
+# PKV_LIB selects another build of the library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("PKV_LIB") or os.path.join(_HERE, "libpkv.so")
 
 PKV_OK = 0
 PKV_ERR_INVALID = -1
@@ -55,7 +56,7 @@ class pkv_decode_args(ctypes.Structure):
                 ("num_seqs", _i32), ("num_q_heads", _i32), ("num_kv_heads", _i32),
                 ("head_dim", _i32), ("block_size", _i32), ("num_blocks", _i32),
                 ("max_blocks", _i32), ("max_seq_len", _i32), ("partition", _i32),
-                ("dtype", _i32), ("scale", ctypes.c_float)]
+                ("dtype", _i32), ("scale", ctypes.c_float), ("host_seq_lens", _vp)]
 
 
 _lib = None
@@ -74,7 +75,7 @@ SIGNATURES = [
     ("pkv_append_slots", ctypes.c_int, [_vp, _P(_i64), _i32, _P(_i32), _P(_i32), _P(_i32)]),
     ("pkv_seq_length", ctypes.c_int, [_vp, _i64, _P(_i32)]),
     ("pkv_seq_table", ctypes.c_int, [_vp, _i64, _P(_i32), _i32, _P(_i32)]),
-    ("pkv_sync_tables", ctypes.c_int, [_vp, _P(_i64), _i32, _vp, _i32, _vp, _vp]),
+    ("pkv_sync_tables", ctypes.c_int, [_vp, _P(_i64), _i32, _vp, _i32, _vp, _vp, _vp]),
     ("pkv_copy_blocks", ctypes.c_int, [_vp, _P(_i32), _i32, _vp]),
     ("pkv_kv_append", ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _i32, _vp]),
     ("pkv_pool_stats", ctypes.c_int, [_vp, _P(pkv_stats)]),
@@ -249,12 +250,18 @@ def pkv_seq_table(pool: PoolHandle, seq_id: int) -> List[int]:
 
 
 def pkv_sync_tables(pool: PoolHandle, ids: Sequence[int], dev_block_tables, dev_seq_lens,
-                    stream=None) -> None:
-    """dev_block_tables: int32 device tensor [n][max_blocks]; dev_seq_lens int32 [n]."""
+                    host_seq_lens_out: Optional[np.ndarray] = None, stream=None) -> None:
+    """dev_block_tables: int32 device tensor [n][max_blocks]; dev_seq_lens int32 [n];
+    host_seq_lens_out: optional int32 numpy array [n] receiving the lengths."""
     ids = np.ascontiguousarray(ids, dtype=np.int64)
     max_blocks = dev_block_tables.shape[1]
+    hl = 0
+    if host_seq_lens_out is not None:
+        assert host_seq_lens_out.dtype == np.int32 and host_seq_lens_out.flags.c_contiguous
+        assert host_seq_lens_out.shape[0] >= len(ids)
+        hl = host_seq_lens_out.ctypes.data
     _check(lib().pkv_sync_tables(pool.ptr, _as_i64p(ids), len(ids), _ptr(dev_block_tables), max_blocks,
-                                 _ptr(dev_seq_lens), _stream(stream)))
+                                 _ptr(dev_seq_lens), hl, _stream(stream)))
 
 
 def pkv_copy_blocks(pool: PoolHandle, pairs: Sequence[Tuple[int, int]], stream=None) -> None:
@@ -301,8 +308,10 @@ def pkv_decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, m
 
 def decode_args(q, out, k_cache, v_cache, block_tables, seq_lens, num_kv_heads: int, num_blocks: int,
                 max_seq_len: int, scale: Optional[float] = None, partition: int = 0, workspace=None,
-                block_size: int = 16) -> pkv_decode_args:
-    """Pack a pkv_decode_args from tensors (q/out [S][Hq][d])."""
+                block_size: int = 16, host_seq_lens: Optional[np.ndarray] = None) -> pkv_decode_args:
+    """Pack a pkv_decode_args from tensors (q/out [S][Hq][d]).  host_seq_lens:
+    optional int32 numpy array [S] (kept alive by the returned object; it is
+    read at every call, so it may be updated in place between calls)."""
     import torch
     S, Hq, d = q.shape
     dtype = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}[q.dtype]
@@ -318,6 +327,10 @@ def decode_args(q, out, k_cache, v_cache, block_tables, seq_lens, num_kv_heads: 
     a.partition = partition
     a.dtype = dtype
     a.scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if host_seq_lens is not None:
+        assert host_seq_lens.dtype == np.int32 and host_seq_lens.flags.c_contiguous
+        a.host_seq_lens = host_seq_lens.ctypes.data
+        a._keep = host_seq_lens
     return a
 
 

@@ -168,3 +168,22 @@ def test_invalid_rows_become_nan():
         assert torch.isnan(out2[s].float()).all(), s
     for s in (0, 4):
         assert torch.equal(out2[s].view(torch.int16), good[s].view(torch.int16))
+
+
+def test_wave_split_does_not_change_bits():
+    """The work split (partitions streamed per wave, chosen from the host
+    length hint) must not change a single output bit."""
+    need_gpu()
+    import paged_kv_cache_08_amd.pkv as P
+    wl = workloads.with_lengths([3072] * 8, Hq=32, Hkv=8, d=128, dtype="bf16", seed=21)
+    q, k, v = wl.tensors(device="cuda")
+    eng, _, out = run_gpu(wl, {0: k}, {0: v}, q, partition=32)
+    with_hint = out[0]
+    no_hint = torch.empty_like(q)
+    a = eng.decode_args(0, q, no_hint, wl.max_len)
+    a.host_seq_lens = None                   # no hint: one partition per wave
+    P.pkv_paged_attention_decode(a)
+    torch.cuda.synchronize()
+    assert torch.equal(with_hint.view(torch.int16), no_hint.view(torch.int16))
+    rp = oracle_replay(wl, {0: k}, {0: v})
+    compare_out(with_hint, oracle_out(rp, wl, q))
