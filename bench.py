@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode attention: KV GB/s read and % of HBM peak; decode tokens/s"
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_08_amd", "csrc", "kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
 def kernel_hash() -> str:
@@ -128,12 +128,11 @@ class DecodeBench:
         slots, cow = P.pkv_append_slots(self.eng.pool, self.ids)
         if cow:
             P.pkv_copy_blocks(self.eng.pool, cow)
-        dslots = torch.from_numpy(slots).pin_memory().to(self.dev, non_blocking=True)
         P.pkv_sync_tables(self.eng.pool, self.ids, self.eng.tables, self.eng.lens, self.eng.host_lens)
         for i in range(len(self.lengths)):
             self.lengths[i] += 1
         for l in range(self.layers):
-            P.pkv_kv_append(self.eng.pool, l, self.knew[l][j], self.vnew[l][j], dslots)
+            P.pkv_kv_append_last(self.eng.pool, l, self.knew[l][j], self.vnew[l][j], self.eng.tables, self.eng.lens)
             if record_events:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
@@ -202,16 +201,22 @@ def cpu_baseline(wl_name: str, seconds: float):
 
 
 def load_traffic(workload: str):
-    """HBM bytes per launch of the partial kernel from committed counter runs,
-    if they were taken on the current kernel source."""
+    """HBM bytes per launch of the partial kernel, from the committed counter
+    summary profiles/decode_partial_<workload>_traffic.md, if it was taken on
+    the current kernel source (its `kernel_sha:` line)."""
+    path = os.path.join(TRAFFIC_DIR, f"decode_partial_{workload}_traffic.md")
     try:
-        with open(TRAFFIC_FILE) as f:
-            rec = json.load(f).get(workload)
-    except (OSError, ValueError):
+        text = open(path).read()
+    except OSError:
         return None
-    if not rec or rec.get("kernel_sha") != kernel_hash():
+    fields = {}
+    for line in text.splitlines():
+        if ":" in line and line.strip().startswith(("kernel_sha", "traffic_bytes_per_launch")):
+            k, v = line.strip().lstrip("- ").split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_sha") != kernel_hash() or "traffic_bytes_per_launch" not in fields:
         return None
-    return rec.get("bytes_per_launch")
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def main():
@@ -257,7 +262,8 @@ def main():
     k3_avg_s = sum(k3_ms) / len(k3_ms) / 1e3
     kv_per_launch = kv_total / len(k3_ms)
     achieved = kv_per_launch / k3_avg_s / 1e9
-    traffic = load_traffic(args.config)
+    traffic_bytes = load_traffic(args.config)
+    traffic = None if traffic_bytes is None else round(traffic_bytes / k3_avg_s / 1e9, 2)
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -278,7 +284,8 @@ def main():
         "decode_tokens_per_s": round(wl.S * args.steps / elapsed, 1),
         "roofline": {"bound": "hbm", "kernel": "decode_partial", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "avg_launch_us": round(k3_avg_s * 1e6, 2),
+                     "traffic": traffic, "traffic_bytes_per_launch": traffic_bytes,
+                     "avg_launch_us": round(k3_avg_s * 1e6, 2),
                      "algorithmic_bytes_per_launch": int(kv_per_launch)},
     }
     log(f"timed {args.steps} steps: {value:.1f} GB/s; partial kernel {k3_avg_s * 1e6:.1f} us")

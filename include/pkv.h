@@ -132,8 +132,9 @@ int pkv_seq_table(const pkv_pool* pool, int64_t seq_id, int32_t* table_out, int3
 /* Upload the block tables and lengths of `n` sequences to caller-owned
  * device arrays: dev_block_tables int32[n][max_blocks] (row i = ids[i],
  * unused entries -1) and dev_seq_lens int32[n].  Asynchronous on `stream`
- * through two pinned staging buffers owned by the pool, used alternately: a
- * call waits only for the upload issued two calls earlier.  If
+ * by one small kernel that reads two pinned staging buffers owned by the
+ * pool (used alternately: a call waits only for the upload issued two calls
+ * earlier).  If
  * host_seq_lens_out is not NULL it also receives the lengths (host int32[n]),
  * e.g. to pass as pkv_decode_args.host_seq_lens.  PKV_ERR_INVALID if a
  * sequence holds more than max_blocks blocks.                              */
@@ -152,6 +153,15 @@ int pkv_copy_blocks(pkv_pool* pool, const int32_t* pairs, int32_t n_pairs, void*
  * skipped.  Runs one kernel on `stream`.                                   */
 int pkv_kv_append(pkv_pool* pool, int32_t layer, const void* k_new, const void* v_new,
                   const int32_t* dev_slot_mapping, int32_t n, void* stream);
+
+/* The decode-step form of kv_append: token i's K and V go to the last
+ * position (length - 1) of row i of tables uploaded by pkv_sync_tables,
+ * i.e. to slot dev_block_tables[i][(len-1) / B] * B + (len-1) % B with
+ * len = dev_seq_lens[i].  Rows with len < 1, len > max_blocks * B or a block
+ * id outside the pool are skipped.  Runs one kernel on `stream`.           */
+int pkv_kv_append_last(pkv_pool* pool, int32_t layer, const void* k_new, const void* v_new,
+                       const int32_t* dev_block_tables, int32_t max_blocks,
+                       const int32_t* dev_seq_lens, int32_t n, void* stream);
 
 typedef struct pkv_stats {
   int64_t num_blocks, free_blocks, used_blocks;

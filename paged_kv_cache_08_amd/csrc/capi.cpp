@@ -317,10 +317,8 @@ int pkv_sync_tables(pkv_pool* pool, const int64_t* ids, int32_t n, int32_t* dev_
       lens[i] = seqs[i]->len;
       if (host_lens_out) host_lens_out[i] = seqs[i]->len;
     }
-    rc = from_hip(hipMemcpyAsync(dev_tables, tab, table_bytes, hipMemcpyHostToDevice, st), "sync_tables: tables");
-    if (rc) return rc;
-    rc = from_hip(hipMemcpyAsync(dev_lens, lens, n * sizeof(int32_t), hipMemcpyHostToDevice, st),
-                  "sync_tables: lengths");
+    rc = from_hip(pkv::launch_table_upload(tab, dev_tables, static_cast<int64_t>(n) * max_blocks, dev_lens, n, st),
+                  "sync_tables: upload");
     if (rc) return rc;
     rc = from_hip(hipEventRecord(pool->upload_done[k], st), "sync_tables: record");
     if (rc) return rc;
@@ -369,6 +367,9 @@ int pkv_kv_append(pkv_pool* pool, int32_t layer, const void* k_new, const void* 
   p.k_new = k_new;
   p.v_new = v_new;
   p.slots = dev_slots;
+  p.tables = nullptr;
+  p.lens = nullptr;
+  p.max_blocks = 0;
   p.k_cache = pool->k_cache[layer];
   p.v_cache = pool->v_cache[layer];
   p.num_slots = static_cast<int64_t>(pool->alloc.num_blocks()) * pool->alloc.block_size();
@@ -378,6 +379,36 @@ int pkv_kv_append(pkv_pool* pool, int32_t layer, const void* k_new, const void* 
   p.block_size = pool->alloc.block_size();
   p.elem_bytes = elem_bytes(pool->dtype);
   return from_hip(pkv::launch_kv_append(p, static_cast<hipStream_t>(stream)), "kv_append");
+}
+
+int pkv_kv_append_last(pkv_pool* pool, int32_t layer, const void* k_new, const void* v_new,
+                       const int32_t* dev_tables, int32_t max_blocks, const int32_t* dev_lens, int32_t n,
+                       void* stream) {
+  if (!pool || n < 0 || max_blocks < 1) return fail(PKV_ERR_INVALID, "kv_append_last: bad argument");
+  if (n == 0) return PKV_OK;
+  if (pool->k_cache.empty()) return fail(PKV_ERR_INVALID, "kv_append_last: pool has no device caches");
+  if (layer < 0 || layer >= pool->num_layers) return fail(PKV_ERR_INVALID, "kv_append_last: layer out of range");
+  if (!k_new || !v_new || !dev_tables || !dev_lens) return fail(PKV_ERR_INVALID, "kv_append_last: null pointer");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(PKV_ERR_INVALID, "kv_append_last: inputs must be 16-byte aligned");
+  if (static_cast<int64_t>(max_blocks) * pool->alloc.block_size() > 0x7fffffffLL)
+    return fail(PKV_ERR_INVALID, "kv_append_last: max_blocks too large");
+  pkv::AppendParams p{};
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.slots = nullptr;
+  p.tables = dev_tables;
+  p.lens = dev_lens;
+  p.max_blocks = max_blocks;
+  p.k_cache = pool->k_cache[layer];
+  p.v_cache = pool->v_cache[layer];
+  p.num_slots = static_cast<int64_t>(pool->alloc.num_blocks()) * pool->alloc.block_size();
+  p.n = n;
+  p.num_kv_heads = pool->num_kv_heads;
+  p.head_dim = pool->head_dim;
+  p.block_size = pool->alloc.block_size();
+  p.elem_bytes = elem_bytes(pool->dtype);
+  return from_hip(pkv::launch_kv_append(p, static_cast<hipStream_t>(stream)), "kv_append_last");
 }
 
 int pkv_pool_stats(const pkv_pool* pool, pkv_stats* out) {

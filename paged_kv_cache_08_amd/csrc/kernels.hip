@@ -91,10 +91,19 @@ template <typename T>
 __global__ __launch_bounds__(64) void kv_append_kernel(AppendParams p) {
   const int i = blockIdx.x;
   const int h = blockIdx.y;
-  const int slot = p.slots[i];
+  const int B = p.block_size;
+  int slot;
+  if (p.slots) {
+    slot = p.slots[i];
+  } else {
+    const int len = p.lens[i];
+    if (len < 1 || len > p.max_blocks * B) return;
+    const int b = p.tables[static_cast<size_t>(i) * p.max_blocks + (len - 1) / B];
+    if (b < 0 || static_cast<int64_t>(b) * B >= p.num_slots) return;
+    slot = b * B + (len - 1) % B;
+  }
   if (slot < 0 || static_cast<int64_t>(slot) >= p.num_slots) return;
   constexpr int x = 16 / sizeof(T);
-  const int B = p.block_size;
   const int d = p.head_dim;
   const int b = slot / B;
   const int o = slot - b * B;
@@ -107,6 +116,20 @@ __global__ __launch_bounds__(64) void kv_append_kernel(AppendParams p) {
     *reinterpret_cast<u32x4*>(kd + (static_cast<size_t>(ch) * B + o) * x) =
         *reinterpret_cast<const u32x4*>(ks + ch * x);
   for (int e = threadIdx.x; e < d; e += 64) vd[static_cast<size_t>(e) * B + o] = vs[e];
+}
+
+// ---------------------------------------------------------------------------
+// table_upload: block tables and lengths from the pinned staging buffer
+// (host memory the GPU reads directly) to the device arrays, in one launch.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void table_upload_kernel(const int32_t* __restrict__ src, int32_t* __restrict__ tab,
+                                                           int64_t n_tab, int32_t* __restrict__ lens, int32_t n_len) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n_tab + n_len; i += stride) {
+    const int32_t v = src[i];
+    if (i < n_tab) tab[i] = v;
+    else lens[i - n_tab] = v;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -648,6 +671,16 @@ hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t stream) {
   if (p.n_pairs <= 0 || p.n_layers <= 0) return hipSuccess;
   dim3 grid(p.n_pairs, p.n_layers, 2);
   hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_table_upload(const int32_t* host_src, int32_t* dev_tables, int64_t n_tab, int32_t* dev_lens,
+                               int32_t n_len, hipStream_t stream) {
+  const int64_t total = n_tab + n_len;
+  if (total <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 1024);
+  hipLaunchKernelGGL(table_upload_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, host_src,
+                     dev_tables, n_tab, dev_lens, n_len);
   return hipGetLastError();
 }
 

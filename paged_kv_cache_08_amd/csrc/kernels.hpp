@@ -25,7 +25,10 @@ struct CopyBlocksParams {
 struct AppendParams {
   const void* k_new;
   const void* v_new;
-  const int32_t* slots;
+  const int32_t* slots;          // slot per token, or null: derive it from
+  const int32_t* tables;         //   tables[i][(lens[i]-1) / B] (decode step)
+  const int32_t* lens;
+  int32_t max_blocks;
   void* k_cache;
   void* v_cache;
   int64_t num_slots;     // num_blocks * block_size
@@ -55,6 +58,10 @@ struct DecodeParams {
 };
 
 hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t stream);
+// Copies n_tab table entries and n_len lengths from a device-visible pinned
+// host buffer (tables first, lengths right after) into device arrays.
+hipError_t launch_table_upload(const int32_t* host_src, int32_t* dev_tables, int64_t n_tab, int32_t* dev_lens,
+                               int32_t n_len, hipStream_t stream);
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream);
 // dtype: 0 = fp32, 1 = bf16.  Returns hipErrorInvalidValue for shapes
 // without a kernel (checked by the caller first).

@@ -103,6 +103,19 @@ class PagedDecodeEngine:
                 raise ValueError(kind)
         return log
 
+    def step_append(self, ids: Sequence[int], values=None, max_blocks: Optional[int] = None, stream=None):
+        """Decode-step append: reserve one slot per id on the host, copy any
+        shared partial blocks, upload tables and lengths, and write each new
+        token at its row's last position (kv_append_last) in every layer of
+        ``values`` ({layer: (k [n][Hkv][d], v)})."""
+        slots, cow = P.pkv_append_slots(self.pool, ids)
+        if cow:
+            P.pkv_copy_blocks(self.pool, cow, stream)
+        self.sync(ids, max_blocks, stream)
+        for layer, (kk, vv) in (values or {}).items():
+            P.pkv_kv_append_last(self.pool, layer, kk.contiguous(), vv.contiguous(), self.tables, self.lens, stream)
+        return slots, cow
+
     # -- decode ------------------------------------------------------------
     def sync(self, ids: Sequence[int], max_blocks: Optional[int] = None, stream=None):
         n = len(ids)

@@ -78,6 +78,7 @@ SIGNATURES = [
     ("pkv_sync_tables", ctypes.c_int, [_vp, _P(_i64), _i32, _vp, _i32, _vp, _vp, _vp]),
     ("pkv_copy_blocks", ctypes.c_int, [_vp, _P(_i32), _i32, _vp]),
     ("pkv_kv_append", ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _i32, _vp]),
+    ("pkv_kv_append_last", ctypes.c_int, [_vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _vp]),
     ("pkv_pool_stats", ctypes.c_int, [_vp, _P(pkv_stats)]),
     ("pkv_pool_snapshot", ctypes.c_int, [_vp, _P(_i32), _P(_i32), _P(_i64), _P(_i32), _P(_i64),
                                          _P(_i32), _P(_i64), _P(_i64), _P(_i64), _P(_i64)]),
@@ -274,6 +275,15 @@ def pkv_kv_append(pool: PoolHandle, layer: int, k_new, v_new, dev_slot_mapping, 
     n = dev_slot_mapping.shape[0]
     _check(lib().pkv_kv_append(pool.ptr, layer, _ptr(k_new), _ptr(v_new), _ptr(dev_slot_mapping), n,
                                _stream(stream)))
+
+
+def pkv_kv_append_last(pool: PoolHandle, layer: int, k_new, v_new, dev_block_tables, dev_seq_lens,
+                       stream=None) -> None:
+    """Write token i of k_new/v_new ([n][Hkv][d]) at the last position of row
+    i of the uploaded tables (dev_block_tables [n][max_blocks], dev_seq_lens [n])."""
+    n = dev_seq_lens.shape[0]
+    _check(lib().pkv_kv_append_last(pool.ptr, layer, _ptr(k_new), _ptr(v_new), _ptr(dev_block_tables),
+                                    dev_block_tables.shape[1], _ptr(dev_seq_lens), n, _stream(stream)))
 
 
 def pkv_pool_stats(pool: PoolHandle) -> dict:

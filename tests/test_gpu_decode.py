@@ -187,3 +187,32 @@ def test_wave_split_does_not_change_bits():
     assert torch.equal(with_hint.view(torch.int16), no_hint.view(torch.int16))
     rp = oracle_replay(wl, {0: k}, {0: v})
     compare_out(with_hint, oracle_out(rp, wl, q))
+
+
+@pytest.mark.parametrize("make", [workloads.tiny, lambda: _cow_workload(),
+                                  lambda: workloads.random_small(90, S=7, Hq=8, Hkv=2, d=128, dtype="bf16",
+                                                                 max_len=300)],
+                         ids=["tiny", "cow", "random"])
+def test_step_append_matches_oracle(make):
+    """Setup through extend/append with slot mappings, then the checked step
+    through the step form (tables upload + kv_append_last)."""
+    need_gpu()
+    from paged_kv_cache_08_amd.engine import PagedDecodeEngine
+    wl = make()
+    note(f"step append: {wl.description}")
+    q, k, v = wl.tensors(device="cuda")
+    eng = PagedDecodeEngine(1, wl.Hkv, wl.d, wl.num_blocks, wl.dtype, init_perm=wl.perm)
+    log = eng.run_script(wl.setup_ops, wl, {0: k}, {0: v})
+    (kind, entries), = wl.step_ops
+    offs = wl.offsets
+    rows = torch.tensor([offs[src] + pos for (_, src, pos) in entries], device="cuda")
+    ids = [e[0] for e in entries]
+    slots, cow = eng.step_append(ids, {0: (k.index_select(0, rows), v.index_select(0, rows))})
+    log.append(("append", ids, slots, cow))
+    eng.sync(wl.seq_ids)                     # the decode batch may differ from the appended ids
+    out = eng.decode(0, q, max_seq_len=wl.max_len)
+    torch.cuda.synchronize()
+    rp = oracle_replay(wl, {0: k}, {0: v})
+    check_allocator(eng, rp, log)
+    check_pool(eng, rp)
+    compare_out(out, oracle_out(rp, wl, q))
