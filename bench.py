@@ -211,8 +211,9 @@ def load_traffic(workload: str):
         return None
     fields = {}
     for line in text.splitlines():
-        if ":" in line and line.strip().startswith(("kernel_sha", "traffic_bytes_per_launch")):
-            k, v = line.strip().lstrip("- ").split(":", 1)
+        line = line.strip().lstrip("-* ").strip()
+        if ":" in line and line.startswith(("kernel_sha", "traffic_bytes_per_launch")):
+            k, v = line.split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
     if fields.get("kernel_sha") != kernel_hash() or "traffic_bytes_per_launch" not in fields:
         return None
