@@ -216,3 +216,30 @@ def test_step_append_matches_oracle(make):
     check_allocator(eng, rp, log)
     check_pool(eng, rp)
     compare_out(out, oracle_out(rp, wl, q))
+
+
+
+def test_workspace_reuse_and_garbage():
+    """The split-K workspace may hold anything: repeated calls on one
+    workspace, and a workspace full of random bytes, give the same bits, with
+    and without the host length hint."""
+    need_gpu()
+    import paged_kv_cache_08_amd.pkv as P
+    wl = workloads.with_lengths([2900] * 6, Hq=16, Hkv=4, d=128, dtype="bf16", seed=33)
+    q, k, v = wl.tensors(device="cuda")
+    eng, _, out = run_gpu(wl, {0: k}, {0: v}, q)
+    ref_bits = out[0].view(torch.int16).clone()
+    for trial in range(4):
+        if trial >= 2:
+            g = torch.Generator(device="cuda").manual_seed(5 + trial)
+            eng.workspace.copy_(torch.randint(0, 256, eng.workspace.shape, generator=g, device="cuda",
+                                              dtype=torch.int32).to(torch.uint8))
+        again = torch.empty_like(q)
+        a = eng.decode_args(0, q, again, wl.max_len)
+        if trial % 2:
+            a.host_seq_lens = None
+        P.pkv_paged_attention_decode(a)
+        torch.cuda.synchronize()
+        assert torch.equal(again.view(torch.int16), ref_bits), trial
+    rp = oracle_replay(wl, {0: k}, {0: v})
+    compare_out(out[0], oracle_out(rp, wl, q))
