@@ -21,6 +21,9 @@ floating-point result):
   into a contiguous array through its block table («¿Cómo gestiona Paged Attention la caché KV…?»: the table maps
   logical order to physical blocks; indirection changes placement, not
   meaning).
+* ``fp8``         — the 8-bit (E4M3) cache codes: value table from the bit
+  fields, round-to-nearest-even encoding, one fp32 scale per (token, head)
+  row (readings stated in the module).
 * ``attention``   — exact attention softmax(q·Kᵀ·scale)·V in fp64 on the
   gathered arrays («Servicio…presupuesto de memoria» §6), with GQA head grouping («¿Cuánta memoria reservar para la caché KV?» "Emplear las
   cabezas KV"); plus the blockwise running-statistics form and the
@@ -37,4 +40,4 @@ Parity unpinned: the six-request page-assignment example of «Servicio…presupu
 (results box ``page_tail_slots = 32``) — its request lengths are not printed,
 so it is not reproduced.
 """
-from . import accounting, allocator, attention, pool, replay  # noqa: F401
+from . import accounting, allocator, attention, fp8, pool, replay  # noqa: F401

@@ -1,0 +1,92 @@
+"""8-bit float (e4m3) KV-cache codes — oracle; test infrastructure only.
+
+«Servicio…presupuesto de memoria» §4 and «¿Cuánta memoria reservar para la
+caché KV?» (the paragraph on quantising and offloading the cache) name cache
+quantisation as a way to shrink the KV term and warn that a change of KV
+precision changes the numerics; neither fixes a format.  The readings taken
+here (the library follows the same ones):
+
+* Format: the OCP 8-bit floating-point "E4M3" encoding — 1 sign bit, 4
+  exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds the
+  subnormals m·2^-9; S.1111.111 is NaN; there is no infinity; the largest
+  finite magnitude is 448 (S.1111.110).
+* Granularity: one fp32 scale per (token, KV head) row of d values, for K
+  and for V separately, so a token is quantised once, when it is written,
+  and a block that is still filling never needs re-quantising.
+* Scale: ``s = amax / 448`` in fp32 (IEEE division, round to nearest even),
+  ``amax`` the largest |x| of the row (exact in fp32).  A row of zeros gets
+  ``s = 0`` and codes 0.
+* Code: ``encode(x / s)``, the quotient in fp32 (IEEE division), rounded to
+  the nearest E4M3 value, ties to the even code; the value a code stands for
+  is ``value(code) · s`` (exact in fp64).
+
+Plain definitions, slow on purpose: the value table is built from the bit
+fields, and rounding picks the nearest table entry.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+MAX = 448.0
+
+
+def value(code: int) -> float:
+    """The number an E4M3 code stands for (NaN for S.1111.111)."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** (1 - 7)
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+# all 256 codes, and the non-negative finite ones in increasing order
+VALUES = np.array([value(c) for c in range(256)], dtype=np.float64)
+_POS_CODES = np.array([c for c in range(0x7F)], dtype=np.int64)      # 0x00 .. 0x7E
+_POS_VALUES = VALUES[_POS_CODES]
+assert np.all(np.diff(_POS_VALUES) > 0)
+
+
+def decode(codes: np.ndarray) -> np.ndarray:
+    """fp64 values of an array of codes."""
+    return VALUES[np.asarray(codes, dtype=np.int64) & 0xFF]
+
+
+def encode(y: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 code to each value of ``y`` (ties to the even code).
+    |y| beyond the rounding range of 448 (that is, > 464) gives NaN (0x7F /
+    0xFF); the sign of zero is kept."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    # index of the first table value >= a; compare with its lower neighbour
+    hi = np.clip(np.searchsorted(_POS_VALUES, a, side="left"), 0, len(_POS_VALUES) - 1)
+    lo = np.clip(hi - 1, 0, len(_POS_VALUES) - 1)
+    d_hi = np.abs(_POS_VALUES[hi] - a)
+    d_lo = np.abs(a - _POS_VALUES[lo])
+    pick_lo = (d_lo < d_hi) | ((d_lo == d_hi) & (_POS_CODES[lo] % 2 == 0))
+    mag = np.where(pick_lo, _POS_CODES[lo], _POS_CODES[hi])
+    mag = np.where(a > MAX + 16.0, 0x7F, mag)          # past the 448/480 midpoint
+    mag = np.where(a == MAX + 16.0, 0x7E, mag)         # the tie itself goes to the even 448
+    mag = np.where(np.isnan(a), 0x7F, mag)
+    sign = np.where(np.signbit(y), 0x80, 0x00)
+    return (mag | sign).astype(np.uint8)
+
+
+def quantize_row(x: np.ndarray):
+    """(codes uint8 [d], scale float32) of one (token, head) row of fp32
+    values, by the readings above."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0.0)
+    scale = np.float32(amax / np.float32(MAX))
+    if scale == 0:
+        return np.zeros(x.shape, dtype=np.uint8), np.float32(0.0)
+    y = (x / scale).astype(np.float32)                  # IEEE fp32 division
+    return encode(y), scale
+
+
+def dequantize_row(codes: np.ndarray, scale) -> np.ndarray:
+    """fp64 values a row of codes stands for."""
+    return decode(codes) * np.float64(np.float32(scale))

@@ -19,7 +19,7 @@ class Replay:
         self.wl = wl
         self.alloc = Allocator(wl.num_blocks, wl.block, wl.perm)
         n_layers = wl.layers if layers is None else layers
-        self.pool = Pool(wl.num_blocks, wl.Hkv, wl.d, wl.dtype, wl.block, layers=n_layers,
+        self.pool = Pool(wl.num_blocks, wl.Hkv, wl.d, wl.cache_dtype, wl.block, layers=n_layers,
                          lazy_layers=True)
         self.log = []          # (op kind, ids, slots, cow pairs) per extend/append
 

@@ -12,8 +12,9 @@ import pytest
 import test_oracle_accounting as T_acc
 import test_oracle_allocator as T_alloc
 import test_oracle_attention as T_att
+import test_oracle_fp8 as T_fp8
 import workloads
-from oracle import accounting, allocator, attention, pool
+from oracle import accounting, allocator, attention, fp8, pool
 
 
 def _fails(fn, *args):
@@ -152,3 +153,56 @@ def test_dropped_factor_two(monkeypatch):
 def test_floor_instead_of_ceil(monkeypatch):
     monkeypatch.setattr(accounting, "blocks_for", lambda T, B: T // B)
     _fails(T_acc.test_pages_for_500_tokens)
+
+
+# -- 8-bit cache ---------------------------------------------------------------
+
+def _fp8_case():
+    return lambda: workloads.random_small(21, S=4, Hq=8, Hkv=2, d=64, dtype="bf16", max_len=70)
+
+
+def test_fp8_ties_away_from_zero(monkeypatch):
+    orig = fp8.encode
+
+    def encode(y):
+        y = np.asarray(y, dtype=np.float64)
+        return orig(y + np.sign(y) * np.abs(y) * 2.0 ** -30)     # nudges every tie upwards
+    monkeypatch.setattr(fp8, "encode", encode)
+    _fails(T_fp8.test_encode_matches_library_rounding)
+
+
+def test_fp8_scale_off_by_one(monkeypatch):
+    def quantize_row(x):
+        x = np.asarray(x, dtype=np.float32)
+        scale = np.float32(np.float32(np.abs(x).max()) / np.float32(447))
+        if scale == 0:
+            return np.zeros(x.shape, dtype=np.uint8), np.float32(0)
+        return fp8.encode((x / scale).astype(np.float32)), scale
+    monkeypatch.setattr(fp8, "quantize_row", quantize_row)
+    _fails(T_fp8.test_paged_fp8_attention_matches_brute_force, _fp8_case())
+
+
+def test_fp8_value_columns_swapped(monkeypatch):
+    orig = pool.Pool.gather
+
+    def gather(self, layer, table, n, head):
+        K, V = orig(self, layer, table, n, head)
+        if self.dtype == "fp8":       # columns 4c + b read as 4b + c inside each group of 16
+            V = V.reshape(n, -1, 4, 4).transpose(0, 1, 3, 2).reshape(n, -1)
+        return K, V
+    monkeypatch.setattr(pool.Pool, "gather", gather)
+    _fails(T_fp8.test_paged_fp8_attention_matches_brute_force, _fp8_case())
+
+
+def test_fp8_one_scale_per_block(monkeypatch):
+    orig = pool.Pool.gather
+
+    def gather(self, layer, table, n, head):
+        K, V = orig(self, layer, table, n, head)
+        if self.dtype == "fp8":       # every token scaled as its block's first one
+            ks = self.KS[layer][np.asarray(table[:-(-n // self.B)]), head].view(np.float32).astype(np.float64)
+            first = np.repeat(ks[:, :1], self.B, axis=1).reshape(-1)[:n]
+            K = K / ks.reshape(-1)[:n, None] * first[:, None]
+        return K, V
+    monkeypatch.setattr(pool.Pool, "gather", gather)
+    _fails(T_fp8.test_paged_fp8_attention_matches_brute_force, _fp8_case())

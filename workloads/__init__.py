@@ -52,6 +52,7 @@ class Workload:
     block: int = BLOCK
     partition: int = 512
     description: str = ""
+    kv_dtype: str = ""         # cache element type if it differs: "fp8" (E4M3 codes)
 
     @property
     def S(self) -> int:
@@ -64,6 +65,10 @@ class Workload:
     @property
     def itemsize(self) -> int:
         return 4 if self.dtype == "f32" else 2
+
+    @property
+    def cache_dtype(self) -> str:
+        return self.kv_dtype or self.dtype
 
     @property
     def offsets(self) -> np.ndarray:
@@ -80,7 +85,11 @@ class Workload:
         return int(self.lengths.max())
 
     def kv_bytes_per_layer(self) -> int:
-        """Algorithmic K+V bytes one decode attention call reads."""
+        """Algorithmic K+V bytes one decode attention call reads (for the
+        8-bit cache: one byte per value plus a 4-byte scale per token and
+        head, for K and for V)."""
+        if self.cache_dtype == "fp8":
+            return 2 * self.total_tokens * self.Hkv * (self.d + 4)
         return 2 * self.total_tokens * self.Hkv * self.d * self.itemsize
 
     def tensors(self, layer: int = 0, device="cpu"):
@@ -240,12 +249,23 @@ def with_lengths(lengths, Hq: int, Hkv: int, d: int, dtype: str, seed: int = 7,
                     description=f"S={len(lengths)}, n={list(map(int, lengths))[:8]}..., Hq={Hq}, Hkv={Hkv}, d={d}, {dtype}")
 
 
+def fp8_cache(wl: Workload) -> Workload:
+    """The same workload with an 8-bit (E4M3) KV cache: the same bf16 input
+    values, quantised per (token, head) row when they are written."""
+    if wl.dtype != "bf16":
+        raise ValueError("the 8-bit cache takes bf16 tokens and queries")
+    return dataclasses.replace(wl, name=wl.name + "_fp8", kv_dtype="fp8",
+                               description=wl.description + ", fp8 (e4m3) KV cache")
+
+
 CONFIGS = {
     "tiny": tiny,
     "single_layer": single_layer,
     "shared_prefix": shared_prefix,
     "long_context": long_context,
     "full_step": full_step,
+    "long_context_fp8": lambda seed=3, **kw: fp8_cache(long_context(seed, **kw)),
+    "full_step_fp8": lambda seed=4, **kw: fp8_cache(full_step(seed, **kw)),
 }
 
 
