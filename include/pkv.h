@@ -24,7 +24,10 @@
  *    running normalisation statistics.  §8: release must not free pages in
  *    use; no request may see another's private continuation.
  *  - «¿Cuánta memoria reservar para la caché KV?», "Emplear las cabezas KV":
- *    grouped-query attention, several query heads per KV head.
+ *    grouped-query attention, several query heads per KV head.  The same
+ *    page, on quantising the cache, and «Servicio…presupuesto de memoria» §4:
+ *    a lower-precision KV cache is a separate choice that changes the
+ *    numerics (here: the 8-bit PKV_FP8_E4M3 pool).
  *
  * Ownership: all device memory (per-layer K/V pools, q, out, block tables,
  * sequence lengths, slot mappings, workspace) belongs to the caller; the
@@ -40,6 +43,22 @@
  *   V: [num_blocks][num_kv_heads][d][B]
  * Slot number s names block s / B, token offset s % B.  One block id
  * addresses the same token range in every layer's pool.
+ *
+ * 8-bit pools (PKV_FP8_E4M3; B = 16, d a multiple of 64): OCP E4M3 codes
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; S.1111.111 = NaN;
+ * largest magnitude 448) plus one fp32 scale per (slot, KV head) for K and
+ * one for V.  The value of a code c in slot s is E4M3(c) * scale[s].
+ *   K codes: [num_blocks][num_kv_heads][d / 16][B][16]   (x = 16)
+ *   V codes: [num_blocks][num_kv_heads][d / 64][B / 4][16][4][4]: value
+ *            column j = 64a + 4c + b of token offset o = 4u + w sits at
+ *            [a][u][c][b][w] (each 16 bytes hold four columns of four
+ *            consecutive tokens, the decode kernel's operand order).
+ *   K and V scales: fp32 [num_blocks][num_kv_heads][B].
+ * Appends quantise each (token, KV head) row of d values on its own:
+ * scale = amax / 448 in fp32 (amax = largest |value|), code = the E4M3
+ * value nearest to value / scale (fp32 quotient; ties to the even code); an
+ * all-zero row gets scale 0 and codes 0.  Tokens, queries and outputs of an
+ * 8-bit pool are bf16.
  */
 #ifndef PKV_H
 #define PKV_H
@@ -60,8 +79,9 @@ extern "C" {
 #define PKV_ERR_UNSUPPORTED -5  /* valid, but no kernel for this shape        */
 
 /* ---- element types ----------------------------------------------------- */
-#define PKV_F32  0
-#define PKV_BF16 1
+#define PKV_F32      0
+#define PKV_BF16     1
+#define PKV_FP8_E4M3 2   /* KV pools only: 8-bit codes + per-slot scales */
 
 /* Name of a status code (static string). */
 const char* pkv_status_string(int status);
@@ -79,11 +99,14 @@ typedef struct pkv_pool_desc {
   int32_t head_dim;        /* d, multiple of 16 bytes / element size        */
   int32_t block_size;      /* B tokens per block (16 for the kernels)       */
   int32_t num_blocks;      /* pool capacity in blocks, >= 1                 */
-  int32_t dtype;           /* PKV_F32 or PKV_BF16                           */
+  int32_t dtype;           /* PKV_F32, PKV_BF16 or PKV_FP8_E4M3             */
   void* const* k_cache;    /* [num_layers] device pointers, or NULL for an  */
   void* const* v_cache;    /*   allocator-only pool (no device calls)       */
   const int32_t* init_perm;/* optional host [num_blocks] permutation: the   */
                            /*   free list hands out init_perm[0], [1], ...  */
+  void* const* k_scale;    /* PKV_FP8_E4M3 with caches: [num_layers] device */
+  void* const* v_scale;    /*   pointers to fp32 [num_blocks][Hkv][B]       */
+                           /*   scale arrays; ignored for other dtypes      */
 } pkv_pool_desc;
 
 /* Create a pool.  The descriptor's arrays are copied.  Free list starts with
@@ -143,14 +166,15 @@ int pkv_sync_tables(pkv_pool* pool, const int64_t* ids, int32_t n, int32_t* dev_
                     void* stream);
 
 /* Copy-on-write copy: for each host pair (src, dst) in pairs[2 * n_pairs],
- * block dst := block src in K and V of every layer (all heads, all slots).
- * Runs one kernel on `stream`.                                             */
+ * block dst := block src in K and V of every layer (all heads, all slots;
+ * with the scales too in an 8-bit pool).  Runs one kernel on `stream`.     */
 int pkv_copy_blocks(pkv_pool* pool, const int32_t* pairs, int32_t n_pairs, void* stream);
 
 /* Write new tokens of one layer: token i's K and V (device, contiguous
- * [n][num_kv_heads][head_dim] in the pool dtype) go to slot
- * dev_slot_mapping[i] (device int32[n]).  Slots outside the pool are
- * skipped.  Runs one kernel on `stream`.                                   */
+ * [n][num_kv_heads][head_dim] in the pool dtype, bf16 for an 8-bit pool,
+ * which quantises them as stated above) go to slot dev_slot_mapping[i]
+ * (device int32[n]).  Slots outside the pool are skipped.  Runs one kernel
+ * on `stream`.                                                             */
 int pkv_kv_append(pkv_pool* pool, int32_t layer, const void* k_new, const void* v_new,
                   const int32_t* dev_slot_mapping, int32_t n, void* stream);
 
@@ -192,10 +216,11 @@ int pkv_pool_snapshot(const pkv_pool* pool, int32_t* free_out, int32_t* ref_out,
  * a reduce kernel merges them.  Sequences with n < 1, n > max_seq_len or a
  * block id outside [0, num_blocks) get NaN rows (the kernels read nothing
  * outside the pool).  Supported: block_size 16, head_dim 64 or 128, any
- * Hq multiple of Hkv.                                                      */
+ * Hq multiple of Hkv; bf16 queries may read an 8-bit (PKV_FP8_E4M3) cache,
+ * whose values are code * scale as stated above.                           */
 typedef struct pkv_decode_args {
-  const void* q;              /* device [S][Hq][d], pool dtype              */
-  void* out;                  /* device [S][Hq][d], pool dtype              */
+  const void* q;              /* device [S][Hq][d], dtype                   */
+  void* out;                  /* device [S][Hq][d], dtype                   */
   const void* k_cache;        /* device, one layer, layout above            */
   const void* v_cache;
   const int32_t* block_tables;/* device [S][max_blocks]                     */
@@ -212,12 +237,16 @@ typedef struct pkv_decode_args {
   int32_t max_seq_len;        /* upper bound of seq_lens (sizes the grid)   */
   int32_t partition;          /* tokens per split-K partition, multiple of  */
                               /*   32; 0 = 512                              */
-  int32_t dtype;              /* PKV_F32 or PKV_BF16                        */
+  int32_t dtype;              /* PKV_F32 or PKV_BF16: q and out             */
   float scale;                /* score scale, e.g. 1/sqrt(d)                */
   const int32_t* host_seq_lens; /* optional host copy of seq_lens [S], read */
                               /*   only to choose how partitions are spread */
                               /*   over waves; NULL = unknown (results do   */
                               /*   not depend on it)                        */
+  const float* k_scale;       /* 8-bit cache: device scales of this layer,  */
+  const float* v_scale;       /*   fp32 [num_blocks][Hkv][B]; else unused   */
+  int32_t kv_dtype;           /* cache type: equal to dtype, or             */
+                              /*   PKV_FP8_E4M3 with dtype PKV_BF16         */
 } pkv_decode_args;
 
 /* Workspace bytes the decode call needs (0 when one partition suffices). */

@@ -75,16 +75,22 @@ def encode(y: np.ndarray) -> np.ndarray:
     return (mag | sign).astype(np.uint8)
 
 
-def quantize_row(x: np.ndarray):
-    """(codes uint8 [d], scale float32) of one (token, head) row of fp32
-    values, by the readings above."""
+def quantize_rows(x: np.ndarray):
+    """(codes uint8 [..., d], scales float32 [...]) of rows of fp32 values
+    (the last axis is the row), each row by the readings above."""
     x = np.asarray(x, dtype=np.float32)
-    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0.0)
-    scale = np.float32(amax / np.float32(MAX))
-    if scale == 0:
-        return np.zeros(x.shape, dtype=np.uint8), np.float32(0.0)
-    y = (x / scale).astype(np.float32)                  # IEEE fp32 division
-    return encode(y), scale
+    amax = np.max(np.abs(x), axis=-1)                               # exact in fp32
+    scale = (amax / np.float32(MAX)).astype(np.float32)             # IEEE fp32 division
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    y = (x / safe[..., None]).astype(np.float32)                    # IEEE fp32 division
+    codes = np.where(scale[..., None] > 0, encode(y), np.uint8(0)).astype(np.uint8)
+    return codes, scale
+
+
+def quantize_row(x: np.ndarray):
+    """(codes uint8 [d], scale float32) of one (token, head) row."""
+    codes, scale = quantize_rows(np.asarray(x, dtype=np.float32)[None])
+    return codes[0], np.float32(scale[0])
 
 
 def dequantize_row(codes: np.ndarray, scale) -> np.ndarray:

@@ -93,17 +93,14 @@ class Pool:
         K, V = self.K[layer], self.V[layer]
         if self.dtype == "fp8":
             # new tokens arrive as bf16 bit patterns; quantise row by row
-            k32 = to_f64(k_bits, "bf16").astype(np.float32)
-            v32 = to_f64(v_bits, "bf16").astype(np.float32)
+            kc, ks = fp8.quantize_rows(to_f64(k_bits, "bf16").astype(np.float32))   # [n][Hkv][d], [n][Hkv]
+            vc, vs = fp8.quantize_rows(to_f64(v_bits, "bf16").astype(np.float32))
             for i, slot in enumerate(slots):
                 b, o = divmod(int(slot), self.B)
-                for h in range(self.Hkv):
-                    kc, ks = fp8.quantize_row(k32[i, h])
-                    vc, vs = fp8.quantize_row(v32[i, h])
-                    K[b, h, :, o, :] = kc.reshape(self.d // 16, 16)
-                    V[b, h, :, o // 4, :, :, o % 4] = vc.reshape(self.d // 64, 16, 4)
-                    self.KS[layer][b, h, o] = np.float32(ks).view(np.uint32)
-                    self.VS[layer][b, h, o] = np.float32(vs).view(np.uint32)
+                K[b, :, :, o, :] = kc[i].reshape(self.Hkv, self.d // 16, 16)
+                V[b, :, :, o // 4, :, :, o % 4] = vc[i].reshape(self.Hkv, self.d // 64, 16, 4)
+                self.KS[layer][b, :, o] = ks[i].view(np.uint32)
+                self.VS[layer][b, :, o] = vs[i].view(np.uint32)
             return
         for i, slot in enumerate(slots):
             b, o = divmod(int(slot), self.B)

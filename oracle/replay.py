@@ -23,9 +23,12 @@ class Replay:
                          lazy_layers=True)
         self.log = []          # (op kind, ids, slots, cow pairs) per extend/append
 
-    def run(self, ops, values=None):
+    def run(self, ops, values=None, sources=None):
         """Execute ``ops``; ``values`` maps layer -> (k_bits, v_bits) logical
-        arrays [sum n][Hkv][d]; every listed layer receives the tokens."""
+        arrays [sum n][Hkv][d]; every listed layer receives the tokens.
+        ``sources``: optional set of logical sequences whose tokens are
+        written (the allocator still runs every op; other slots keep their
+        poison) — for spot checks of batches too large to fill whole."""
         offs = self.wl.offsets
         values = values or {}
 
@@ -36,10 +39,15 @@ class Replay:
             if op[0] == "extend":
                 _, sid, k, src, pos = op
                 rows = np.arange(offs[src] + pos, offs[src] + pos + k)
+                keep = np.full(k, sources is None or src in sources)
             else:
                 rows = np.array([offs[src] + pos for (_, src, pos) in op[1]], dtype=np.int64)
+                keep = np.array([sources is None or src in sources for (_, src, _) in op[1]], dtype=bool)
+            if not keep.any():
+                return
+            sl = np.asarray(slots)[keep]
             for layer, (kb, vb) in values.items():
-                self.pool.scatter(layer, slots, kb[rows], vb[rows])
+                self.pool.scatter(layer, sl, kb[rows[keep]], vb[rows[keep]])
 
         run_script(self.alloc, ops, on_slots)
         return self

@@ -21,6 +21,7 @@ struct pkv_pool {
   pkv::BlockPool alloc;
   int32_t num_layers, num_kv_heads, head_dim, dtype;
   std::vector<void*> k_cache, v_cache;    // empty for an allocator-only pool
+  std::vector<void*> k_scale, v_scale;    // 8-bit pools: per-slot scales
   // Two pinned staging buffers for table uploads, used alternately; a buffer
   // is refilled only after the upload that last read it has finished.
   void* staging[2] = {nullptr, nullptr};
@@ -52,7 +53,8 @@ int from_hip(hipError_t e, const char* what) {
   return fail(PKV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-int elem_bytes(int32_t dtype) { return dtype == PKV_F32 ? 4 : 2; }
+// Bytes per cached value.
+int elem_bytes(int32_t dtype) { return dtype == PKV_F32 ? 4 : dtype == PKV_BF16 ? 2 : 1; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -72,9 +74,14 @@ int guarded(F&& f) {
 int32_t effective_partition(int32_t partition) { return partition == 0 ? 512 : partition; }
 
 // Checks the decode arguments and fills the kernel parameter block.
-int prepare_decode(const pkv_decode_args* a, pkv::DecodeParams* p) {
+int prepare_decode(const pkv_decode_args* a, pkv::DecodeParams* p, int* kind_out) {
   if (!a) return fail(PKV_ERR_INVALID, "decode: null args");
   if (a->dtype != PKV_F32 && a->dtype != PKV_BF16) return fail(PKV_ERR_INVALID, "decode: bad dtype");
+  if (a->kv_dtype != a->dtype && !(a->kv_dtype == PKV_FP8_E4M3 && a->dtype == PKV_BF16))
+    return fail(PKV_ERR_INVALID, "decode: kv_dtype must equal dtype, or be PKV_FP8_E4M3 with PKV_BF16 queries");
+  const int kind = a->kv_dtype == PKV_FP8_E4M3 ? pkv::kDecodeFP8KV
+                   : a->dtype == PKV_BF16    ? pkv::kDecodeBF16
+                                             : pkv::kDecodeF32;
   if (a->num_seqs < 1 || a->num_kv_heads < 1 || a->num_q_heads < 1 || a->head_dim < 1 ||
       a->block_size < 1 || a->num_blocks < 1 || a->max_blocks < 1 || a->max_seq_len < 1)
     return fail(PKV_ERR_INVALID, "decode: sizes must be positive");
@@ -83,12 +90,15 @@ int prepare_decode(const pkv_decode_args* a, pkv::DecodeParams* p) {
   const int32_t part = effective_partition(a->partition);
   if (part < 32 || part > 1024 || part % 32 != 0)
     return fail(PKV_ERR_INVALID, "decode: partition must be a multiple of 32 in [32, 1024]");
-  if (!pkv::decode_shape_supported(a->dtype == PKV_BF16 ? 1 : 0, a->head_dim, a->block_size))
+  if (!pkv::decode_shape_supported(kind, a->head_dim, a->block_size))
     return fail(PKV_ERR_UNSUPPORTED, "decode: supported shapes are block_size 16, head_dim 64 or 128");
   if (!a->q || !a->out || !a->k_cache || !a->v_cache || !a->block_tables || !a->seq_lens)
     return fail(PKV_ERR_INVALID, "decode: null device pointer");
   if (!aligned16(a->q) || !aligned16(a->out) || !aligned16(a->k_cache) || !aligned16(a->v_cache))
     return fail(PKV_ERR_INVALID, "decode: q, out and caches must be 16-byte aligned");
+  if (kind == pkv::kDecodeFP8KV &&
+      (!a->k_scale || !a->v_scale || !aligned16(a->k_scale) || !aligned16(a->v_scale)))
+    return fail(PKV_ERR_INVALID, "decode: an 8-bit cache needs 16-byte aligned k_scale and v_scale");
   const int64_t pmax = (static_cast<int64_t>(a->max_seq_len) + part - 1) / part;
   const int64_t gx = pmax * a->num_seqs * a->num_kv_heads;
   if (gx > 0x7fffffffLL || static_cast<int64_t>(a->num_seqs) * a->num_q_heads > 0x7fffffffLL)
@@ -105,6 +115,8 @@ int prepare_decode(const pkv_decode_args* a, pkv::DecodeParams* p) {
   p->v_cache = a->v_cache;
   p->block_tables = a->block_tables;
   p->seq_lens = a->seq_lens;
+  p->k_scale = kind == pkv::kDecodeFP8KV ? a->k_scale : nullptr;
+  p->v_scale = kind == pkv::kDecodeFP8KV ? a->v_scale : nullptr;
   p->S = a->num_seqs;
   p->Hq = a->num_q_heads;
   p->Hkv = a->num_kv_heads;
@@ -143,6 +155,7 @@ int prepare_decode(const pkv_decode_args* a, pkv::DecodeParams* p) {
     p->part_ml = nullptr;
     p->part_acc = nullptr;
   }
+  *kind_out = kind;
   return PKV_OK;
 }
 
@@ -173,9 +186,15 @@ int pkv_pool_create(const pkv_pool_desc* d, pkv_pool** out) {
     if (d->num_layers < 1 || d->num_kv_heads < 1 || d->head_dim < 1 || d->block_size < 1 ||
         d->num_blocks < 1)
       return fail(PKV_ERR_INVALID, "pool_create: sizes must be positive");
-    if (d->dtype != PKV_F32 && d->dtype != PKV_BF16) return fail(PKV_ERR_INVALID, "pool_create: bad dtype");
+    if (d->dtype != PKV_F32 && d->dtype != PKV_BF16 && d->dtype != PKV_FP8_E4M3)
+      return fail(PKV_ERR_INVALID, "pool_create: bad dtype");
     if ((d->head_dim * elem_bytes(d->dtype)) % 16 != 0)
       return fail(PKV_ERR_INVALID, "pool_create: head_dim must be a multiple of 16 bytes");
+    const bool fp8 = d->dtype == PKV_FP8_E4M3;
+    if (fp8 && (d->head_dim % 64 != 0 || d->block_size != 16))
+      return fail(PKV_ERR_INVALID, "pool_create: an 8-bit pool needs head_dim % 64 == 0 and block_size 16");
+    if (fp8 && d->k_cache && (!d->k_scale || !d->v_scale))
+      return fail(PKV_ERR_INVALID, "pool_create: an 8-bit pool needs k_scale and v_scale arrays");
     if (static_cast<int64_t>(d->num_blocks) * d->block_size > 0x7fffffffLL)
       return fail(PKV_ERR_INVALID, "pool_create: num_blocks * block_size must fit in int32 slots");
     if ((d->k_cache == nullptr) != (d->v_cache == nullptr))
@@ -202,6 +221,14 @@ int pkv_pool_create(const pkv_pool_desc* d, pkv_pool** out) {
         }
         pool->k_cache.push_back(d->k_cache[l]);
         pool->v_cache.push_back(d->v_cache[l]);
+        if (fp8) {
+          if (!d->k_scale[l] || !d->v_scale[l] || !aligned16(d->k_scale[l]) || !aligned16(d->v_scale[l])) {
+            delete pool;
+            return fail(PKV_ERR_INVALID, "pool_create: layer scale arrays must be non-null and 16-byte aligned");
+          }
+          pool->k_scale.push_back(d->k_scale[l]);
+          pool->v_scale.push_back(d->v_scale[l]);
+        }
       }
     }
     *out = pool;
@@ -343,9 +370,15 @@ int pkv_copy_blocks(pkv_pool* pool, const int32_t* pairs, int32_t n_pairs, void*
       p.n_layers = std::min(pkv::kCopyMaxLayers, pool->num_layers - l0);
       p.n_pairs = std::min(pkv::kCopyMaxPairs, n_pairs - p0);
       p.block_bytes = block_bytes;
+      const bool scaled = !pool->k_scale.empty();
+      p.scale_bytes = scaled ? static_cast<int64_t>(pool->num_kv_heads) * pool->alloc.block_size() * 4 : 0;
       for (int32_t l = 0; l < p.n_layers; ++l) {
         p.k[l] = pool->k_cache[l0 + l];
         p.v[l] = pool->v_cache[l0 + l];
+        if (scaled) {
+          p.ks[l] = pool->k_scale[l0 + l];
+          p.vs[l] = pool->v_scale[l0 + l];
+        }
       }
       std::memcpy(p.pairs, pairs + 2 * p0, sizeof(int32_t) * 2 * p.n_pairs);
       const int rc = from_hip(pkv::launch_copy_blocks(p, static_cast<hipStream_t>(stream)), "copy_blocks");
@@ -378,6 +411,10 @@ int pkv_kv_append(pkv_pool* pool, int32_t layer, const void* k_new, const void* 
   p.head_dim = pool->head_dim;
   p.block_size = pool->alloc.block_size();
   p.elem_bytes = elem_bytes(pool->dtype);
+  if (!pool->k_scale.empty()) {
+    p.k_scale = static_cast<float*>(pool->k_scale[layer]);
+    p.v_scale = static_cast<float*>(pool->v_scale[layer]);
+  }
   return from_hip(pkv::launch_kv_append(p, static_cast<hipStream_t>(stream)), "kv_append");
 }
 
@@ -408,6 +445,10 @@ int pkv_kv_append_last(pkv_pool* pool, int32_t layer, const void* k_new, const v
   p.head_dim = pool->head_dim;
   p.block_size = pool->alloc.block_size();
   p.elem_bytes = elem_bytes(pool->dtype);
+  if (!pool->k_scale.empty()) {
+    p.k_scale = static_cast<float*>(pool->k_scale[layer]);
+    p.v_scale = static_cast<float*>(pool->v_scale[layer]);
+  }
   return from_hip(pkv::launch_kv_append(p, static_cast<hipStream_t>(stream)), "kv_append_last");
 }
 
@@ -476,29 +517,29 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
 
 int pkv_paged_decode_partial(const pkv_decode_args* a, void* stream) {
   pkv::DecodeParams p{};
-  const int rc = prepare_decode(a, &p);
+  int kind = 0;
+  const int rc = prepare_decode(a, &p, &kind);
   if (rc) return rc;
-  return from_hip(pkv::launch_decode_partial(p, a->dtype == PKV_BF16 ? 1 : 0, static_cast<hipStream_t>(stream)),
-                  "decode_partial");
+  return from_hip(pkv::launch_decode_partial(p, kind, static_cast<hipStream_t>(stream)), "decode_partial");
 }
 
 int pkv_paged_decode_reduce(const pkv_decode_args* a, void* stream) {
   pkv::DecodeParams p{};
-  const int rc = prepare_decode(a, &p);
+  int kind = 0;
+  const int rc = prepare_decode(a, &p, &kind);
   if (rc) return rc;
-  return from_hip(pkv::launch_decode_reduce(p, a->dtype == PKV_BF16 ? 1 : 0, static_cast<hipStream_t>(stream)),
-                  "decode_reduce");
+  return from_hip(pkv::launch_decode_reduce(p, kind, static_cast<hipStream_t>(stream)), "decode_reduce");
 }
 
 int pkv_paged_attention_decode(const pkv_decode_args* a, void* stream) {
   pkv::DecodeParams p{};
-  int rc = prepare_decode(a, &p);
+  int kind = 0;
+  int rc = prepare_decode(a, &p, &kind);
   if (rc) return rc;
-  const int dt = a->dtype == PKV_BF16 ? 1 : 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  rc = from_hip(pkv::launch_decode_partial(p, dt, st), "decode_partial");
+  rc = from_hip(pkv::launch_decode_partial(p, kind, st), "decode_partial");
   if (rc) return rc;
-  return from_hip(pkv::launch_decode_reduce(p, dt, st), "decode_reduce");
+  return from_hip(pkv::launch_decode_reduce(p, kind, st), "decode_reduce");
 }
 
 }  // extern "C"

@@ -49,6 +49,10 @@ constexpr int kBlock = 16;   // tokens per block on the decode path
 #define PKV_DEPTH 3
 #endif
 constexpr int kDepth = PKV_DEPTH;  // blocks in flight per wave on the bf16 decode path
+#ifndef PKV_DEPTH_FP8
+#define PKV_DEPTH_FP8 4
+#endif
+constexpr int kDepthFp8 = PKV_DEPTH_FP8;  // the same on the 8-bit cache path
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -87,22 +91,31 @@ __device__ __forceinline__ float wave_sum(float x) {
 // ---------------------------------------------------------------------------
 // kv_append
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(64) void kv_append_kernel(AppendParams p) {
-  const int i = blockIdx.x;
-  const int h = blockIdx.y;
+// Slot of token i: given, or the last position of row i of the tables (decode
+// step).  -1 when the row or the slot is invalid (the token is skipped).
+__device__ __forceinline__ int append_slot(const AppendParams& p, int i) {
   const int B = p.block_size;
   int slot;
   if (p.slots) {
     slot = p.slots[i];
   } else {
     const int len = p.lens[i];
-    if (len < 1 || len > p.max_blocks * B) return;
+    if (len < 1 || len > p.max_blocks * B) return -1;
     const int b = p.tables[static_cast<size_t>(i) * p.max_blocks + (len - 1) / B];
-    if (b < 0 || static_cast<int64_t>(b) * B >= p.num_slots) return;
+    if (b < 0 || static_cast<int64_t>(b) * B >= p.num_slots) return -1;
     slot = b * B + (len - 1) % B;
   }
-  if (slot < 0 || static_cast<int64_t>(slot) >= p.num_slots) return;
+  if (slot < 0 || static_cast<int64_t>(slot) >= p.num_slots) return -1;
+  return slot;
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) void kv_append_kernel(AppendParams p) {
+  const int i = blockIdx.x;
+  const int h = blockIdx.y;
+  const int B = p.block_size;
+  const int slot = append_slot(p, i);
+  if (slot < 0) return;
   constexpr int x = 16 / sizeof(T);
   const int d = p.head_dim;
   const int b = slot / B;
@@ -116,6 +129,47 @@ __global__ __launch_bounds__(64) void kv_append_kernel(AppendParams p) {
     *reinterpret_cast<u32x4*>(kd + (static_cast<size_t>(ch) * B + o) * x) =
         *reinterpret_cast<const u32x4*>(ks + ch * x);
   for (int e = threadIdx.x; e < d; e += 64) vd[static_cast<size_t>(e) * B + o] = vs[e];
+}
+
+// 8-bit cache: one wave quantises one (token, KV head) row of K and of V.
+// scale = amax / 448 (the largest E4M3 magnitude), code = E4M3 nearest to
+// value / scale (hardware conversion, round to nearest even); a row of zeros
+// gets scale 0 and codes 0.  B = 16; K codes [d/16][B][16]; V codes
+// [d/64][B/4][16][4][4] (column 64a + 4c + b of slot 4u + w at [a][u][c][b][w]).
+__device__ __forceinline__ uint8_t e4m3_code(float v, float scale) {
+  const float y = scale > 0.f ? v / scale : 0.f;
+  return static_cast<uint8_t>(__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.f, 0u, false) & 0xFFu);
+}
+
+__global__ __launch_bounds__(64) void kv_append_fp8_kernel(AppendParams p) {
+  const int i = blockIdx.x;
+  const int h = blockIdx.y;
+  const int slot = append_slot(p, i);
+  if (slot < 0) return;
+  const int d = p.head_dim;
+  const int b = slot / kBlock;
+  const int o = slot - b * kBlock;
+  const __bf16* ks = static_cast<const __bf16*>(p.k_new) + (static_cast<size_t>(i) * p.num_kv_heads + h) * d;
+  const __bf16* vs = static_cast<const __bf16*>(p.v_new) + (static_cast<size_t>(i) * p.num_kv_heads + h) * d;
+  float ka = 0.f, va = 0.f;
+  for (int e = threadIdx.x; e < d; e += 64) {
+    ka = fmaxf(ka, fabsf(static_cast<float>(ks[e])));
+    va = fmaxf(va, fabsf(static_cast<float>(vs[e])));
+  }
+  const float kscale = wave_max(ka) / 448.f;
+  const float vscale = wave_max(va) / 448.f;
+  const size_t row = static_cast<size_t>(b) * p.num_kv_heads + h;
+  uint8_t* kd = static_cast<uint8_t*>(p.k_cache) + row * kBlock * d;
+  uint8_t* vd = static_cast<uint8_t*>(p.v_cache) + row * kBlock * d;
+  for (int e = threadIdx.x; e < d; e += 64) {
+    kd[(e >> 4) * (kBlock * 16) + o * 16 + (e & 15)] = e4m3_code(static_cast<float>(ks[e]), kscale);
+    vd[(e >> 6) * 1024 + (o >> 2) * 256 + ((e & 63) >> 2) * 16 + (e & 3) * 4 + (o & 3)] =
+        e4m3_code(static_cast<float>(vs[e]), vscale);
+  }
+  if (threadIdx.x == 0) {
+    p.k_scale[row * kBlock + o] = kscale;
+    p.v_scale[row * kBlock + o] = vscale;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -140,10 +194,13 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksParams p) {
   const int layer = blockIdx.y;
   const int src = p.pairs[2 * pair];
   const int dst = p.pairs[2 * pair + 1];
-  char* base = static_cast<char*>(blockIdx.z ? p.v[layer] : p.k[layer]);
-  const u32x4* s = reinterpret_cast<const u32x4*>(base + static_cast<int64_t>(src) * p.block_bytes);
-  u32x4* d = reinterpret_cast<u32x4*>(base + static_cast<int64_t>(dst) * p.block_bytes);
-  const int64_t n16 = p.block_bytes / 16;
+  // z: 0 = K, 1 = V, 2 = K scales, 3 = V scales (8-bit pools)
+  const int z = blockIdx.z;
+  char* base = static_cast<char*>(z == 0 ? p.k[layer] : z == 1 ? p.v[layer] : z == 2 ? p.ks[layer] : p.vs[layer]);
+  const int64_t bytes = z < 2 ? p.block_bytes : p.scale_bytes;
+  const u32x4* s = reinterpret_cast<const u32x4*>(base + static_cast<int64_t>(src) * bytes);
+  u32x4* d = reinterpret_cast<u32x4*>(base + static_cast<int64_t>(dst) * bytes);
+  const int64_t n16 = bytes / 16;
   for (int64_t i = threadIdx.x; i < n16; i += 256) d[i] = s[i];
 }
 
@@ -240,36 +297,72 @@ __device__ __forceinline__ int block_id(int id0, int id1, int id2, int id3, int 
 }
 
 // ---------------------------------------------------------------------------
-// decode_partial, bf16
+// decode_partial, bf16 queries (bf16 cache, or 8-bit E4M3 cache)
 //
-// Work unit: one 16-token block (a 4 KiB K tile and a 4 KiB V tile of one KV
-// head).  With lane l = 16*g + c (g = l/16, c = l%16):
-//   scores S^T = K · Q^T with v_mfma_f32_16x16x32_bf16 over four 32-wide
-//   slices of the head dimension: A = K tile (row = token c, k = 8 values of
-//   16-byte chunk g of the slice), B = Q^T (column = query head c, same k).
+// Work unit: one 16-token block of one KV head.  With lane l = 16*g + c
+// (g = l/16, c = l%16):
+//   scores S^T = K · Q^T with v_mfma_f32_16x16x32_bf16 over 32-wide slices of
+//   the head dimension: A = K tile (row = token c, k = 8 values of 16-byte
+//   chunk g of the slice), B = Q^T (column = query head c, same k).
 //   Lane l receives the scores of tokens 4g..4g+3 for head c.
 //   out^T += V^T · P with v_mfma_f32_16x16x16_bf16 per 16 value columns:
-//   A = V^T (row = value column c, k = tokens 4g..4g+3, read as one 8-byte
-//   run of the token-fastest V tile), B = P (the lane's own four
-//   probabilities, head c).  Lane l accumulates value columns
-//   16t+4g..16t+4g+3 of head c.
+//   A = V^T (row = a value column, k = tokens 4g..4g+3), B = P (the lane's
+//   own four probabilities, head c).
 // The token order inside k is the same on both operands, so only the max and
 // sum reductions move data between lanes.  NBUF blocks are in flight per
 // wave in rotating register sets: block i+NBUF is requested as soon as
 // block i has been consumed.
+//
+// bf16 cache: the K chunk is read as it lies; V^T row c of tile t is value
+// column 16t+c, read as one 8-byte run of the token-fastest V tile; lane l
+// accumulates value columns 16t+4g..16t+4g+3 of head c.
+//
+// 8-bit cache: each lane reads 16 bytes per 1 KiB of K (one token's 16
+// codes; MFMA 2i+h takes head-dimension values 16(4i+g)+8h.. of the chunk,
+// and Q is loaded in that order) and 16 bytes per 1 KiB of V (four value
+// columns 64a+4c+b, b = 0..3, of the lane's four tokens).  Codes become bf16
+// exactly (v_cvt_scalef32_pk_bf16_fp8, scale 1).  The per-token K scale
+// multiplies the lane's scores; the per-token V scale multiplies its
+// probabilities before they are rounded to bf16 for the PV product, so no
+// value is rescaled.  Tile t = 4a+b holds value column 64a+4c+b in row c;
+// lane l accumulates columns 64a+16g+4j+b (j = 0..3).
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
+template <int D, bool kFp8>
+struct BlockRegs;
 template <int D>
-struct BlockRegs {
+struct BlockRegs<D, false> {
   u32x4 k[D / 32];
   u32x2 v[D / 16];
 };
+template <int D>
+struct BlockRegs<D, true> {
+  u32x4 k[D / 64];
+  u32x4 v[D / 64];
+  f32x4 ks;              // scales of the lane's tokens 4g..4g+3
+  f32x4 vs;
+};
 
-template <int D, int NBUF>
+// Four E4M3 codes (one 32-bit word) -> four bf16 values, exactly.  The packed
+// result is used whole (as a 32-bit word) on purpose.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
+  const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+  return u32x2{lo, hi};
+}
+
+// Value column of accumulator element j of tile t for lane group g4.
+template <bool kFp8>
+__device__ __forceinline__ int acc_column(int t, int j, int g4) {
+  return kFp8 ? 64 * (t >> 2) + 16 * g4 + 4 * j + (t & 3) : 16 * t + 4 * g4 + j;
+}
+
+template <int D, int NBUF, bool kFp8>
 __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
-  constexpr int KC = D / 32;
-  constexpr int NT = D / 16;
+  constexpr int KC = D / 32;                   // QK MFMAs per block
+  constexpr int NT = D / 16;                   // PV MFMAs (value tiles) per block
+  constexpr int ELEM = kFp8 ? 1 : 2;           // cache bytes per value
   // Partials of the wave's finished partitions wait here until its load
   // stream ends: a global store in the middle of the stream would make every
   // later wait drain all loads in flight (stores and loads share vmcnt).
@@ -286,34 +379,47 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
   const int c16 = lane & 15;
   const int g4 = lane >> 4;
 
-  // Q^T operand: head c16, head-dim values 32c + 8g4 .. +7.
+  // Q^T operand of QK MFMA c: head c16, the head-dimension values that the
+  // K operand's lane holds (see above).
   bf16x8 qreg[KC];
   {
     const __bf16* q = static_cast<const __bf16*>(p.q) + (static_cast<size_t>(s_) * p.Hq + h0 + c16) * D;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
+      const int off = kFp8 ? 64 * (c >> 1) + 16 * g4 + 8 * (c & 1) : 32 * c + 8 * g4;
       u32x4 v = {0, 0, 0, 0};
-      if (c16 < nh) v = *reinterpret_cast<const u32x4*>(q + 32 * c + 8 * g4);
+      if (c16 < nh) v = *reinterpret_cast<const u32x4*>(q + off);
       qreg[c] = __builtin_bit_cast(bf16x8, v);
     }
   }
 
-  const size_t tile = static_cast<size_t>(kBlock) * D;               // elements per (block, head)
-  const size_t blk_bytes = static_cast<size_t>(p.Hkv) * tile * sizeof(__bf16);
-  const char* kc_b = reinterpret_cast<const char*>(static_cast<const __bf16*>(p.k_cache) + kvh * tile);
-  const char* vc_b = reinterpret_cast<const char*>(static_cast<const __bf16*>(p.v_cache) + kvh * tile);
+  const size_t tile_bytes = static_cast<size_t>(kBlock) * D * ELEM;  // one (block, head) tile
+  const size_t blk_bytes = static_cast<size_t>(p.Hkv) * tile_bytes;
+  const char* kc_b = static_cast<const char*>(p.k_cache) + kvh * tile_bytes;
+  const char* vc_b = static_cast<const char*>(p.v_cache) + kvh * tile_bytes;
   // Block bases are wave-uniform; per-lane byte offsets are 32-bit.
   const uint32_t k_off = static_cast<uint32_t>(lane) * 16u;
-  const uint32_t v_off = static_cast<uint32_t>(c16 * 4 + g4) * 8u;
+  const uint32_t v_off = kFp8 ? static_cast<uint32_t>(lane) * 16u : static_cast<uint32_t>(c16 * 4 + g4) * 8u;
 
-  auto load_block = [&](BlockRegs<D>& r, int i) {
+  auto load_block = [&](BlockRegs<D, kFp8>& r, int i) {
     const size_t b = static_cast<size_t>(block_id(id0, id1, id2, id3, i));
     const u32x4* kp = reinterpret_cast<const u32x4*>(kc_b + b * blk_bytes + k_off);
-    const u32x2* vp = reinterpret_cast<const u32x2*>(vc_b + b * blk_bytes + v_off);
+    if constexpr (kFp8) {
+      const u32x4* vp = reinterpret_cast<const u32x4*>(vc_b + b * blk_bytes + v_off);
 #pragma unroll
-    for (int c = 0; c < KC; ++c) r.k[c] = stream_load(kp + 64 * c);
+      for (int c = 0; c < D / 64; ++c) r.k[c] = stream_load(kp + 64 * c);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) r.v[t] = stream_load(vp + 64 * t);
+      for (int a = 0; a < D / 64; ++a) r.v[a] = stream_load(vp + 64 * a);
+      const size_t srow = (b * p.Hkv + kvh) * kBlock + 4 * g4;
+      r.ks = stream_load(reinterpret_cast<const f32x4*>(p.k_scale + srow));
+      r.vs = stream_load(reinterpret_cast<const f32x4*>(p.v_scale + srow));
+    } else {
+      const u32x2* vp = reinterpret_cast<const u32x2*>(vc_b + b * blk_bytes + v_off);
+#pragma unroll
+      for (int c = 0; c < KC; ++c) r.k[c] = stream_load(kp + 64 * c);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) r.v[t] = stream_load(vp + 64 * t);
+    }
   };
 
   f32x4 acc[NT];
@@ -335,7 +441,7 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dst[16 * t + 4 * g4 + j] = acc[t][j];
+        for (int j = 0; j < 4; ++j) dst[acc_column<kFp8>(t, j, g4)] = acc[t][j];
       if (g4 == 0) {
         dst[D] = m_run;
         dst[D + 1] = l_tot;
@@ -350,17 +456,32 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
 
   // kTail: the block may hold tokens past the sequence end (only the wave's
   // last block can).
-  auto compute_block = [&](const BlockRegs<D>& r, int i, auto tail_tag) {
+  auto compute_block = [&](const BlockRegs<D, kFp8>& r, int i, auto tail_tag) {
     constexpr bool kTail = decltype(tail_tag)::value;
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (kFp8) {
 #pragma unroll
-    for (int c = 0; c < KC; ++c)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.k[c]), qreg[c], sc, 0, 0, 0);
+      for (int c = 0; c < D / 64; ++c) {
+        const u32x2 a0 = e4m3x4_to_bf16x4(r.k[c].x), a1 = e4m3x4_to_bf16x4(r.k[c].y);
+        const u32x2 a2 = e4m3x4_to_bf16x4(r.k[c].z), a3 = e4m3x4_to_bf16x4(r.k[c].w);
+        const u32x4 lo = {a0.x, a0.y, a1.x, a1.y};
+        const u32x4 hi = {a2.x, a2.y, a3.x, a3.y};
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, lo), qreg[2 * c], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hi), qreg[2 * c + 1], sc, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.k[c]), qreg[c], sc, 0, 0, 0);
+    }
     const int tok0 = (blk_first + i) * kBlock + 4 * g4;           // token of x[0]
     const bool tail = kTail && (blk_first + i + 1) * kBlock > t_end;
     float x[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) x[j] = sc[j] * p.scale_log2;
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (kFp8) x[j] = sc[j] * (r.ks[j] * p.scale_log2);
+      else x[j] = sc[j] * p.scale_log2;
+    }
     if (tail) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -380,23 +501,50 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
     }
     bf16x4 pb;
     float ps = 0.f;
+    if constexpr (kFp8) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const __bf16 e = static_cast<__bf16>(exp2_fast(x[j] - m_run));
-      pb[j] = e;
-      ps += static_cast<float>(e);
+      for (int j = 0; j < 4; ++j) {
+        const float e = exp2_fast(x[j] - m_run);
+        const float vsj = (tail && tok0 + j >= t_end) ? 0.f : r.vs[j];   // NaN-poisoned slots
+        pb[j] = static_cast<__bf16>(e * vsj);
+        ps += e;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const __bf16 e = static_cast<__bf16>(exp2_fast(x[j] - m_run));
+        pb[j] = e;
+        ps += static_cast<float>(e);
+      }
     }
     l_run += ps;
-    uint32_t mk0 = 0xFFFFFFFFu, mk1 = 0xFFFFFFFFu;
-    if (tail) {
-      auto half = [&](int tok) -> uint32_t { return tok < t_end ? 0xFFFFu : 0u; };
-      mk0 = half(tok0) | (half(tok0 + 1) << 16);
-      mk1 = half(tok0 + 2) | (half(tok0 + 3) << 16);
-    }
+    if constexpr (kFp8) {
+      uint32_t mk = 0xFFFFFFFFu;                // byte k of a word = token 4g+k
+      if (tail) {
+        mk = 0u;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const u32x2 vv = {r.v[t].x & mk0, r.v[t].y & mk1};
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vv), pb, acc[t], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) mk |= (tok0 + j < t_end ? 0xFFu : 0u) << (8 * j);
+      }
+#pragma unroll
+      for (int a = 0; a < D / 64; ++a) {
+        const uint32_t w[4] = {r.v[a].x, r.v[a].y, r.v[a].z, r.v[a].w};
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          acc[4 * a + b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              __builtin_bit_cast(bf16x4, e4m3x4_to_bf16x4(w[b] & mk)), pb, acc[4 * a + b], 0, 0, 0);
+      }
+    } else {
+      uint32_t mk0 = 0xFFFFFFFFu, mk1 = 0xFFFFFFFFu;
+      if (tail) {
+        auto half = [&](int tok) -> uint32_t { return tok < t_end ? 0xFFFFu : 0u; };
+        mk0 = half(tok0) | (half(tok0 + 1) << 16);
+        mk1 = half(tok0 + 2) | (half(tok0 + 3) << 16);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const u32x2 vv = {r.v[t].x & mk0, r.v[t].y & mk1};
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vv), pb, acc[t], 0, 0, 0);
+      }
     }
     if (i + 1 == next_boundary && i + 1 < nblk) {
       stage_partition();
@@ -409,7 +557,7 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
   // finishes the last blocks (and short runs).
   using NoTail = std::integral_constant<bool, false>;
   using MayTail = std::integral_constant<bool, true>;
-  BlockRegs<D> buf[NBUF];
+  BlockRegs<D, kFp8> buf[NBUF];
   int i = 0;
   if (nblk >= 2 * NBUF) {
     // Issue order matters: the loop expects buf[0] to be the oldest load in
@@ -461,19 +609,40 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
   const size_t head_row = static_cast<size_t>(s_) * p.Hq + h0 + c16;
   if (P == 1) {
     const float inv = 1.f / l_tot;
-    __bf16* out = static_cast<__bf16*>(p.out) + head_row * D + 4 * g4;
+    __bf16* out = static_cast<__bf16*>(p.out) + head_row * D;
+    if constexpr (kFp8) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      bf16x4 o;
+      for (int a = 0; a < D / 64; ++a)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] = static_cast<__bf16>(acc[t][j] * inv);
-      *reinterpret_cast<bf16x4*>(out + 16 * t) = o;
+        for (int j = 0; j < 4; ++j) {
+          bf16x4 o;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) o[b] = static_cast<__bf16>(acc[4 * a + b][j] * inv);
+          *reinterpret_cast<bf16x4*>(out + acc_column<true>(4 * a, j, g4)) = o;
+        }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        bf16x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = static_cast<__bf16>(acc[t][j] * inv);
+        *reinterpret_cast<bf16x4*>(out + acc_column<false>(t, 0, g4)) = o;
+      }
     }
   } else {
     const size_t row = head_row * p.pmax + part_end - 1;
-    float* pa = p.part_acc + row * D + 4 * g4;
+    float* pa = p.part_acc + row * D;
+    if constexpr (kFp8) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4*>(pa + 16 * t) = acc[t];
+      for (int a = 0; a < D / 64; ++a)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<f32x4*>(pa + acc_column<true>(4 * a, j, g4)) =
+              f32x4{acc[4 * a][j], acc[4 * a + 1][j], acc[4 * a + 2][j], acc[4 * a + 3][j]};
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4*>(pa + acc_column<false>(t, 0, g4)) = acc[t];
+    }
     if (g4 == 0) {
       p.part_ml[2 * row] = m_run;
       p.part_ml[2 * row + 1] = l_tot;
@@ -669,7 +838,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams p) {
 // ---------------------------------------------------------------------------
 hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t stream) {
   if (p.n_pairs <= 0 || p.n_layers <= 0) return hipSuccess;
-  dim3 grid(p.n_pairs, p.n_layers, 2);
+  dim3 grid(p.n_pairs, p.n_layers, p.scale_bytes > 0 ? 4 : 2);
   hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
@@ -687,24 +856,29 @@ hipError_t launch_table_upload(const int32_t* host_src, int32_t* dev_tables, int
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream) {
   if (p.n <= 0) return hipSuccess;
   dim3 grid(p.n, p.num_kv_heads);
-  if (p.elem_bytes == 4)
+  if (p.elem_bytes == 1)
+    hipLaunchKernelGGL(kv_append_fp8_kernel, grid, dim3(64), 0, stream, p);
+  else if (p.elem_bytes == 4)
     hipLaunchKernelGGL(kv_append_kernel<uint32_t>, grid, dim3(64), 0, stream, p);
   else
     hipLaunchKernelGGL(kv_append_kernel<uint16_t>, grid, dim3(64), 0, stream, p);
   return hipGetLastError();
 }
 
-bool decode_shape_supported(int dtype, int head_dim, int block_size) {
-  return block_size == kBlock && (dtype == 0 || dtype == 1) && (head_dim == 64 || head_dim == 128);
+bool decode_shape_supported(int kind, int head_dim, int block_size) {
+  if (block_size != kBlock) return false;
+  if (kind == kDecodeF32 || kind == kDecodeBF16) return head_dim == 64 || head_dim == 128;
+  if (kind == kDecodeFP8KV) return head_dim == 64 || head_dim == 128;
+  return false;
 }
 
-// Partitions per wave for the bf16 kernel.  Each wave streams a run of
+// Partitions per wave for the bf16-query kernels.  Each wave streams a run of
 // consecutive partitions; for long batches runs are made as long as possible
 // while the grid still fills every resident wave slot once (one round:
 // equal-length runs then finish together instead of leaving a partly filled
 // last round).
 // PKV_WAVE_PARTITIONS overrides the choice.
-template <int D>
+template <int D, int NBUF, bool kFp8>
 static int pick_partitions_per_wave(const DecodeParams& p) {
   static int slots = 0;   // resident waves on the device (per kernel variant)
   static int forced = -1;
@@ -712,7 +886,6 @@ static int pick_partitions_per_wave(const DecodeParams& p) {
     const char* e = std::getenv("PKV_WAVE_PARTITIONS");
     forced = e ? std::max(0, std::atoi(e)) : 0;
   }
-  const int hg = (p.G + 15) / 16;
   const int rows = std::min(16, p.G);
   int max_ppw = std::min(p.pmax, kMaxWaveBlocks * kBlock / p.partition);
   // LDS for the staged partials stays within 20 KiB per wave, so eight
@@ -725,7 +898,7 @@ static int pick_partitions_per_wave(const DecodeParams& p) {
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_partial_bf16<D, kDepth>, 64, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_partial_bf16<D, NBUF, kFp8>, 64, 0) !=
             hipSuccess || per_cu <= 0)
       per_cu = 8;
     slots = cus * per_cu;
@@ -733,34 +906,48 @@ static int pick_partitions_per_wave(const DecodeParams& p) {
   // Long runs pay only for batches of equal-length sequences with at least
   // three rounds of work; mixed lengths balance better with one partition
   // per wave.  Without the caller's length hint nothing is known: one.
-  (void)hg;
   if (p.tasks_hint <= 0 || !p.uniform_hint || p.tasks_hint < 3LL * slots) return 1;
   return static_cast<int>(std::min<long long>(p.tasks_hint / slots, max_ppw));
 }
 
-hipError_t launch_decode_partial(const DecodeParams& p0, int dtype, hipStream_t stream) {
-  DecodeParams p = p0;
-  p.ppw = dtype != 1 ? 1 : (p.d == 128 ? pick_partitions_per_wave<128>(p) : pick_partitions_per_wave<64>(p));
+template <int D, int NBUF, bool kFp8>
+static hipError_t launch_bf16q(DecodeParams p, hipStream_t stream) {
+  p.ppw = pick_partitions_per_wave<D, NBUF, kFp8>(p);
   const long long groups = (p.pmax + p.ppw - 1) / p.ppw;
-  const long long gx = groups * p.S * p.Hkv;
-  dim3 grid(static_cast<unsigned>(gx), (p.G + 15) / 16);
-  if (dtype == 1) {
-    const size_t shmem = static_cast<size_t>(p.ppw - 1) * std::min(16, p.G) * (p.d + 2) * sizeof(float);
-    if (p.d == 128) hipLaunchKernelGGL((decode_partial_bf16<128, kDepth>), grid, dim3(64), shmem, stream, p);
-    else if (p.d == 64) hipLaunchKernelGGL((decode_partial_bf16<64, kDepth>), grid, dim3(64), shmem, stream, p);
-    else return hipErrorInvalidValue;
-  } else {
-    if (p.d == 128) hipLaunchKernelGGL(decode_partial_f32<128>, grid, dim3(64), 0, stream, p);
-    else if (p.d == 64) hipLaunchKernelGGL(decode_partial_f32<64>, grid, dim3(64), 0, stream, p);
-    else return hipErrorInvalidValue;
-  }
+  dim3 grid(static_cast<unsigned>(groups * p.S * p.Hkv), (p.G + 15) / 16);
+  const size_t shmem = static_cast<size_t>(p.ppw - 1) * std::min(16, p.G) * (p.d + 2) * sizeof(float);
+  hipLaunchKernelGGL((decode_partial_bf16<D, NBUF, kFp8>), grid, dim3(64), shmem, stream, p);
   return hipGetLastError();
 }
 
-hipError_t launch_decode_reduce(const DecodeParams& p, int dtype, hipStream_t stream) {
+hipError_t launch_decode_partial(const DecodeParams& p0, int kind, hipStream_t stream) {
+  DecodeParams p = p0;
+  switch (kind) {
+    case kDecodeBF16:
+      if (p.d == 128) return launch_bf16q<128, kDepth, false>(p, stream);
+      if (p.d == 64) return launch_bf16q<64, kDepth, false>(p, stream);
+      return hipErrorInvalidValue;
+    case kDecodeFP8KV:
+      if (p.d == 128) return launch_bf16q<128, kDepthFp8, true>(p, stream);
+      if (p.d == 64) return launch_bf16q<64, kDepthFp8, true>(p, stream);
+      return hipErrorInvalidValue;
+    case kDecodeF32: {
+      p.ppw = 1;
+      dim3 grid(static_cast<unsigned>(static_cast<long long>(p.pmax) * p.S * p.Hkv), (p.G + 15) / 16);
+      if (p.d == 128) hipLaunchKernelGGL(decode_partial_f32<128>, grid, dim3(64), 0, stream, p);
+      else if (p.d == 64) hipLaunchKernelGGL(decode_partial_f32<64>, grid, dim3(64), 0, stream, p);
+      else return hipErrorInvalidValue;
+      return hipGetLastError();
+    }
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_reduce(const DecodeParams& p, int kind, hipStream_t stream) {
   if (p.pmax <= 1) return hipSuccess;
   dim3 grid(static_cast<unsigned>(p.S * p.Hq));
-  if (dtype == 1) {
+  if (kind == kDecodeBF16 || kind == kDecodeFP8KV) {   // bf16 outputs
     if (p.d == 128) hipLaunchKernelGGL((decode_reduce_kernel<__bf16, 128>), grid, dim3(256), 0, stream, p);
     else if (p.d == 64) hipLaunchKernelGGL((decode_reduce_kernel<__bf16, 64>), grid, dim3(256), 0, stream, p);
     else return hipErrorInvalidValue;

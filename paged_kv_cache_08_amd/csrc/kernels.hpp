@@ -16,10 +16,13 @@ constexpr int kCopyMaxPairs = 64;
 struct CopyBlocksParams {
   void* k[kCopyMaxLayers];
   void* v[kCopyMaxLayers];
+  void* ks[kCopyMaxLayers];   // 8-bit pools: per-slot scales of K and V
+  void* vs[kCopyMaxLayers];
   int32_t pairs[2 * kCopyMaxPairs];
   int32_t n_layers;
   int32_t n_pairs;
   int64_t block_bytes;   // bytes of one block (all heads) in one layer's K or V
+  int64_t scale_bytes;   // bytes of one block's scales (0: no scale arrays)
 };
 
 struct AppendParams {
@@ -36,7 +39,9 @@ struct AppendParams {
   int32_t num_kv_heads;
   int32_t head_dim;
   int32_t block_size;
-  int32_t elem_bytes;    // 4 (fp32) or 2 (bf16)
+  int32_t elem_bytes;    // 4 (fp32) or 2 (bf16) of the pool; 1: 8-bit pool
+  float* k_scale;        // 8-bit pool: per-slot scales [block][head][B]
+  float* v_scale;
 };
 
 struct DecodeParams {
@@ -46,6 +51,8 @@ struct DecodeParams {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* seq_lens;
+  const float* k_scale;  // 8-bit cache: per-slot scales [block][head][B]
+  const float* v_scale;
   float* part_ml;        // [S][Hq][Pmax][2]   (running max in log2 units, sum)
   float* part_acc;       // [S][Hq][Pmax][d]   unnormalised accumulators
   int32_t S, Hq, Hkv, G, d;
@@ -63,10 +70,15 @@ hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t stream);
 hipError_t launch_table_upload(const int32_t* host_src, int32_t* dev_tables, int64_t n_tab, int32_t* dev_lens,
                                int32_t n_len, hipStream_t stream);
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream);
-// dtype: 0 = fp32, 1 = bf16.  Returns hipErrorInvalidValue for shapes
-// without a kernel (checked by the caller first).
-hipError_t launch_decode_partial(const DecodeParams& p, int dtype, hipStream_t stream);
-hipError_t launch_decode_reduce(const DecodeParams& p, int dtype, hipStream_t stream);
-bool decode_shape_supported(int dtype, int head_dim, int block_size);
+// Decode kernel families.  Returns hipErrorInvalidValue for shapes without a
+// kernel (checked by the caller first).
+enum DecodeKind : int {
+  kDecodeF32 = 0,      // fp32 queries, fp32 cache
+  kDecodeBF16 = 1,     // bf16 queries, bf16 cache
+  kDecodeFP8KV = 2,    // bf16 queries, 8-bit E4M3 cache with per-slot scales
+};
+hipError_t launch_decode_partial(const DecodeParams& p, int kind, hipStream_t stream);
+hipError_t launch_decode_reduce(const DecodeParams& p, int kind, hipStream_t stream);
+bool decode_shape_supported(int kind, int head_dim, int block_size);
 
 }  // namespace pkv

@@ -14,7 +14,10 @@ import torch
 
 from . import pkv as P
 
-_DT = {"f32": (torch.float32, P.PKV_F32), "bf16": (torch.bfloat16, P.PKV_BF16)}
+# cache dtype -> (cache tensor dtype, pool dtype, token/query dtype)
+_DT = {"f32": (torch.float32, P.PKV_F32, torch.float32),
+       "bf16": (torch.bfloat16, P.PKV_BF16, torch.bfloat16),
+       "fp8": (torch.uint8, P.PKV_FP8_E4M3, torch.bfloat16)}
 
 
 class PagedDecodeEngine:
@@ -22,16 +25,22 @@ class PagedDecodeEngine:
                  dtype: str = "bf16", block_size: int = 16, init_perm=None, device="cuda",
                  poison: bool = True, partition: int = 0):
         self.L, self.Hkv, self.d, self.N, self.B = num_layers, num_kv_heads, head_dim, num_blocks, block_size
-        self.dtype = dtype
-        self.tdtype, self.cdtype = _DT[dtype]
+        self.dtype = dtype                 # cache dtype: "f32", "bf16" or "fp8"
+        self.tdtype, self.cdtype, self.qdtype = _DT[dtype]
         self.device = torch.device(device)
         self.partition = partition
         numel = num_blocks * num_kv_heads * head_dim * block_size
-        fill = float("nan") if poison else 0.0
+        fill = (0x7F if dtype == "fp8" else float("nan")) if poison else 0   # 0x7F: the E4M3 NaN
         self.k = [torch.full((numel,), fill, dtype=self.tdtype, device=self.device) for _ in range(num_layers)]
         self.v = [torch.full((numel,), fill, dtype=self.tdtype, device=self.device) for _ in range(num_layers)]
+        self.ks = self.vs = None
+        if dtype == "fp8":                 # one fp32 scale per (slot, KV head)
+            sfill = float("nan") if poison else 0.0
+            nsc = num_blocks * num_kv_heads * block_size
+            self.ks = [torch.full((nsc,), sfill, dtype=torch.float32, device=self.device) for _ in range(num_layers)]
+            self.vs = [torch.full((nsc,), sfill, dtype=torch.float32, device=self.device) for _ in range(num_layers)]
         self.pool = P.pkv_pool_create(num_layers, num_kv_heads, head_dim, block_size, num_blocks,
-                                      self.cdtype, self.k, self.v, init_perm)
+                                      self.cdtype, self.k, self.v, init_perm, self.ks, self.vs)
         self.tables = None
         self.lens = None
         self.host_lens = None      # host copy of the last uploaded lengths
@@ -135,7 +144,9 @@ class PagedDecodeEngine:
             self.workspace = torch.empty((need,), dtype=torch.uint8, device=self.device)
         return P.decode_args(q, out, self.k[layer], self.v[layer], self.tables, self.lens, self.Hkv, self.N,
                              max_seq_len, scale, self.partition, self.workspace if need else None, self.B,
-                             host_seq_lens=self.host_lens)
+                             host_seq_lens=self.host_lens,
+                             k_scale=None if self.ks is None else self.ks[layer],
+                             v_scale=None if self.vs is None else self.vs[layer])
 
     def decode(self, layer: int, q: torch.Tensor, max_seq_len: int, out: Optional[torch.Tensor] = None,
                scale: Optional[float] = None, stream=None) -> torch.Tensor:

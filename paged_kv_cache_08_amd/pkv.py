@@ -25,6 +25,7 @@ PKV_ERR_HIP = -4
 PKV_ERR_UNSUPPORTED = -5
 PKV_F32 = 0
 PKV_BF16 = 1
+PKV_FP8_E4M3 = 2
 
 _i32 = ctypes.c_int32
 _i64 = ctypes.c_int64
@@ -41,7 +42,8 @@ class PkvError(RuntimeError):
 class pkv_pool_desc(ctypes.Structure):
     _fields_ = [("num_layers", _i32), ("num_kv_heads", _i32), ("head_dim", _i32),
                 ("block_size", _i32), ("num_blocks", _i32), ("dtype", _i32),
-                ("k_cache", _P(_vp)), ("v_cache", _P(_vp)), ("init_perm", _P(_i32))]
+                ("k_cache", _P(_vp)), ("v_cache", _P(_vp)), ("init_perm", _P(_i32)),
+                ("k_scale", _P(_vp)), ("v_scale", _P(_vp))]
 
 
 class pkv_stats(ctypes.Structure):
@@ -56,7 +58,8 @@ class pkv_decode_args(ctypes.Structure):
                 ("num_seqs", _i32), ("num_q_heads", _i32), ("num_kv_heads", _i32),
                 ("head_dim", _i32), ("block_size", _i32), ("num_blocks", _i32),
                 ("max_blocks", _i32), ("max_seq_len", _i32), ("partition", _i32),
-                ("dtype", _i32), ("scale", ctypes.c_float), ("host_seq_lens", _vp)]
+                ("dtype", _i32), ("scale", ctypes.c_float), ("host_seq_lens", _vp),
+                ("k_scale", _vp), ("v_scale", _vp), ("kv_dtype", _i32)]
 
 
 _lib = None
@@ -168,15 +171,22 @@ class PoolHandle:
 
 def pkv_pool_create(num_layers: int, num_kv_heads: int, head_dim: int, block_size: int,
                     num_blocks: int, dtype: int, k_cache: Optional[Sequence] = None,
-                    v_cache: Optional[Sequence] = None, init_perm=None) -> PoolHandle:
+                    v_cache: Optional[Sequence] = None, init_perm=None,
+                    k_scale: Optional[Sequence] = None, v_scale: Optional[Sequence] = None) -> PoolHandle:
+    """k_scale / v_scale: per-layer fp32 scale tensors of an 8-bit pool."""
     d = pkv_pool_desc(num_layers, num_kv_heads, head_dim, block_size, num_blocks, dtype)
     keep = []
+
+    def ptrs(ts):
+        arr = (_vp * num_layers)(*[_ptr(t) for t in ts])
+        keep.append(arr)
+        return ctypes.cast(arr, _P(_vp))
     if k_cache is not None:
-        kp = (_vp * num_layers)(*[_ptr(t) for t in k_cache])
-        vp = (_vp * num_layers)(*[_ptr(t) for t in v_cache])
-        d.k_cache = ctypes.cast(kp, _P(_vp))
-        d.v_cache = ctypes.cast(vp, _P(_vp))
-        keep += [kp, vp]
+        d.k_cache = ptrs(k_cache)
+        d.v_cache = ptrs(v_cache)
+    if k_scale is not None:
+        d.k_scale = ptrs(k_scale)
+        d.v_scale = ptrs(v_scale)
     if init_perm is not None:
         perm = np.ascontiguousarray(init_perm, dtype=np.int32)
         d.init_perm = _as_i32p(perm)
@@ -318,10 +328,13 @@ def pkv_decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, m
 
 def decode_args(q, out, k_cache, v_cache, block_tables, seq_lens, num_kv_heads: int, num_blocks: int,
                 max_seq_len: int, scale: Optional[float] = None, partition: int = 0, workspace=None,
-                block_size: int = 16, host_seq_lens: Optional[np.ndarray] = None) -> pkv_decode_args:
+                block_size: int = 16, host_seq_lens: Optional[np.ndarray] = None,
+                k_scale=None, v_scale=None) -> pkv_decode_args:
     """Pack a pkv_decode_args from tensors (q/out [S][Hq][d]).  host_seq_lens:
     optional int32 numpy array [S] (kept alive by the returned object; it is
-    read at every call, so it may be updated in place between calls)."""
+    read at every call, so it may be updated in place between calls).  The
+    cache type follows the cache tensors' dtype (uint8 = 8-bit E4M3 codes,
+    which need the layer's k_scale / v_scale tensors)."""
     import torch
     S, Hq, d = q.shape
     dtype = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}[q.dtype]
@@ -336,6 +349,8 @@ def decode_args(q, out, k_cache, v_cache, block_tables, seq_lens, num_kv_heads: 
     a.max_seq_len = max_seq_len
     a.partition = partition
     a.dtype = dtype
+    a.kv_dtype = PKV_FP8_E4M3 if k_cache.dtype == torch.uint8 else dtype
+    a.k_scale, a.v_scale = _ptr(k_scale), _ptr(v_scale)
     a.scale = 1.0 / math.sqrt(d) if scale is None else scale
     if host_seq_lens is not None:
         assert host_seq_lens.dtype == np.int32 and host_seq_lens.flags.c_contiguous

@@ -34,7 +34,7 @@ def run_gpu(wl, k_log, v_log, q=None, layers=(0,), partition=0, scale=None, engi
     """Build the batch on the GPU through the library; optionally decode
     layer 0 with q.  k_log / v_log: {layer: device tensor}."""
     from paged_kv_cache_08_amd.engine import PagedDecodeEngine
-    eng = PagedDecodeEngine(engine_layers or (max(layers) + 1), wl.Hkv, wl.d, wl.num_blocks, wl.dtype,
+    eng = PagedDecodeEngine(engine_layers or (max(layers) + 1), wl.Hkv, wl.d, wl.num_blocks, wl.cache_dtype,
                             init_perm=wl.perm, partition=partition)
     log = eng.run_script(wl.setup_ops + wl.step_ops, wl, k_log, v_log, layers=layers)
     eng.sync(wl.seq_ids)
@@ -69,6 +69,9 @@ def check_pool(eng, rp, layer=0):
     ov = rp.pool.V[layer]
     gv = gpu_bits(eng.v[layer]).reshape(ov.shape)
     assert np.array_equal(gv, ov), "V pool differs"
+    if rp.pool.dtype == "fp8":
+        for name, o, g in (("K", rp.pool.KS[layer], eng.ks[layer]), ("V", rp.pool.VS[layer], eng.vs[layer])):
+            assert np.array_equal(gpu_bits(g).reshape(o.shape), o), f"{name} scales differ"
 
 
 def compare_out(gpu_out: torch.Tensor, ref: np.ndarray, rows=None):

@@ -10,8 +10,11 @@ from oracle.replay import Replay
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
-    """Raw bit patterns of a CPU fp32 / bf16 tensor as uint32 / uint16."""
+    """Raw bit patterns of a CPU fp32 / bf16 / uint8 tensor as uint32 /
+    uint16 / uint8."""
     t = t.detach().cpu().contiguous()
+    if t.dtype == torch.uint8:
+        return t.numpy()
     if t.dtype == torch.float32:
         return t.view(torch.int32).numpy().view(np.uint32)
     if t.dtype == torch.bfloat16:

@@ -63,6 +63,25 @@ def test_pool_create_validation():
         P.pkv_pool_create(0, 8, 128, 16, 4, P.PKV_BF16)
 
 
+def test_fp8_pool_create_validation():
+    P.pkv_pool_create(1, 8, 128, 16, 10, P.PKV_FP8_E4M3)            # allocator only: fine
+    for kw in (dict(head_dim=96), dict(block_size=32)):
+        args = dict(num_layers=1, num_kv_heads=8, head_dim=128, block_size=16, num_blocks=10,
+                    dtype=P.PKV_FP8_E4M3)
+        args.update(kw)
+        with pytest.raises(P.PkvError) as e:
+            P.pkv_pool_create(**args)
+        assert e.value.status == P.PKV_ERR_INVALID
+    # caches without scale arrays (pointers are only checked, never read)
+    with pytest.raises(P.PkvError) as e:
+        P.pkv_pool_create(1, 8, 128, 16, 10, P.PKV_FP8_E4M3, k_cache=[16], v_cache=[16])
+    assert "scale" in P.pkv_last_error()
+    with pytest.raises(P.PkvError):
+        P.pkv_pool_create(1, 8, 128, 16, 10, P.PKV_FP8_E4M3, k_cache=[16], v_cache=[16],
+                          k_scale=[16], v_scale=[4])
+    P.pkv_pool_create(1, 8, 128, 16, 10, P.PKV_FP8_E4M3, k_cache=[16], v_cache=[16], k_scale=[32], v_scale=[48])
+
+
 def test_device_calls_rejected_without_caches():
     pool = P.pkv_pool_create(1, 1, 64, 16, 8, P.PKV_F32)
     with pytest.raises(P.PkvError) as e:
@@ -75,7 +94,8 @@ def _args(**kw):
     a = P.pkv_decode_args()
     base = dict(q=16, out=16, k_cache=16, v_cache=16, block_tables=16, seq_lens=16, workspace=0,
                 workspace_bytes=0, num_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
-                num_blocks=10, max_blocks=4, max_seq_len=64, partition=0, dtype=P.PKV_BF16, scale=0.1)
+                num_blocks=10, max_blocks=4, max_seq_len=64, partition=0, dtype=P.PKV_BF16, scale=0.1,
+                kv_dtype=P.PKV_BF16)
     base.update(kw)
     for k, v in base.items():
         setattr(a, k, v)
@@ -93,6 +113,11 @@ def _args(**kw):
     (dict(q=8), P.PKV_ERR_INVALID),                       # misaligned
     (dict(max_seq_len=4096), P.PKV_ERR_INVALID),          # needs a workspace
     (dict(dtype=7), P.PKV_ERR_INVALID),
+    (dict(kv_dtype=P.PKV_F32), P.PKV_ERR_INVALID),       # cache type differs from bf16 queries
+    (dict(dtype=P.PKV_F32, kv_dtype=P.PKV_FP8_E4M3), P.PKV_ERR_INVALID),
+    (dict(kv_dtype=P.PKV_FP8_E4M3), P.PKV_ERR_INVALID),  # no scale arrays
+    (dict(kv_dtype=P.PKV_FP8_E4M3, k_scale=16, v_scale=8), P.PKV_ERR_INVALID),   # misaligned
+    (dict(kv_dtype=P.PKV_FP8_E4M3, k_scale=16, v_scale=16, head_dim=96), P.PKV_ERR_UNSUPPORTED),
 ])
 def test_decode_argument_validation(bad, status):
     with pytest.raises(P.PkvError) as e:

@@ -1,0 +1,229 @@
+"""GPU parity of the 8-bit (E4M3) KV cache: the library's quantising
+kv_append, copy-on-write of codes and scales, and the decode kernel reading
+codes, against the oracle on the same seeded bf16 inputs.
+
+Codes and scales are compared bit for bit (the oracle takes every rounding
+decision in the same fp32 precision: amax / 448, value / scale, nearest
+E4M3 with ties to even); outputs with the bf16 bar (max |err| <= 2e-2,
+row-normwise <= 1e-2) against exact fp64 attention over the dequantised
+cache.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_common import (check_allocator, check_pool, compare_out, gpu_bits, need_gpu, note, oracle_out,
+                        oracle_replay, run_gpu)
+from helpers import bits
+from oracle.replay import Replay
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(wl, partition=0, scale=None, q_scale=1.0):
+    need_gpu()
+    note(f"fp8 case: {wl.description} partition={partition} q_scale={q_scale}")
+    q, k, v = wl.tensors(device="cuda")
+    if q_scale != 1.0:
+        q = (q.float() * q_scale).to(q.dtype)
+    eng, log, out = run_gpu(wl, {0: k}, {0: v}, q, partition=partition, scale=scale)
+    rp = oracle_replay(wl, {0: k}, {0: v})
+    check_allocator(eng, rp, log)
+    check_pool(eng, rp)
+    ref = oracle_out(rp, wl, q, scale=scale)
+    err = compare_out(out[0], ref)
+    note(f"  max_abs={err[0]:.3e} row_rel={err[1]:.3e}")
+    return eng, log, out[0], ref
+
+
+SHAPES = [
+    # S, Hq, Hkv, d, max_len
+    (5, 8, 2, 128, 300),
+    (4, 40, 8, 128, 1100),
+    (3, 40, 2, 128, 700),        # two query-head groups per KV head
+    (6, 8, 1, 64, 200),
+    (4, 64, 8, 128, 2100),
+    (3, 32, 32, 128, 900),       # MHA
+    (4, 12, 3, 64, 1500),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fp8_shapes(shape):
+    S, Hq, Hkv, d, ml = shape
+    base = workloads.random_small(140 + len(str(shape)), S=S, Hq=Hq, Hkv=Hkv, d=d, dtype="bf16", max_len=ml)
+    _case(workloads.fp8_cache(base))
+
+
+EDGE = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 511, 512, 513, 1023, 1024, 1025, 1535]
+
+
+@pytest.mark.parametrize("partition", [0, 32, 64, 1024])
+def test_fp8_edge_lengths(partition):
+    wl = workloads.with_lengths(EDGE, Hq=16, Hkv=4, d=128, dtype="bf16", seed=partition + 11)
+    _case(workloads.fp8_cache(wl), partition=partition)
+
+
+def test_fp8_extreme_logits():
+    base = workloads.random_small(161, S=4, Hq=8, Hkv=2, d=128, dtype="bf16", max_len=700)
+    _case(workloads.fp8_cache(base), q_scale=3000.0)
+
+
+def test_fp8_zero_and_tiny_rows():
+    """Rows of zeros get scale 0 and codes 0; rows far below 1 keep their
+    relative precision (the scale follows the row)."""
+    need_gpu()
+    wl = workloads.fp8_cache(workloads.random_small(162, S=3, Hq=8, Hkv=2, d=128, dtype="bf16", max_len=200))
+    q, k, v = wl.tensors(device="cuda")
+    k[5:40] = 0
+    v[17:30] = 0
+    k[50:90] *= 1e-20
+    v[60:120] *= 1e-12
+    eng, log, out = run_gpu(wl, {0: k}, {0: v}, q)
+    rp = oracle_replay(wl, {0: k}, {0: v})
+    check_allocator(eng, rp, log)
+    check_pool(eng, rp)
+    compare_out(out[0], oracle_out(rp, wl, q))
+
+
+def _cow_workload(d=128):
+    lengths = np.array([21, 21, 21, 37])
+    ops = [("create",), ("extend", 0, 20, 0, 0), ("fork", 0), ("fork", 0),
+           ("append", [(1, 1, 20), (2, 2, 20), (0, 0, 20)]),
+           ("fork", 1), ("extend", 3, 15, 3, 21)]
+    step = [("append", [(3, 3, 36)])]
+    return workloads.Workload("cow_fp8", 2, 8, 2, d, "bf16", lengths, 12,
+                              np.arange(12, dtype=np.int32)[::-1].copy(), ops, step, [0, 1, 2, 3], 78,
+                              description="fork/copy-on-write script, fp8 cache", kv_dtype="fp8")
+
+
+def test_fp8_copy_on_write_two_layers():
+    """A shared partial block is copied whole (codes and scales, every
+    layer) before the writer's token lands."""
+    need_gpu()
+    wl = _cow_workload()
+    t0 = wl.tensors(0, device="cuda")
+    t1 = wl.tensors(1, device="cuda")
+    k = {0: t0[1], 1: t1[1]}
+    v = {0: t0[2], 1: t1[2]}
+    eng, log, out = run_gpu(wl, k, v, {0: t0[0], 1: t1[0]}, layers=(0, 1))
+    assert [len(c) for _, _, _, c in log] == [0, 2, 1, 0]
+    rp = oracle_replay(wl, k, v, layers=(0, 1))
+    check_allocator(eng, rp, log)
+    for layer, q in ((0, t0[0]), (1, t1[0])):
+        check_pool(eng, rp, layer)
+        compare_out(out[layer], oracle_out(rp, wl, q, layer=layer))
+
+
+def test_fp8_step_append_matches_oracle():
+    """The decode-step form (table upload + kv_append_last) quantises the
+    new token in place."""
+    need_gpu()
+    from paged_kv_cache_08_amd.engine import PagedDecodeEngine
+    wl = workloads.fp8_cache(workloads.random_small(190, S=7, Hq=8, Hkv=2, d=128, dtype="bf16", max_len=300))
+    q, k, v = wl.tensors(device="cuda")
+    eng = PagedDecodeEngine(1, wl.Hkv, wl.d, wl.num_blocks, "fp8", init_perm=wl.perm)
+    log = eng.run_script(wl.setup_ops, wl, {0: k}, {0: v})
+    (kind, entries), = wl.step_ops
+    offs = wl.offsets
+    rows = torch.tensor([offs[src] + pos for (_, src, pos) in entries], device="cuda")
+    ids = [e[0] for e in entries]
+    slots, cow = eng.step_append(ids, {0: (k.index_select(0, rows), v.index_select(0, rows))})
+    log.append(("append", ids, slots, cow))
+    eng.sync(wl.seq_ids)
+    out = eng.decode(0, q, max_seq_len=wl.max_len)
+    torch.cuda.synchronize()
+    rp = oracle_replay(wl, {0: k}, {0: v})
+    check_allocator(eng, rp, log)
+    check_pool(eng, rp)
+    compare_out(out, oracle_out(rp, wl, q))
+
+
+def test_fp8_wave_split_and_permutation_keep_bits():
+    need_gpu()
+    import paged_kv_cache_08_amd.pkv as P
+    wl = workloads.fp8_cache(workloads.with_lengths([3072] * 8, Hq=32, Hkv=8, d=128, dtype="bf16", seed=121))
+    q, k, v = wl.tensors(device="cuda")
+    eng, _, out = run_gpu(wl, {0: k}, {0: v}, q, partition=32)
+    no_hint = torch.empty_like(q)
+    a = eng.decode_args(0, q, no_hint, wl.max_len)
+    a.host_seq_lens = None
+    P.pkv_paged_attention_decode(a)
+    torch.cuda.synchronize()
+    assert torch.equal(out[0].view(torch.int16), no_hint.view(torch.int16))
+    del eng
+    wl2 = dataclasses.replace(wl, perm=np.random.default_rng(7).permutation(wl.num_blocks).astype(np.int32))
+    _, _, out2 = run_gpu(wl2, {0: k}, {0: v}, q, partition=32)
+    assert torch.equal(out[0].view(torch.int16), out2[0].view(torch.int16))
+    rp = oracle_replay(wl, {0: k}, {0: v})
+    compare_out(out[0], oracle_out(rp, wl, q))
+
+
+def test_fp8_shared_prefix_equals_private_copies_bits():
+    need_gpu()
+    kw = dict(seed=19, S=12, prefix=256, lo=16, hi=200)
+    sh = workloads.fp8_cache(workloads.shared_prefix(**kw))
+    pr = workloads.fp8_cache(workloads.shared_prefix(private_copies=True, **kw))
+    q, k, v = sh.tensors(device="cuda")
+    offs = sh.offsets
+    for s in range(1, sh.S):
+        k[offs[s]:offs[s] + 256] = k[0:256]
+        v[offs[s]:offs[s] + 256] = v[0:256]
+    _, _, out_s = run_gpu(sh, {0: k}, {0: v}, q)
+    _, _, out_p = run_gpu(pr, {0: k}, {0: v}, q)
+    assert torch.equal(out_s[0].view(torch.int16), out_p[0].view(torch.int16))
+
+
+def _check_sampled(eng, wl, k_log, v_log, q, out, seqs, rows, layer=0):
+    """Replay the whole allocator script but quantise only the sampled
+    sequences' tokens; compare their blocks (codes and scales) bit for bit
+    and the sampled output rows with the tolerance."""
+    rp = Replay(wl, layers=layer + 1)
+    rp.run(wl.setup_ops + wl.step_ops, {layer: (bits(k_log.cpu()), bits(v_log.cpu()))}, sources=set(seqs))
+    assert eng.snapshot() == tuple(rp.alloc.snapshot())
+    pool = rp.pool
+    gk = gpu_bits(eng.k[layer]).reshape(pool.K[layer].shape)
+    gv = gpu_bits(eng.v[layer]).reshape(pool.V[layer].shape)
+    gks = gpu_bits(eng.ks[layer]).reshape(pool.KS[layer].shape)
+    gvs = gpu_bits(eng.vs[layer]).reshape(pool.VS[layer].shape)
+    tables, lengths = rp.tables(), rp.lengths()
+    for s in seqs:
+        n = lengths[s]
+        full, tail = divmod(n, 16)
+        blocks = np.asarray(tables[s][:full])
+        for ours, ref in ((gk, pool.K[layer]), (gv, pool.V[layer]), (gks, pool.KS[layer]), (gvs, pool.VS[layer])):
+            assert np.array_equal(ours[blocks], ref[blocks]), s
+        if tail:                       # the last block's written slots
+            b = tables[s][full]
+            assert np.array_equal(gk[b][:, :, :tail], pool.K[layer][b][:, :, :tail])
+            assert np.array_equal(gks[b][:, :tail], pool.KS[layer][b][:, :tail])
+            assert np.array_equal(gvs[b][:, :tail], pool.VS[layer][b][:, :tail])
+            for o in range(tail):      # V codes of slot o = 4u + w sit at [..][u][..][..][w]
+                assert np.array_equal(gv[b][:, :, o // 4, :, :, o % 4], pool.V[layer][b][:, :, o // 4, :, :, o % 4])
+    e = compare_out(out, oracle_out(rp, wl, q, layer=layer, rows=rows), rows=rows)
+    note(f"  sampled rows max_abs={e[0]:.3e} row_rel={e[1]:.3e}")
+    assert torch.isfinite(out.float()).all()
+
+
+def test_long_context_fp8_config_sampled():
+    need_gpu()
+    wl = workloads.CONFIGS["long_context_fp8"]()
+    note(wl.description)
+    q, k, v = wl.tensors(device="cuda")
+    eng, log, out = run_gpu(wl, {0: k}, {0: v}, q)
+    seqs = (0, 9, 15)
+    _check_sampled(eng, wl, k, v, q, out[0], seqs, [(s, h) for s in seqs for h in (0, 7, 8, 33, 63)])
+
+
+def test_full_step_fp8_config_sampled():
+    need_gpu()
+    wl = workloads.CONFIGS["full_step_fp8"]()
+    note(wl.description)
+    q, k, v = wl.tensors(5, device="cuda")
+    eng, log, out = run_gpu(wl, {5: k}, {5: v}, {5: q}, layers=(5,), engine_layers=wl.layers)
+    longest = int(np.argmax(wl.lengths))
+    seqs = sorted({0, 17, 100, 255, longest})
+    _check_sampled(eng, wl, k, v, q, out[5], seqs, [(s, h) for s in seqs for h in (0, 13, 31)], layer=5)

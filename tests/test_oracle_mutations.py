@@ -172,13 +172,13 @@ def test_fp8_ties_away_from_zero(monkeypatch):
 
 
 def test_fp8_scale_off_by_one(monkeypatch):
-    def quantize_row(x):
+    def quantize_rows(x):
         x = np.asarray(x, dtype=np.float32)
-        scale = np.float32(np.float32(np.abs(x).max()) / np.float32(447))
-        if scale == 0:
-            return np.zeros(x.shape, dtype=np.uint8), np.float32(0)
-        return fp8.encode((x / scale).astype(np.float32)), scale
-    monkeypatch.setattr(fp8, "quantize_row", quantize_row)
+        scale = (np.max(np.abs(x), axis=-1) / np.float32(447)).astype(np.float32)
+        safe = np.where(scale > 0, scale, np.float32(1)).astype(np.float32)
+        codes = np.where(scale[..., None] > 0, fp8.encode((x / safe[..., None]).astype(np.float32)), 0)
+        return codes.astype(np.uint8), scale
+    monkeypatch.setattr(fp8, "quantize_rows", quantize_rows)
     _fails(T_fp8.test_paged_fp8_attention_matches_brute_force, _fp8_case())
 
 
