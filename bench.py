@@ -11,7 +11,9 @@ bytes are counted from the lengths of each step.
 Default workload: 16 sequences of 32768 tokens, 64 query / 8 KV heads,
 d = 128, bf16, 16-token blocks in random physical order, 512-token split-K
 partitions (the long-context configuration).  `value` is KV bytes read by
-attention per second (decimal GB/s) over the timed steps.
+attention per second (decimal GB/s) over the timed steps.  The *_fp8
+configurations keep the same batch in an 8-bit E4M3 cache (bf16 tokens and
+queries; KV bytes count the codes and the per-token scales).
 
 Prints one JSON line.  Options: --gpus N (only 1 is supported), --steps K,
 --warmup W, --config NAME, --no-cpu-baseline, --cpu-seconds S.
@@ -83,7 +85,7 @@ class DecodeBench:
         self.wl = wl
         self.dev = torch.device(device)
         self.layers = wl.layers
-        self.eng = PagedDecodeEngine(wl.layers, wl.Hkv, wl.d, wl.num_blocks, wl.dtype, init_perm=wl.perm,
+        self.eng = PagedDecodeEngine(wl.layers, wl.Hkv, wl.d, wl.num_blocks, wl.cache_dtype, init_perm=wl.perm,
                                      device=device, partition=partition)
         # prefill every sequence to n - 1 tokens, layer by layer so the logical
         # tensors of one layer at a time are resident
@@ -109,7 +111,7 @@ class DecodeBench:
         # per-step inputs: new K/V per layer and the step's queries
         g = torch.Generator(device=self.dev)
         g.manual_seed(wl.seed * 7919 + 1)
-        dt = self.eng.tdtype
+        dt = self.eng.qdtype
         S = len(self.ids)
         self.knew = [torch.randn((steps_total, S, wl.Hkv, wl.d), generator=g, device=self.dev).to(dt)
                      for _ in range(wl.layers)]
@@ -143,7 +145,7 @@ class DecodeBench:
                 self.events.append((e0, e1))
             P.pkv_paged_decode_reduce(self.args[l])
         wl = self.wl
-        self.kv_bytes.append(2 * sum(self.lengths) * wl.Hkv * wl.d * self.eng.tdtype.itemsize * self.layers)
+        self.kv_bytes.append(sum(self.lengths) * wl.Hkv * wl.kv_bytes_per_token_head() * self.layers)
         self.step_idx += 1
 
 
@@ -163,15 +165,18 @@ def cpu_baseline(wl_name: str, seconds: float):
         return (t.view(torch.int32).numpy().view(np.uint32) if t.dtype == torch.float32
                 else t.view(torch.int16).numpy().view(np.uint16))
 
-    if wl_name == "long_context":
+    base = wl_name[:-len("_fp8")] if wl_name.endswith("_fp8") else wl_name
+    if base == "long_context":
         wl = workloads.long_context(S=2)
         sample = "2 of the 16 sequences (32768 tokens, all 8 KV / 64 query heads), one layer"
-    elif wl_name == "full_step":
+    elif base == "full_step":
         wl = workloads.full_step(S=16, layers=1)
         sample = "16 sequences of the same length distribution, 1 of 32 layers"
     else:
-        wl = workloads.CONFIGS[wl_name]()
+        wl = workloads.CONFIGS[base]()
         sample = "whole batch, one layer"
+    if base != wl_name:
+        wl = workloads.fp8_cache(wl)
     q, k, v = wl.tensors(0, device="cpu")
     rp = Replay(wl, layers=1).run(wl.setup_ops, {0: (bits(k), bits(v))})
     g = torch.Generator().manual_seed(5)
@@ -189,7 +194,7 @@ def cpu_baseline(wl_name: str, seconds: float):
         lengths = [n + 1 for n in lengths]
         OA.decode(rp.pool, 0, rp.tables(), lengths, q64, wl.Hq)
         t += time.perf_counter() - t0
-        kv += 2 * sum(lengths) * wl.Hkv * wl.d * wl.itemsize
+        kv += sum(lengths) * wl.Hkv * wl.kv_bytes_per_token_head()
         steps += 1
     try:
         from threadpoolctl import threadpool_info
@@ -278,7 +283,8 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": wl.name, "description": wl.description, "layers": wl.layers,
+        "config": {"workload": wl.name, "description": wl.description, "kv_cache": wl.cache_dtype,
+                   "layers": wl.layers,
                    "S": wl.S, "Hq": wl.Hq, "Hkv": wl.Hkv, "d": wl.d, "block": wl.block,
                    "partition": args.partition or 512, "start_lengths_mean": float(wl.lengths.mean())},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),

@@ -84,13 +84,16 @@ class Workload:
     def max_len(self) -> int:
         return int(self.lengths.max())
 
-    def kv_bytes_per_layer(self) -> int:
-        """Algorithmic K+V bytes one decode attention call reads (for the
-        8-bit cache: one byte per value plus a 4-byte scale per token and
-        head, for K and for V)."""
+    def kv_bytes_per_token_head(self) -> int:
+        """K+V bytes of one token of one KV head in one layer (for the 8-bit
+        cache: one byte per value plus a 4-byte scale, for K and for V)."""
         if self.cache_dtype == "fp8":
-            return 2 * self.total_tokens * self.Hkv * (self.d + 4)
-        return 2 * self.total_tokens * self.Hkv * self.d * self.itemsize
+            return 2 * (self.d + 4)
+        return 2 * self.d * self.itemsize
+
+    def kv_bytes_per_layer(self) -> int:
+        """Algorithmic K+V bytes one decode attention call reads."""
+        return self.total_tokens * self.Hkv * self.kv_bytes_per_token_head()
 
     def tensors(self, layer: int = 0, device="cpu"):
         """(q [S][Hq][d], k_log [sum n][Hkv][d], v_log [sum n][Hkv][d]).
