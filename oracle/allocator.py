@@ -28,6 +28,15 @@ compared bit for bit):
 * release walks the table in logical order and pushes each block whose
   count drops to zero;
 * every call is all-or-nothing: on pool exhaustion nothing changes.
+
+Sliding window («¿Cuánta memoria reservar para la caché KV?», "Adaptar…": a
+layer with windowed attention keeps a bounded history; «¿Cómo gestiona…?»:
+a window changes how much state a sequence keeps, paging how it is
+allocated): ``release_before(sid, pos)`` gives back every block whose
+positions all lie before ``pos``, walking the table in logical order as a
+release does; its table entry becomes ``HOLE`` (-1) so the table stays
+indexed by position.  ``pos`` may not exceed the length, so the block being
+filled is never released.
 """
 from __future__ import annotations
 
@@ -49,6 +58,9 @@ class BadSeq(AllocError):
 
 class Invalid(AllocError):
     pass
+
+
+HOLE = -1      # table entry of a block released by release_before
 
 
 class Allocator:
@@ -79,7 +91,8 @@ class Allocator:
             raise BadSeq(parent)
         n, table = self.seqs[parent]
         for b in table:
-            self.ref[b] += 1
+            if b != HOLE:
+                self.ref[b] += 1
         sid = self.next_id
         self.next_id += 1
         self.seqs[sid] = (n, list(table))
@@ -90,9 +103,32 @@ class Allocator:
             raise BadSeq(sid)
         _, table = self.seqs.pop(sid)
         for b in table:
+            if b == HOLE:
+                continue
             self.ref[b] -= 1
             if self.ref[b] == 0:
                 self.free.append(b)
+
+    def release_before(self, sid: int, pos: int) -> int:
+        """Release the blocks of ``sid`` that hold only positions < ``pos``
+        (block i with (i + 1)·B <= pos) and are not holes yet, in logical
+        order; returns how many were released."""
+        if sid not in self.seqs:
+            raise BadSeq(sid)
+        n, table = self.seqs[sid]
+        if pos < 0 or pos > n:
+            raise Invalid("release position outside [0, length]")
+        released = 0
+        for i in range(pos // self.B):
+            b = table[i]
+            if b == HOLE:
+                continue
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.append(b)
+            table[i] = HOLE
+            released += 1
+        return released
 
     # -- slot reservation ----------------------------------------------------
     def _append_one(self, sid: int, cow: List[Tuple[int, int]]) -> int:
@@ -177,7 +213,7 @@ class Allocator:
 
     def check_invariants(self) -> None:
         """Raise AssertionError if the state breaks a pool invariant."""
-        assert sum(self.ref) == sum(len(t) for _, t in self.seqs.values())
+        assert sum(self.ref) == sum(sum(1 for b in t if b != HOLE) for _, t in self.seqs.values())
         live = {b for b in range(self.N) if self.ref[b] > 0}
         assert len(set(self.free)) == len(self.free)
         assert live.isdisjoint(self.free)
@@ -189,7 +225,12 @@ class Allocator:
             assert len(t) == -(-n // self.B)
             assert 0 <= self.B * len(t) - n <= self.B - 1 or n == 0
             for b in t:
-                counts[b] += 1
+                if b != HOLE:
+                    counts[b] += 1
+            # holes only at the head, and never the block being filled
+            live_from = next((i for i, b in enumerate(t) if b != HOLE), len(t))
+            assert all(b != HOLE for b in t[live_from:])
+            assert n % self.B == 0 or live_from < len(t)
         assert counts == self.ref
 
     def clone(self) -> "Allocator":
@@ -208,6 +249,10 @@ def run_script(alloc: Allocator, ops, on_slots=None):
             alloc.fork(op[1])
         elif kind == "free":
             alloc.free_seq(op[1])
+        elif kind == "release":
+            alloc.release_before(op[1], op[2])
+        elif kind == "window":              # keep the last op[2] positions
+            alloc.release_before(op[1], max(0, alloc.length(op[1]) - op[2]))
         elif kind == "extend":
             slots, cow = alloc.extend(op[1], op[2])
             if on_slots:

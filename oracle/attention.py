@@ -9,6 +9,10 @@ grouped-query attention several query heads share one KV head (e.g. 40 query
 heads over 8 KV heads, five per group); the cache stores KV heads only.
 
 Readings (where the pages are silent):
+* sliding window («¿Cuánta memoria reservar para la caché KV?», "Adaptar…":
+  windowed layers keep a bounded history): with window W > 0 the query of
+  a sequence of length n attends to positions max(0, n - W) .. n - 1 only;
+  W = 0 is full attention;
 * score scale: 1/sqrt(d) by default, passed in explicitly;
 * query head h uses KV head floor(h / G), G = Hq / Hkv (contiguous groups,
   the repeat-interleave convention);
@@ -78,9 +82,10 @@ def attend_split(q, K, V, scale: float, part: int) -> np.ndarray:
 
 
 def decode(pool: Pool, layer: int, tables, lengths, q: np.ndarray, Hq: int,
-           scale: float = None, heads=None) -> np.ndarray:
+           scale: float = None, heads=None, window: int = 0) -> np.ndarray:
     """out[s][h] = attention of query head h of sequence s over the sequence's
-    gathered keys/values of KV head floor(h/G).
+    gathered keys/values of KV head floor(h/G) (the last ``window`` of them
+    when window > 0).
 
     ``q`` is float64 [S][Hq][d] (already upcast).  ``heads`` optionally limits
     the (s, h) pairs computed; others are left NaN.
@@ -101,6 +106,7 @@ def decode(pool: Pool, layer: int, tables, lengths, q: np.ndarray, Hq: int,
             hs = [h for h in range(g * G, (g + 1) * G) if heads is None or (s, h) in heads]
             if not hs:
                 continue
-            Kc, Vc = pool.gather(layer, tables[s], n, g)
+            start = max(0, n - window) if window > 0 else 0
+            Kc, Vc = pool.gather(layer, tables[s], n, g, start=start)
             out[s, hs] = attend(q[s, hs], Kc, Vc, scale)
     return out

@@ -117,12 +117,21 @@ class Pool:
                     self.KS[l][dst] = self.KS[l][src]
                     self.VS[l][dst] = self.VS[l][src]
 
-    def gather(self, layer: int, table, n: int, head: int):
-        """Contiguous fp64 (K [n][d], V [n][d]) of one sequence and KV head:
-        logical token t comes from block ``table[t // B]``, slot ``t % B``."""
+    def gather(self, layer: int, table, n: int, head: int, start: int = 0):
+        """Contiguous fp64 (K [n - start][d], V [n - start][d]) of tokens
+        start .. n-1 of one sequence and KV head: logical token t comes from
+        block ``table[t // B]``, slot ``t % B`` (blocks before start // B are
+        not read; a sliding window may have released them)."""
         self._materialize(layer)
+        first = start // self.B
+        if start:
+            K, V = self.gather(layer, list(table[first:]), n - first * self.B, head)
+            off = start - first * self.B
+            return K[off:], V[off:]
         nblk = -(-n // self.B)
         blocks = np.asarray(table[:nblk], dtype=np.int64)
+        if np.any(blocks < 0):
+            raise ValueError("gather reached a released block")
         kb = self.K[layer][blocks, head]                 # [nblk][d/x][B][x]
         kb = kb.transpose(0, 2, 1, 3).reshape(nblk * self.B, self.d)
         if self.dtype == "fp8":

@@ -22,19 +22,21 @@ def bits(t: torch.Tensor) -> np.ndarray:
     raise TypeError(t.dtype)
 
 
-def oracle_run(wl, q, k, v, layer=0, heads=None, scale=None):
-    """Replay the workload's setup + step on the oracle and decode one layer.
-    Returns (replay, out_f64 [S][Hq][d])."""
+def oracle_run(wl, q, k, v, layer=0, heads=None, scale=None, window=0, extra_ops=()):
+    """Replay the workload's setup + step (+ extra_ops) on the oracle and
+    decode one layer.  Returns (replay, out_f64 [S][Hq][d])."""
     rp = Replay(wl, layers=max(wl.layers, layer + 1))
-    rp.run(wl.setup_ops + wl.step_ops, values={layer: (bits(k), bits(v))})
+    rp.run(wl.setup_ops + wl.step_ops + list(extra_ops), values={layer: (bits(k), bits(v))})
     q64 = to_f64(bits(q), wl.dtype)
-    out = OA.decode(rp.pool, layer, rp.tables(), rp.lengths(), q64, wl.Hq, scale=scale, heads=heads)
+    out = OA.decode(rp.pool, layer, rp.tables(), rp.lengths(), q64, wl.Hq, scale=scale, heads=heads,
+                    window=window)
     return rp, out
 
 
-def brute_force(wl, q, k, v, scale=None):
+def brute_force(wl, q, k, v, scale=None, window=0):
     """Pure-Python loops over the logical (unpaged) tensors: the definition
-    softmax(q·K/sqrt(d))·V, query head h reading KV head h // (Hq/Hkv)."""
+    softmax(q·K/sqrt(d))·V, query head h reading KV head h // (Hq/Hkv), over
+    the last ``window`` tokens when window > 0."""
     G = wl.Hq // wl.Hkv
     d = wl.d
     scale = 1.0 / math.sqrt(d) if scale is None else scale
@@ -45,16 +47,17 @@ def brute_force(wl, q, k, v, scale=None):
     out = []
     for s in range(wl.S):
         n = int(wl.lengths[s])
+        t0 = max(0, n - window) if window > 0 else 0
         rows = []
         for h in range(wl.Hq):
             g = h // G
             sc = []
-            for t in range(n):
+            for t in range(t0, n):
                 kt = kk[offs[s] + t][g]
                 sc.append(sum(qq[s][h][j] * kt[j] for j in range(d)) * scale)
             m = max(sc)
             w = [math.exp(x - m) for x in sc]
             z = sum(w)
-            rows.append([sum(w[t] * vv[offs[s] + t][g][j] for t in range(n)) / z for j in range(d)])
+            rows.append([sum(w[t - t0] * vv[offs[s] + t][g][j] for t in range(t0, n)) / z for j in range(d)])
         out.append(rows)
     return np.array(out)

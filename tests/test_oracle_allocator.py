@@ -27,6 +27,8 @@ def run_golden_steps(alloc, steps):
         res = _apply(alloc, op)
         if "id" in st:
             assert res == st["id"]
+        if "released" in st:
+            assert res == st["released"], op
         if "slots" in st:
             slots, cow = res
             assert slots == st["slots"], op
@@ -46,11 +48,17 @@ def _apply(alloc, op):
         return alloc.extend(op[1], op[2])
     if k == "append":
         return alloc.append(op[1])
+    if k == "release":
+        return alloc.release_before(op[1], op[2])
     raise ValueError(k)
 
 
-def test_golden_fork_cow_free_oom():
-    sc = GOLD["scenarios"][0]
+SCRIPTED = {sc["name"]: sc for sc in GOLD["scenarios"] if "steps" in sc}
+
+
+@pytest.mark.parametrize("which", ["fork_cow_free_oom", "sliding_window_release"])
+def test_golden_scenarios(which):
+    sc = SCRIPTED[which]
     alloc = A.Allocator(sc["num_blocks"], sc["block"], sc["perm"])
     run_golden_steps(alloc, sc["steps"])
     free, ref, seqs, next_id = alloc.snapshot()
@@ -132,9 +140,9 @@ def test_oom_rolls_back_whole_batch():
     assert alloc.snapshot() == before
 
 
-@pytest.mark.parametrize("seed", range(4))
-def test_random_ops_invariants(seed):
-    ops = workloads.random_op_script(seed, 2500)
+@pytest.mark.parametrize("seed,windows", [(0, False), (1, False), (2, True), (3, True)])
+def test_random_ops_invariants(seed, windows):
+    ops = workloads.random_op_script(seed, 2500, windows=windows)
     alloc = A.Allocator(24, 4, np.random.default_rng(seed).permutation(24))
     fails = 0
     for op in ops:

@@ -13,6 +13,7 @@ import test_oracle_accounting as T_acc
 import test_oracle_allocator as T_alloc
 import test_oracle_attention as T_att
 import test_oracle_fp8 as T_fp8
+import test_oracle_window as T_win
 import workloads
 from oracle import accounting, allocator, attention, fp8, pool
 
@@ -46,7 +47,7 @@ def test_wrong_shift_sign(monkeypatch):
 def test_wrong_gqa_mapping(monkeypatch):
     orig = pool.Pool.gather
 
-    def decode(pl, layer, tables, lengths, q, Hq, scale=None, heads=None):
+    def decode(pl, layer, tables, lengths, q, Hq, scale=None, heads=None, window=0):
         S, d = len(lengths), pl.d
         scale = 1 / math.sqrt(d) if scale is None else scale
         out = np.zeros((S, Hq, d))
@@ -61,7 +62,7 @@ def test_wrong_gqa_mapping(monkeypatch):
 
 
 def test_transposed_value_gather(monkeypatch):
-    def gather(self, layer, table, n, head):
+    def gather(self, layer, table, n, head, start=0):
         nblk = -(-n // self.B)
         blocks = np.asarray(table[:nblk])
         kb = self.K[layer][blocks, head].transpose(0, 2, 1, 3).reshape(nblk * self.B, self.d)
@@ -112,7 +113,7 @@ def test_fifo_free_list(monkeypatch):
         orig(self, *a, **k)
         self.free = list(reversed(self.free))       # pops now give perm[-1] first
     monkeypatch.setattr(allocator.Allocator, "__init__", init)
-    _fails(T_alloc.test_golden_fork_cow_free_oom)
+    _fails(T_alloc.test_golden_scenarios, "fork_cow_free_oom")
 
 
 def test_no_copy_on_write(monkeypatch):
@@ -128,7 +129,7 @@ def test_no_copy_on_write(monkeypatch):
         self.seqs[sid] = (n + 1, table)
         return slot
     monkeypatch.setattr(allocator.Allocator, "_append_one", append_one)
-    _fails(T_alloc.test_golden_fork_cow_free_oom)
+    _fails(T_alloc.test_golden_scenarios, "fork_cow_free_oom")
     _fails(T_att.test_fork_isolation)
 
 
@@ -185,10 +186,10 @@ def test_fp8_scale_off_by_one(monkeypatch):
 def test_fp8_value_columns_swapped(monkeypatch):
     orig = pool.Pool.gather
 
-    def gather(self, layer, table, n, head):
-        K, V = orig(self, layer, table, n, head)
+    def gather(self, layer, table, n, head, start=0):
+        K, V = orig(self, layer, table, n, head, start)
         if self.dtype == "fp8":       # columns 4c + b read as 4b + c inside each group of 16
-            V = V.reshape(n, -1, 4, 4).transpose(0, 1, 3, 2).reshape(n, -1)
+            V = V.reshape(V.shape[0], -1, 4, 4).transpose(0, 1, 3, 2).reshape(V.shape[0], -1)
         return K, V
     monkeypatch.setattr(pool.Pool, "gather", gather)
     _fails(T_fp8.test_paged_fp8_attention_matches_brute_force, _fp8_case())
@@ -197,8 +198,8 @@ def test_fp8_value_columns_swapped(monkeypatch):
 def test_fp8_one_scale_per_block(monkeypatch):
     orig = pool.Pool.gather
 
-    def gather(self, layer, table, n, head):
-        K, V = orig(self, layer, table, n, head)
+    def gather(self, layer, table, n, head, start=0):
+        K, V = orig(self, layer, table, n, head, start)
         if self.dtype == "fp8":       # every token scaled as its block's first one
             ks = self.KS[layer][np.asarray(table[:-(-n // self.B)]), head].view(np.float32).astype(np.float64)
             first = np.repeat(ks[:, :1], self.B, axis=1).reshape(-1)[:n]
@@ -206,3 +207,32 @@ def test_fp8_one_scale_per_block(monkeypatch):
         return K, V
     monkeypatch.setattr(pool.Pool, "gather", gather)
     _fails(T_fp8.test_paged_fp8_attention_matches_brute_force, _fp8_case())
+
+
+# -- sliding window --------------------------------------------------------------
+
+def test_window_off_by_one(monkeypatch):
+    orig = attention.decode
+
+    def decode(*a, window=0, **k):
+        return orig(*a, window=window + 1 if window > 0 else 0, **k)
+    monkeypatch.setattr(attention, "decode", decode)
+    _fails(T_win.test_window_matches_brute_force, 5)
+
+
+def test_window_gather_from_block_start(monkeypatch):
+    orig = pool.Pool.gather
+
+    def gather(self, layer, table, n, head, start=0):       # starts at the window's block, not its token
+        return orig(self, layer, table, n, head, start=(start // self.B) * self.B)
+    monkeypatch.setattr(pool.Pool, "gather", gather)
+    _fails(T_win.test_window_matches_brute_force, 5)
+
+
+def test_window_release_keeps_one_block_too_many(monkeypatch):
+    orig = allocator.Allocator.release_before
+
+    def release_before(self, sid, pos):
+        return orig(self, sid, max(0, pos - self.B))
+    monkeypatch.setattr(allocator.Allocator, "release_before", release_before)
+    _fails(T_alloc.test_golden_scenarios, "sliding_window_release")

@@ -22,6 +22,9 @@ Script operations (ids are assigned 0, 1, 2, ... in create/fork order):
 * ``("free", sid)``                    release a sequence
 * ``("append", [(sid, src, pos), ...])``  one new token for each listed id,
   in list order (the batched decode append)
+* ``("release", sid, pos)``            sliding window: give back the blocks
+  holding only positions < pos
+* ``("window", sid, W)``               the same with pos = max(0, length - W)
 """
 from __future__ import annotations
 
@@ -272,9 +275,10 @@ CONFIGS = {
 }
 
 
-def random_op_script(seed: int, n_ops: int, max_live: int = 12, max_extend: int = 40):
+def random_op_script(seed: int, n_ops: int, max_live: int = 12, max_extend: int = 40, windows: bool = False):
     """A random allocator-only script (no tensor values) for allocator tests:
-    create / extend / fork / free / batched append, ids valid at issue time."""
+    create / extend / fork / free / batched append (and, with ``windows``,
+    sliding-window releases), ids valid at issue time."""
     rng = np.random.default_rng(seed)
     ops = []
     live: List[int] = []
@@ -297,6 +301,8 @@ def random_op_script(seed: int, n_ops: int, max_live: int = 12, max_extend: int 
             sid = int(rng.choice(live))
             ops.append(("free", sid))
             live.remove(sid)
+        elif windows and r < 0.74:
+            ops.append(("window", int(rng.choice(live)), int(rng.integers(0, 3 * max_extend))))
         else:
             k = int(rng.integers(1, len(live) + 1))
             ids = [int(x) for x in rng.choice(live, size=k, replace=False)]
