@@ -124,6 +124,16 @@ int pkv_seq_fork(pkv_pool* pool, int64_t parent, int64_t* child);
  * block's count and push blocks that reach 0 onto the free list.           */
 int pkv_seq_free(pkv_pool* pool, int64_t seq_id);
 
+/* Sliding window: give back every block of a sequence that holds only
+ * positions < pos (block i with (i + 1) * B <= pos), walking its table in
+ * logical order; a block's count drops by one and it returns to the free
+ * list at zero.  Released entries read -1 in tables (a table stays indexed
+ * by position); they are never read again by appends or by a decode whose
+ * window starts at or after pos.  0 <= pos <= length, else
+ * PKV_ERR_INVALID.  *n_released (may be NULL) gets the number of blocks
+ * released by this call.                                                   */
+int pkv_seq_release_before(pkv_pool* pool, int64_t seq_id, int32_t pos, int32_t* n_released);
+
 /* Reserve `ntok` >= 0 consecutive slots for one sequence (bulk prefill).
  * slots_out: host int32[ntok].  cow_pairs_out: host int32[2] receiving at
  * most one (src, dst) block pair; *n_cow gets the count (0 or 1).
@@ -209,7 +219,10 @@ int pkv_pool_snapshot(const pkv_pool* pool, int32_t* free_out, int32_t* ref_out,
  * G = Hq / Hkv and KV head g = h / G:
  *   out[s][h] = sum_t softmax_t(scale * q[s][h] . K_s[t]) V_s[t],
  *   K_s[t] = K[block_tables[s][t / B]][g][token t % B], same for V,
- * accumulated in fp32, rounded to the q/out dtype (nearest even).
+ * accumulated in fp32, rounded to the q/out dtype (nearest even).  With
+ * window W > 0 the sum runs over t = max(0, n - W) .. n - 1 only (sliding
+ * window, «¿Cuánta memoria reservar para la caché KV?», "Adaptar…"); blocks
+ * before the window are not read and may have been released.
  * Tokens are split into partitions of `partition` tokens (split-K); a
  * sequence with more than one partition writes fp32 partial results
  * (running max, running sum, unnormalised accumulator) to the workspace and
@@ -247,9 +260,12 @@ typedef struct pkv_decode_args {
   const float* v_scale;       /*   fp32 [num_blocks][Hkv][B]; else unused   */
   int32_t kv_dtype;           /* cache type: equal to dtype, or             */
                               /*   PKV_FP8_E4M3 with dtype PKV_BF16         */
+  int32_t window;             /* > 0: attend to the last `window` positions */
+                              /*   only; 0 = full attention                 */
 } pkv_decode_args;
 
-/* Workspace bytes the decode call needs (0 when one partition suffices). */
+/* Workspace bytes the decode call needs (0 when one partition suffices);
+ * enough for any window, which needs at most as much.                     */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_seq_len, int32_t partition);
 /* Partial kernel followed, when max_seq_len exceeds one partition, by the

@@ -30,7 +30,8 @@ Status BlockPool::fork(int64_t parent, int64_t* child) {
     return Status::BadSeq;
   }
   Sequence copy = it->second;
-  for (int32_t b : copy.table) ref_[b] += 1;
+  for (int32_t b : copy.table)
+    if (b != kHole) ref_[b] += 1;
   const int64_t sid = next_id_++;
   seqs_.emplace(sid, std::move(copy));
   *child = sid;
@@ -44,9 +45,32 @@ Status BlockPool::release(int64_t id) {
     return Status::BadSeq;
   }
   for (int32_t b : it->second.table) {
-    if (--ref_[b] == 0) free_.push_back(b);
+    if (b != kHole && --ref_[b] == 0) free_.push_back(b);
   }
   seqs_.erase(it);
+  return Status::Ok;
+}
+
+Status BlockPool::release_before(int64_t id, int32_t pos, int32_t* n_released) {
+  *n_released = 0;
+  auto it = seqs_.find(id);
+  if (it == seqs_.end()) {
+    err_ = "release_before: unknown sequence id " + std::to_string(id);
+    return Status::BadSeq;
+  }
+  Sequence& seq = it->second;
+  if (pos < 0 || pos > seq.len) {
+    err_ = "release_before: position " + std::to_string(pos) + " outside [0, " + std::to_string(seq.len) + "]";
+    return Status::Invalid;
+  }
+  // block i holds positions [i*B, (i+1)*B): wholly before pos iff i < pos / B
+  for (int32_t i = 0; i < pos / block_; ++i) {
+    int32_t& b = seq.table[i];
+    if (b == kHole) continue;
+    if (--ref_[b] == 0) free_.push_back(b);
+    b = kHole;
+    *n_released += 1;
+  }
   return Status::Ok;
 }
 

@@ -16,6 +16,13 @@
 // reused first); ids count up from 0; a batch is served in array order; a
 // release walks the table in logical order; every mutating call is
 // all-or-nothing, checked before anything changes.
+//
+// Sliding window («¿Cuánta memoria reservar para la caché KV?», "Adaptar…":
+// a windowed layer keeps a bounded history; «¿Cómo gestiona…?»: a window
+// changes how much state a sequence keeps, paging how it is allocated):
+// release_before gives back the blocks that hold only positions before the
+// window and marks their table entries kHole, so tables stay indexed by
+// position.
 #pragma once
 
 #include <cstdint>
@@ -26,6 +33,8 @@
 namespace pkv {
 
 enum class Status : int { Ok = 0, Invalid = -1, NoBlocks = -2, BadSeq = -3 };
+
+constexpr int32_t kHole = -1;   // table entry of a block given back by release_before
 
 struct Sequence {
   int32_t len = 0;
@@ -42,6 +51,9 @@ class BlockPool {
   Status create(int64_t* id);
   Status fork(int64_t parent, int64_t* child);
   Status release(int64_t id);
+  // Gives back the blocks holding only positions < pos (0 <= pos <= length),
+  // in logical order; their entries become kHole.
+  Status release_before(int64_t id, int32_t pos, int32_t* n_released);
   // k slots for one sequence; at most one copy-on-write pair.
   Status extend(int64_t id, int32_t k, int32_t* slots, int32_t* cow, int32_t* n_cow);
   // one slot per id, in order.

@@ -73,6 +73,20 @@ int guarded(F&& f) {
 
 int32_t effective_partition(int32_t partition) { return partition == 0 ? 512 : partition; }
 
+// Partitions a sequence of up to max_len tokens can touch: all of them, or
+// with a window of W tokens at most floor((W - 2) / part) + 2 (the window may
+// start just before a partition boundary).
+int64_t partitions_bound(int32_t max_len, int32_t part, int32_t window) {
+  int64_t pmax = (static_cast<int64_t>(max_len) + part - 1) / part;
+  if (window > 0) pmax = std::min<int64_t>(pmax, (static_cast<int64_t>(window) + part - 2) / part + 1);
+  return pmax;
+}
+
+size_t workspace_bytes(int64_t rows, int32_t head_dim) {
+  const size_t ml_bytes = (static_cast<size_t>(rows) * 2 * sizeof(float) + 255) & ~size_t(255);
+  return ml_bytes + static_cast<size_t>(rows) * head_dim * sizeof(float);
+}
+
 // Checks the decode arguments and fills the kernel parameter block.
 int prepare_decode(const pkv_decode_args* a, pkv::DecodeParams* p, int* kind_out) {
   if (!a) return fail(PKV_ERR_INVALID, "decode: null args");
@@ -90,6 +104,7 @@ int prepare_decode(const pkv_decode_args* a, pkv::DecodeParams* p, int* kind_out
   const int32_t part = effective_partition(a->partition);
   if (part < 32 || part > 1024 || part % 32 != 0)
     return fail(PKV_ERR_INVALID, "decode: partition must be a multiple of 32 in [32, 1024]");
+  if (a->window < 0) return fail(PKV_ERR_INVALID, "decode: window must be >= 0");
   if (!pkv::decode_shape_supported(kind, a->head_dim, a->block_size))
     return fail(PKV_ERR_UNSUPPORTED, "decode: supported shapes are block_size 16, head_dim 64 or 128");
   if (!a->q || !a->out || !a->k_cache || !a->v_cache || !a->block_tables || !a->seq_lens)
@@ -99,12 +114,12 @@ int prepare_decode(const pkv_decode_args* a, pkv::DecodeParams* p, int* kind_out
   if (kind == pkv::kDecodeFP8KV &&
       (!a->k_scale || !a->v_scale || !aligned16(a->k_scale) || !aligned16(a->v_scale)))
     return fail(PKV_ERR_INVALID, "decode: an 8-bit cache needs 16-byte aligned k_scale and v_scale");
-  const int64_t pmax = (static_cast<int64_t>(a->max_seq_len) + part - 1) / part;
+  const int64_t pmax = partitions_bound(a->max_seq_len, part, a->window);
   const int64_t gx = pmax * a->num_seqs * a->num_kv_heads;
   if (gx > 0x7fffffffLL || static_cast<int64_t>(a->num_seqs) * a->num_q_heads > 0x7fffffffLL)
     return fail(PKV_ERR_INVALID, "decode: grid too large");
-  const size_t need = pkv_decode_workspace_bytes(a->num_seqs, a->num_q_heads, a->head_dim,
-                                                 a->max_seq_len, a->partition);
+  const int64_t rows = pmax > 1 ? static_cast<int64_t>(a->num_seqs) * a->num_q_heads * pmax : 0;
+  const size_t need = rows > 0 ? workspace_bytes(rows, a->head_dim) : 0;
   if (need > 0 && (!a->workspace || a->workspace_bytes < need))
     return fail(PKV_ERR_INVALID, "decode: workspace missing or smaller than pkv_decode_workspace_bytes()");
   if (need > 0 && !aligned16(a->workspace))
@@ -125,6 +140,7 @@ int prepare_decode(const pkv_decode_args* a, pkv::DecodeParams* p, int* kind_out
   p->num_blocks = a->num_blocks;
   p->max_blocks = a->max_blocks;
   p->max_seq_len = a->max_seq_len;
+  p->window = a->window;
   p->partition = part;
   p->pmax = static_cast<int32_t>(pmax);
   p->ppw = 1;
@@ -136,7 +152,8 @@ int prepare_decode(const pkv_decode_args* a, pkv::DecodeParams* p, int* kind_out
     for (int32_t i = 0; i < a->num_seqs; ++i) {
       const int32_t n = a->host_seq_lens[i];
       if (n < 1 || n > a->max_seq_len) continue;
-      const int64_t P = (n + part - 1) / part;
+      const int32_t t0 = a->window > 0 ? std::max(0, n - a->window) : 0;
+      const int64_t P = (n - 1) / part - t0 / part + 1;
       sum += P;
       lo = std::min(lo, P);
       hi = std::max(hi, P);
@@ -147,8 +164,7 @@ int prepare_decode(const pkv_decode_args* a, pkv::DecodeParams* p, int* kind_out
   }
   p->scale_log2 = a->scale * 1.4426950408889634f;
   if (need > 0) {
-    const size_t rows = static_cast<size_t>(a->num_seqs) * a->num_q_heads * pmax;
-    const size_t ml_bytes = (rows * 2 * sizeof(float) + 255) & ~size_t(255);
+    const size_t ml_bytes = (static_cast<size_t>(rows) * 2 * sizeof(float) + 255) & ~size_t(255);
     p->part_ml = static_cast<float*>(a->workspace);
     p->part_acc = reinterpret_cast<float*>(static_cast<char*>(a->workspace) + ml_bytes);
   } else {
@@ -264,6 +280,12 @@ int pkv_seq_fork(pkv_pool* pool, int64_t parent, int64_t* child) {
 int pkv_seq_free(pkv_pool* pool, int64_t id) {
   if (!pool) return fail(PKV_ERR_INVALID, "seq_free: null pool");
   return guarded([&] { return from_alloc(pool->alloc.release(id), pool); });
+}
+
+int pkv_seq_release_before(pkv_pool* pool, int64_t id, int32_t pos, int32_t* n_released) {
+  if (!pool) return fail(PKV_ERR_INVALID, "seq_release_before: null pool");
+  int32_t dummy = 0;
+  return guarded([&] { return from_alloc(pool->alloc.release_before(id, pos, n_released ? n_released : &dummy), pool); });
 }
 
 int pkv_seq_extend(pkv_pool* pool, int64_t id, int32_t ntok, int32_t* slots, int32_t* cow,
@@ -508,11 +530,9 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
                                   int32_t max_seq_len, int32_t partition) {
   const int32_t part = effective_partition(partition);
   if (num_seqs < 1 || num_q_heads < 1 || head_dim < 1 || max_seq_len < 1 || part < 1) return 0;
-  const int64_t pmax = (static_cast<int64_t>(max_seq_len) + part - 1) / part;
+  const int64_t pmax = partitions_bound(max_seq_len, part, 0);
   if (pmax <= 1) return 0;
-  const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * pmax;
-  const size_t ml_bytes = (rows * 2 * sizeof(float) + 255) & ~size_t(255);
-  return ml_bytes + rows * head_dim * sizeof(float);
+  return workspace_bytes(static_cast<int64_t>(num_seqs) * num_q_heads * pmax, head_dim);
 }
 
 int pkv_paged_decode_partial(const pkv_decode_args* a, void* stream) {

@@ -211,14 +211,26 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksParams p) {
 // (sequence, KV head, query-head group): at most kMaxWaveBlocks blocks.
 constexpr int kMaxWaveBlocks = 256;
 
+// Partitions are aligned to absolute positions (partition k holds tokens
+// [k·P, (k+1)·P)); with a sliding window they are numbered from the first
+// one that overlaps the window, and only the window's tokens count.
 struct WaveTask {
   int s, kvh, h0, nh;           // sequence, KV head, first query head, heads here
-  int n, P;                     // length, partitions of this sequence
+  int n, P;                     // length, partitions of this sequence (in the window)
   int part0, part_end;          // partitions [part0, part_end) of this wave
-  int t_end;                    // one past the last token of the wave's run
+  int t_lo, t_end;              // the wave's tokens: [t_lo, t_end)
   int blk_first, nblk;          // first logical block and block count
+  int boundary0;                // wave-local block count that closes its first partition
   int id0, id1, id2, id3;       // lane l of idC holds block blk_first + 64C + l
 };
+
+// First partition overlapping the window of a sequence of length n, and the
+// number of partitions from there to the end.
+__device__ __forceinline__ void window_partitions(const DecodeParams& p, int n, int& t0, int& pf, int& P) {
+  t0 = p.window > 0 ? max(0, n - p.window) : 0;
+  pf = t0 / p.partition;
+  P = (n - 1) / p.partition - pf + 1;
+}
 
 template <typename T, int D>
 __device__ __forceinline__ void write_nan_rows(const DecodeParams& p, int s, int h0, int nh) {
@@ -256,14 +268,16 @@ __device__ __forceinline__ bool setup_task(const DecodeParams& p, WaveTask& w) {
     if (grp == 0) write_nan_rows<T, D>(p, w.s, w.h0, w.nh);
     return false;
   }
-  w.P = (w.n + p.partition - 1) / p.partition;
+  int t0, pf;
+  window_partitions(p, w.n, t0, pf, w.P);
   w.part0 = grp * p.ppw;
   if (w.part0 >= w.P) return false;
   w.part_end = min(w.P, w.part0 + p.ppw);
-  const int t_begin = w.part0 * p.partition;
-  w.t_end = min(w.n, w.part_end * p.partition);
-  w.blk_first = t_begin / kBlock;
-  w.nblk = (w.t_end - t_begin + kBlock - 1) / kBlock;
+  w.t_lo = max(t0, (pf + w.part0) * p.partition);
+  w.t_end = min(w.n, (pf + w.part_end) * p.partition);
+  w.blk_first = w.t_lo / kBlock;
+  w.nblk = (w.t_end - w.blk_first * kBlock + kBlock - 1) / kBlock;
+  w.boundary0 = (pf + w.part0 + 1) * (p.partition / kBlock) - w.blk_first;
   bool bad = w.blk_first + w.nblk > p.max_blocks;
   bool bad_lane = false;
   const int32_t* row = p.block_tables + static_cast<size_t>(w.s) * p.max_blocks + w.blk_first;
@@ -367,12 +381,12 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
   // stream ends: a global store in the middle of the stream would make every
   // later wait drain all loads in flight (stores and loads share vmcnt).
   extern __shared__ float staged[];
-  int s_, kvh, h0, nh, P, part0, part_end, t_end, blk_first, nblk, id0, id1, id2, id3;
+  int s_, kvh, h0, nh, P, part0, part_end, t_lo, t_end, blk_first, nblk, boundary0, id0, id1, id2, id3;
   {
     WaveTask w;
     if (!setup_task<__bf16, D>(p, w)) return;
     s_ = w.s; kvh = w.kvh; h0 = w.h0; nh = w.nh; P = w.P; part0 = w.part0; part_end = w.part_end;
-    t_end = w.t_end; blk_first = w.blk_first; nblk = w.nblk;
+    t_lo = w.t_lo; t_end = w.t_end; blk_first = w.blk_first; nblk = w.nblk; boundary0 = w.boundary0;
     id0 = w.id0; id1 = w.id1; id2 = w.id2; id3 = w.id3;
   }
   const int lane = threadIdx.x;
@@ -428,7 +442,7 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
   float m_run = -INFINITY;
   float l_run = 0.f;
   const int bpp = p.partition / kBlock;        // blocks per partition
-  int next_boundary = bpp;                     // block count that closes a partition
+  int next_boundary = boundary0;               // block count that closes a partition
   int staged_parts = 0;
   const int row_floats = D + 2;                // staged row: accumulator, m, l
 
@@ -455,7 +469,8 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
   };
 
   // kTail: the block may hold tokens past the sequence end (only the wave's
-  // last block can).
+  // last block can).  Only the wave's first block can start before t_lo (a
+  // sliding window's first token); that check is one scalar compare.
   auto compute_block = [&](const BlockRegs<D, kFp8>& r, int i, auto tail_tag) {
     constexpr bool kTail = decltype(tail_tag)::value;
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
@@ -475,7 +490,8 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
         sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.k[c]), qreg[c], sc, 0, 0, 0);
     }
     const int tok0 = (blk_first + i) * kBlock + 4 * g4;           // token of x[0]
-    const bool tail = kTail && (blk_first + i + 1) * kBlock > t_end;
+    const bool tail = (kTail && (blk_first + i + 1) * kBlock > t_end) || (blk_first + i) * kBlock < t_lo;
+    auto outside = [&](int tok) { return tok >= t_end || tok < t_lo; };
     float x[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -485,7 +501,7 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
     if (tail) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (tok0 + j >= t_end) x[j] = -INFINITY;
+        if (outside(tok0 + j)) x[j] = -INFINITY;
     }
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = max_over_rows(mx);
@@ -505,7 +521,7 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float e = exp2_fast(x[j] - m_run);
-        const float vsj = (tail && tok0 + j >= t_end) ? 0.f : r.vs[j];   // NaN-poisoned slots
+        const float vsj = (tail && outside(tok0 + j)) ? 0.f : r.vs[j];   // NaN-poisoned slots
         pb[j] = static_cast<__bf16>(e * vsj);
         ps += e;
       }
@@ -523,7 +539,7 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
       if (tail) {
         mk = 0u;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mk |= (tok0 + j < t_end ? 0xFFu : 0u) << (8 * j);
+        for (int j = 0; j < 4; ++j) mk |= (outside(tok0 + j) ? 0u : 0xFFu) << (8 * j);
       }
 #pragma unroll
       for (int a = 0; a < D / 64; ++a) {
@@ -536,7 +552,7 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
     } else {
       uint32_t mk0 = 0xFFFFFFFFu, mk1 = 0xFFFFFFFFu;
       if (tail) {
-        auto half = [&](int tok) -> uint32_t { return tok < t_end ? 0xFFFFu : 0u; };
+        auto half = [&](int tok) -> uint32_t { return outside(tok) ? 0u : 0xFFFFu; };
         mk0 = half(tok0) | (half(tok0 + 1) << 16);
         mk1 = half(tok0 + 2) | (half(tok0 + 3) << 16);
       }
@@ -661,12 +677,12 @@ template <int D>
 __global__ __launch_bounds__(64) void decode_partial_f32(DecodeParams p) {
   constexpr int KC = D / 16;
   constexpr int NT = D / 16;
-  int s_, kvh, h0, nh, P, part0, t_end, blk_first, nblk, id0, id1, id2, id3;
+  int s_, kvh, h0, nh, P, part0, t_lo, t_end, blk_first, nblk, id0, id1, id2, id3;
   {
     WaveTask w;
     if (!setup_task<float, D>(p, w)) return;
     s_ = w.s; kvh = w.kvh; h0 = w.h0; nh = w.nh; P = w.P; part0 = w.part0;
-    t_end = w.t_end; blk_first = w.blk_first; nblk = w.nblk;
+    t_lo = w.t_lo; t_end = w.t_end; blk_first = w.blk_first; nblk = w.nblk;
     id0 = w.id0; id1 = w.id1; id2 = w.id2; id3 = w.id3;
   }
   const int lane = threadIdx.x;
@@ -711,7 +727,7 @@ __global__ __launch_bounds__(64) void decode_partial_f32(DecodeParams p) {
     const int tok0 = (blk_first + i) * kBlock + 4 * g4;
     float x[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) x[j] = (tok0 + j < t_end) ? sc[j] * p.scale_log2 : -INFINITY;
+    for (int j = 0; j < 4; ++j) x[j] = (tok0 + j < t_end && tok0 + j >= t_lo) ? sc[j] * p.scale_log2 : -INFINITY;
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     mx = max_over_rows(mx);
     const float m_new = fmaxf(m_run, mx);
@@ -730,7 +746,7 @@ __global__ __launch_bounds__(64) void decode_partial_f32(DecodeParams p) {
       acc[t] *= alpha;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float v = (tok0 + j < t_end) ? vr[t][j] : 0.f;
+        const float v = (tok0 + j < t_end && tok0 + j >= t_lo) ? vr[t][j] : 0.f;
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(v, pr[j], acc[t], 0, 0, 0);
       }
     }
@@ -792,7 +808,8 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams p) {
   const int s = row / p.Hq;
   const int n = p.seq_lens[s];
   if (n < 1 || n > p.max_seq_len) return;
-  const int P = (n + p.partition - 1) / p.partition;
+  int t0, pf, P;
+  window_partitions(p, n, t0, pf, P);
   if (P <= 1) return;
   const float* ml = p.part_ml + static_cast<size_t>(row) * p.pmax * 2;
   const float* acc = p.part_acc + static_cast<size_t>(row) * p.pmax * D;

@@ -57,6 +57,7 @@ struct DecodeParams {
   float* part_acc;       // [S][Hq][Pmax][d]   unnormalised accumulators
   int32_t S, Hq, Hkv, G, d;
   int32_t num_blocks, max_blocks, max_seq_len;
+  int32_t window;        // > 0: attend to the last `window` positions only
   int32_t partition, pmax;
   int32_t ppw;           // partitions streamed per wave (set by the launcher)
   int64_t tasks_hint;    // exact (sequence, KV head, head group, partition) count, 0 = unknown

@@ -90,6 +90,10 @@ class PagedDecodeEngine:
                 self.fork(op[1])
             elif kind == "free":
                 self.free(op[1])
+            elif kind == "release":
+                P.pkv_seq_release_before(self.pool, op[1], op[2])
+            elif kind == "window":             # keep the last op[2] positions
+                P.pkv_seq_release_before(self.pool, op[1], max(0, self.length(op[1]) - op[2]))
             elif kind in ("extend", "append"):
                 if kind == "extend":
                     _, sid, k, src, pos = op
@@ -138,7 +142,7 @@ class PagedDecodeEngine:
         return self.tables, self.lens
 
     def decode_args(self, layer: int, q: torch.Tensor, out: torch.Tensor, max_seq_len: int,
-                    scale: Optional[float] = None):
+                    scale: Optional[float] = None, window: int = 0):
         need = P.pkv_decode_workspace_bytes(q.shape[0], q.shape[1], self.d, max_seq_len, self.partition)
         if need and (self.workspace is None or self.workspace.numel() < need):
             self.workspace = torch.empty((need,), dtype=torch.uint8, device=self.device)
@@ -146,13 +150,13 @@ class PagedDecodeEngine:
                              max_seq_len, scale, self.partition, self.workspace if need else None, self.B,
                              host_seq_lens=self.host_lens,
                              k_scale=None if self.ks is None else self.ks[layer],
-                             v_scale=None if self.vs is None else self.vs[layer])
+                             v_scale=None if self.vs is None else self.vs[layer], window=window)
 
     def decode(self, layer: int, q: torch.Tensor, max_seq_len: int, out: Optional[torch.Tensor] = None,
-               scale: Optional[float] = None, stream=None) -> torch.Tensor:
+               scale: Optional[float] = None, stream=None, window: int = 0) -> torch.Tensor:
         if out is None:
             out = torch.empty_like(q)
-        a = self.decode_args(layer, q, out, max_seq_len, scale)
+        a = self.decode_args(layer, q, out, max_seq_len, scale, window)
         P.pkv_paged_attention_decode(a, stream)
         return out
 

@@ -59,7 +59,7 @@ class pkv_decode_args(ctypes.Structure):
                 ("head_dim", _i32), ("block_size", _i32), ("num_blocks", _i32),
                 ("max_blocks", _i32), ("max_seq_len", _i32), ("partition", _i32),
                 ("dtype", _i32), ("scale", ctypes.c_float), ("host_seq_lens", _vp),
-                ("k_scale", _vp), ("v_scale", _vp), ("kv_dtype", _i32)]
+                ("k_scale", _vp), ("v_scale", _vp), ("kv_dtype", _i32), ("window", _i32)]
 
 
 _lib = None
@@ -74,6 +74,7 @@ SIGNATURES = [
     ("pkv_seq_create", ctypes.c_int, [_vp, _P(_i64)]),
     ("pkv_seq_fork", ctypes.c_int, [_vp, _i64, _P(_i64)]),
     ("pkv_seq_free", ctypes.c_int, [_vp, _i64]),
+    ("pkv_seq_release_before", ctypes.c_int, [_vp, _i64, _i32, _P(_i32)]),
     ("pkv_seq_extend", ctypes.c_int, [_vp, _i64, _i32, _P(_i32), _P(_i32), _P(_i32)]),
     ("pkv_append_slots", ctypes.c_int, [_vp, _P(_i64), _i32, _P(_i32), _P(_i32), _P(_i32)]),
     ("pkv_seq_length", ctypes.c_int, [_vp, _i64, _P(_i32)]),
@@ -221,6 +222,13 @@ def pkv_seq_free(pool: PoolHandle, seq_id: int) -> None:
     _check(lib().pkv_seq_free(pool.ptr, seq_id))
 
 
+def pkv_seq_release_before(pool: PoolHandle, seq_id: int, pos: int) -> int:
+    """Give back the blocks holding only positions < pos; returns how many."""
+    out = _i32()
+    _check(lib().pkv_seq_release_before(pool.ptr, seq_id, pos, ctypes.byref(out)))
+    return out.value
+
+
 def _pairs(cow: np.ndarray, n: int) -> List[Tuple[int, int]]:
     return [(int(cow[2 * i]), int(cow[2 * i + 1])) for i in range(n)]
 
@@ -329,7 +337,7 @@ def pkv_decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, m
 def decode_args(q, out, k_cache, v_cache, block_tables, seq_lens, num_kv_heads: int, num_blocks: int,
                 max_seq_len: int, scale: Optional[float] = None, partition: int = 0, workspace=None,
                 block_size: int = 16, host_seq_lens: Optional[np.ndarray] = None,
-                k_scale=None, v_scale=None) -> pkv_decode_args:
+                k_scale=None, v_scale=None, window: int = 0) -> pkv_decode_args:
     """Pack a pkv_decode_args from tensors (q/out [S][Hq][d]).  host_seq_lens:
     optional int32 numpy array [S] (kept alive by the returned object; it is
     read at every call, so it may be updated in place between calls).  The
@@ -350,6 +358,7 @@ def decode_args(q, out, k_cache, v_cache, block_tables, seq_lens, num_kv_heads: 
     a.partition = partition
     a.dtype = dtype
     a.kv_dtype = PKV_FP8_E4M3 if k_cache.dtype == torch.uint8 else dtype
+    a.window = window
     a.k_scale, a.v_scale = _ptr(k_scale), _ptr(v_scale)
     a.scale = 1.0 / math.sqrt(d) if scale is None else scale
     if host_seq_lens is not None:

@@ -46,10 +46,10 @@ def run_gpu(wl, k_log, v_log, q=None, layers=(0,), partition=0, scale=None, engi
     return eng, log, out
 
 
-def oracle_replay(wl, k_log, v_log, layers=(0,)):
+def oracle_replay(wl, k_log, v_log, layers=(0,), extra_ops=()):
     rp = Replay(wl, layers=max(layers) + 1)
     vals = {l: (bits(k_log[l].cpu()), bits(v_log[l].cpu())) for l in layers}
-    rp.run(wl.setup_ops + wl.step_ops, vals)
+    rp.run(wl.setup_ops + wl.step_ops + list(extra_ops), vals)
     return rp
 
 
@@ -92,7 +92,8 @@ def compare_out(gpu_out: torch.Tensor, ref: np.ndarray, rows=None):
     return max_abs, row_rel
 
 
-def oracle_out(rp, wl, q, layer=0, rows=None, scale=None):
+def oracle_out(rp, wl, q, layer=0, rows=None, scale=None, window=0):
     q64 = to_f64(bits(q.cpu()), wl.dtype)
     heads = None if rows is None else set(rows)
-    return OA.decode(rp.pool, layer, rp.tables(), rp.lengths(), q64, wl.Hq, scale=scale, heads=heads)
+    return OA.decode(rp.pool, layer, rp.tables(), rp.lengths(), q64, wl.Hq, scale=scale, heads=heads,
+                     window=window)

@@ -34,6 +34,11 @@ def apply_both(pool, alloc, op):
             res_o = alloc.extend(op[1], op[2])
         elif kind == "append":
             res_o = alloc.append([e[0] if isinstance(e, (tuple, list)) else e for e in op[1]])
+        elif kind == "release":
+            res_o = alloc.release_before(op[1], op[2])
+        elif kind == "window":
+            res_o = alloc.release_before(op[1], max(0, alloc.length(op[1]) - op[2])) if op[1] in alloc.seqs else \
+                alloc.release_before(op[1], 0)
     except A.AllocError as e:
         err_o = ERR[type(e)]
     err_l = res_l = None
@@ -50,6 +55,14 @@ def apply_both(pool, alloc, op):
         elif kind == "append":
             s, c = P.pkv_append_slots(pool, [e[0] if isinstance(e, (tuple, list)) else e for e in op[1]])
             res_l = (list(map(int, s)), c)
+        elif kind == "release":
+            res_l = P.pkv_seq_release_before(pool, op[1], op[2])
+        elif kind == "window":
+            try:
+                n = P.pkv_seq_length(pool, op[1])
+            except P.PkvError:
+                n = 0
+            res_l = P.pkv_seq_release_before(pool, op[1], max(0, n - op[2]))
     except P.PkvError as e:
         err_l = e.status
     assert err_o == err_l, (op, err_o, err_l)
@@ -61,9 +74,10 @@ def apply_both(pool, alloc, op):
     assert P.pkv_pool_snapshot(pool) == tuple(alloc.snapshot()), op
 
 
-def test_golden_scenario_matches():
+@pytest.mark.parametrize("name", ["fork_cow_free_oom", "sliding_window_release"])
+def test_golden_scenario_matches(name):
     with open(os.path.join(GOLDEN, "allocator_scripts.json")) as f:
-        sc = json.load(f)["scenarios"][0]
+        sc = {s["name"]: s for s in json.load(f)["scenarios"]}[name]
     pool = lib_pool(sc["num_blocks"], sc["block"], sc["perm"])
     alloc = A.Allocator(sc["num_blocks"], sc["block"], sc["perm"])
     for st in sc["steps"]:
@@ -76,9 +90,9 @@ def test_golden_scenario_matches():
     assert [[i, n, t] for i, n, t in seqs] == sc["final"]["seqs"] and next_id == sc["final"]["next_id"]
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(8))
 def test_random_scripts(seed):
-    ops = workloads.random_op_script(seed, 1500)
+    ops = workloads.random_op_script(seed, 1500, windows=seed >= 4)
     nb, B = (24, 4) if seed % 2 == 0 else (40, 16)
     perm = np.random.default_rng(seed).permutation(nb).astype(np.int32)
     pool = lib_pool(nb, B, perm)
@@ -91,7 +105,9 @@ def test_bad_ids_and_duplicates():
     pool = lib_pool(8, 4)
     alloc = A.Allocator(8, 4)
     for op in [("create",), ("free", 3), ("fork", -1), ("extend", 5, 2, 0, 0), ("append", [0, 0]),
-               ("append", [0, 9]), ("extend", 0, 0, 0, 0), ("append", []), ("free", 0), ("free", 0)]:
+               ("append", [0, 9]), ("extend", 0, 0, 0, 0), ("append", []), ("release", 0, 1),
+               ("release", 0, -1), ("release", 7, 0), ("extend", 0, 5, 0, 0), ("release", 0, 6),
+               ("release", 0, 5), ("free", 0), ("free", 0)]:
         apply_both(pool, alloc, op)
 
 
