@@ -110,3 +110,56 @@ def decode(pool: Pool, layer: int, tables, lengths, q: np.ndarray, Hq: int,
             Kc, Vc = pool.gather(layer, tables[s], n, g, start=start)
             out[s, hs] = attend(q[s, hs], Kc, Vc, scale)
     return out
+
+
+def prefill(pool: Pool, layer: int, tables, lengths, chunk_lens, q: np.ndarray, Hq: int,
+            scale: float = None, window: int = 0, rows=None) -> np.ndarray:
+    """Chunked (paged) prefill: the last ``chunk_lens[s]`` of the
+    ``lengths[s]`` tokens of sequence s are new, and each is a query.  Query
+    i of sequence s sits at position p = lengths[s] - chunk_lens[s] + i and
+    attends causally to positions 0 .. p (the last ``window`` of them when
+    window > 0), through the block table.  With one new token this is the
+    decode step.
+
+    «Servicio…presupuesto de memoria» §6: exact attention — scaled scores,
+    softmax, weighted values; «…» §2 and §4: prefill work has another shape
+    than decode steps (many queries at once).
+
+    ``q`` is float64 [T][Hq][d], T = sum(chunk_lens), the rows of sequence s
+    after those of sequences 0 .. s-1.  Returns float64 [T][Hq][d];
+    ``rows`` optionally limits the (row, head) pairs computed (others NaN).
+    """
+    d = pool.d
+    G = Hq // pool.Hkv
+    if Hq % pool.Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    T = int(sum(chunk_lens))
+    out = np.full((T, Hq, d), np.nan)
+    r0 = 0
+    for s, (n, m) in enumerate(zip(lengths, chunk_lens)):
+        n, m = int(n), int(m)
+        if m < 1 or m > n:
+            raise ValueError("a chunk holds 1 .. length tokens")
+        c = n - m
+        pos = c + np.arange(m)                                 # query positions
+        lo = pos - window + 1 if window > 0 else np.zeros(m, dtype=np.int64)
+        start = int(max(0, lo.min()))
+        keys = np.arange(start, n)
+        allowed = (keys[None, :] <= pos[:, None]) & (keys[None, :] >= lo[:, None])
+        for g in range(pool.Hkv):
+            hs = [h for h in range(g * G, (g + 1) * G)
+                  if rows is None or any((r0 + i, h) in rows for i in range(m))]
+            if not hs:
+                continue
+            Kc, Vc = pool.gather(layer, tables[s], n, g, start=start)
+            for h in hs:
+                X = (q[r0:r0 + m, h] @ Kc.T) * scale
+                X = np.where(allowed, X, -np.inf)
+                X = X - X.max(axis=1, keepdims=True)
+                P = np.exp(X)
+                out[r0:r0 + m, h] = (P @ Vc) / P.sum(axis=1, keepdims=True)
+        r0 += m
+    return out
+

@@ -14,6 +14,7 @@ import test_oracle_allocator as T_alloc
 import test_oracle_attention as T_att
 import test_oracle_fp8 as T_fp8
 import test_oracle_window as T_win
+import test_oracle_prefill as T_pre
 import workloads
 from oracle import accounting, allocator, attention, fp8, pool
 
@@ -236,3 +237,40 @@ def test_window_release_keeps_one_block_too_many(monkeypatch):
         return orig(self, sid, max(0, pos - self.B))
     monkeypatch.setattr(allocator.Allocator, "release_before", release_before)
     _fails(T_alloc.test_golden_scenarios, "sliding_window_release")
+
+
+# -- prefill -------------------------------------------------------------------
+
+def _mutated_prefill(allowed_fn):
+    """A prefill whose key mask is allowed_fn(keys, positions) (brute layout)."""
+    def prefill(pool_, layer, tables, lengths, chunk_lens, q, Hq, scale=None, window=0, rows=None):
+        d = pool_.d
+        G = Hq // pool_.Hkv
+        scale = 1 / math.sqrt(d) if scale is None else scale
+        out = np.zeros((int(sum(chunk_lens)), Hq, d))
+        r0 = 0
+        for s, (n, m) in enumerate(zip(lengths, chunk_lens)):
+            n, m = int(n), int(m)
+            ok = allowed_fn(np.arange(n)[None, :], (n - m + np.arange(m))[:, None], np.arange(m)[:, None])
+            for g in range(pool_.Hkv):
+                Kc, Vc = pool_.gather(layer, tables[s], n, g)
+                for h in range(g * G, (g + 1) * G):
+                    X = np.where(ok, q[r0:r0 + m, h] @ Kc.T * scale, -np.inf)
+                    P = np.exp(X - X.max(1, keepdims=True))
+                    P = np.nan_to_num(P)
+                    out[r0:r0 + m, h] = P @ Vc / np.maximum(P.sum(1, keepdims=True), 1e-300)
+            r0 += m
+        return out
+    return prefill
+
+
+def test_prefill_causal_off_by_one(monkeypatch):
+    # each query misses its own position
+    monkeypatch.setattr(attention, "prefill", _mutated_prefill(lambda t, p, i: t < p))
+    _fails(T_pre.test_prefill_matches_brute_force, 0)
+
+
+def test_prefill_mask_ignores_context(monkeypatch):
+    # positions counted from the chunk start instead of the sequence start
+    monkeypatch.setattr(attention, "prefill", _mutated_prefill(lambda t, p, i: t <= i))
+    _fails(T_pre.test_prefill_matches_brute_force, 0)

@@ -56,6 +56,7 @@ class Workload:
     partition: int = 512
     description: str = ""
     kv_dtype: str = ""         # cache element type if it differs: "fp8" (E4M3 codes)
+    chunk: Optional[np.ndarray] = None   # prefill: new tokens (queries) per sequence
 
     @property
     def S(self) -> int:
@@ -86,6 +87,39 @@ class Workload:
     @property
     def max_len(self) -> int:
         return int(self.lengths.max())
+
+    @property
+    def chunk_lens(self) -> np.ndarray:
+        """Queries per sequence: the prefill chunk, or 1 (the decode step)."""
+        return self.chunk if self.chunk is not None else np.ones(self.S, dtype=np.int64)
+
+    @property
+    def query_offsets(self) -> np.ndarray:
+        o = np.zeros(self.S + 1, dtype=np.int64)
+        o[1:] = np.cumsum(self.chunk_lens)
+        return o
+
+    def prefill_queries(self, layer: int = 0, device="cpu"):
+        """Queries of a prefill batch, [sum chunk][Hq][d], N(0,1) drawn in fp32
+        from their own generator and rounded to the workload dtype."""
+        import torch
+        dt = torch.float32 if self.dtype == "f32" else torch.bfloat16
+        g = torch.Generator(device=device)
+        g.manual_seed(self.seed * 1000003 + 7919 + layer)
+        return torch.randn((int(self.chunk_lens.sum()), self.Hq, self.d), generator=g, device=device,
+                           dtype=torch.float32).to(dt)
+
+    def prefill_flops(self, window: int = 0) -> int:
+        """Multiply-adds x 2 of QK and PV over the causal pairs (query,
+        key) of the chunk: 4 d Hq per pair."""
+        pairs = 0
+        for n, m in zip(self.lengths, self.chunk_lens):
+            n, m = int(n), int(m)
+            keys = np.arange(n - m, n) + 1                      # keys 0..p of query at p
+            if window > 0:
+                keys = np.minimum(keys, window)
+            pairs += int(keys.sum())
+        return 4 * self.d * self.Hq * pairs
 
     def kv_bytes_per_token_head(self) -> int:
         """K+V bytes of one token of one KV head in one layer (for the 8-bit
@@ -255,6 +289,39 @@ def with_lengths(lengths, Hq: int, Hkv: int, d: int, dtype: str, seed: int = 7,
                     description=f"S={len(lengths)}, n={list(map(int, lengths))[:8]}..., Hq={Hq}, Hkv={Hkv}, d={d}, {dtype}")
 
 
+def prefill_chunks(contexts, chunks, Hq: int, Hkv: int, d: int, dtype: str = "bf16", seed: int = 11,
+                   slack: float = 1.25, name: str = "prefill") -> Workload:
+    """Sequence s holds contexts[s] cached tokens and receives chunks[s] new
+    ones, whose K/V are appended (one extend each) before the chunk's
+    queries attend causally to everything up to themselves."""
+    rng = np.random.default_rng(seed)
+    contexts = np.asarray(contexts, dtype=np.int64)
+    chunks = np.asarray(chunks, dtype=np.int64)
+    lengths = contexts + chunks
+    nb = max(1, math.ceil(slack * _blocks_needed(lengths)))
+    setup = [("create",) for _ in lengths]
+    for s, c in enumerate(contexts):
+        if c > 0:
+            setup.append(("extend", s, int(c), s, 0))
+    step = [("extend", s, int(m), s, int(c)) for s, (c, m) in enumerate(zip(contexts, chunks))]
+    return Workload(name, 1, Hq, Hkv, d, dtype, lengths, nb, _pool_perm(rng, nb), setup, step,
+                    list(range(len(lengths))), seed, chunk=chunks,
+                    description=f"prefill S={len(lengths)}, context={list(map(int, contexts))[:6]}, "
+                                f"chunk={list(map(int, chunks))[:6]}, Hq={Hq}, Hkv={Hkv}, d={d}, {dtype}")
+
+
+def prefill_prompts(seed: int = 12) -> Workload:
+    """8 prompts of 4096 tokens each prefilled from an empty cache, 32 query /
+    8 KV heads, d = 128, bf16 (the prefill measured for throughput)."""
+    return prefill_chunks([0] * 8, [4096] * 8, 32, 8, 128, "bf16", seed, name="prefill_prompts")
+
+
+def prefill_chunked(seed: int = 13) -> Workload:
+    """8 sequences with 8192 cached tokens each taking a 1024-token chunk,
+    32 query / 8 KV heads, d = 128, bf16 (chunked prefill over a cache)."""
+    return prefill_chunks([8192] * 8, [1024] * 8, 32, 8, 128, "bf16", seed, name="prefill_chunked")
+
+
 def fp8_cache(wl: Workload) -> Workload:
     """The same workload with an 8-bit (E4M3) KV cache: the same bf16 input
     values, quantised per (token, head) row when they are written."""
@@ -272,6 +339,8 @@ CONFIGS = {
     "full_step": full_step,
     "long_context_fp8": lambda seed=3, **kw: fp8_cache(long_context(seed, **kw)),
     "full_step_fp8": lambda seed=4, **kw: fp8_cache(full_step(seed, **kw)),
+    "prefill_prompts": prefill_prompts,
+    "prefill_chunked": prefill_chunked,
 }
 
 
