@@ -276,6 +276,44 @@ int pkv_paged_decode_partial(const pkv_decode_args* args, void* stream);
 /* The reduce kernel alone (no-op when one partition suffices). */
 int pkv_paged_decode_reduce(const pkv_decode_args* args, void* stream);
 
+/* ---- paged prefill attention -------------------------------------------
+ * Chunked prefill («Servicio…presupuesto de memoria» §6: exact attention,
+ * blockwise with running statistics; §2/§4: prefill work has another shape
+ * than decode): sequence s holds n = seq_lens[s] tokens in the cache, the
+ * last m = query_start[s+1] - query_start[s] of which are new and already
+ * written (pkv_seq_extend + pkv_kv_append).  Query row query_start[s] + i
+ * sits at position p = n - m + i; for query head h (KV head g = h / G):
+ *   out[row][h] = sum_t softmax_t(scale * q[row][h] . K_s[t]) V_s[t],
+ * t over 0 .. p (the last `window` of those when window > 0), K_s / V_s
+ * gathered through block_tables as for decode.  fp32 accumulation, bf16
+ * output (nearest even).  Sequences with m > n, n > max_seq_len or a needed
+ * block id outside the pool get NaN rows; m = 0 is allowed (no rows).
+ * Supported: bf16 q/out/cache, block_size 16, head_dim 64 or 128.          */
+typedef struct pkv_prefill_args {
+  const void* q;              /* device [T][Hq][d] bf16, T = query_start[S] */
+  void* out;                  /* device [T][Hq][d] bf16                     */
+  const void* k_cache;        /* device, one layer, pool layout             */
+  const void* v_cache;
+  const int32_t* block_tables;/* device [S][max_blocks]                     */
+  const int32_t* seq_lens;    /* device [S]: tokens cached, chunk included  */
+  const int32_t* query_start; /* device [S + 1]: prefix sums of chunk sizes */
+  int32_t num_seqs;           /* S >= 1                                     */
+  int32_t num_q_heads;        /* Hq                                         */
+  int32_t num_kv_heads;       /* Hkv, divides Hq                            */
+  int32_t head_dim;           /* d                                          */
+  int32_t block_size;         /* B                                          */
+  int32_t num_blocks;         /* pool capacity (bounds check)               */
+  int32_t max_blocks;         /* row stride of block_tables                 */
+  int32_t max_seq_len;        /* upper bound of seq_lens                    */
+  int32_t max_query_len;      /* upper bound of the chunk sizes (grid)      */
+  int32_t dtype;              /* PKV_BF16                                   */
+  float scale;                /* score scale, e.g. 1/sqrt(d)                */
+  int32_t window;             /* > 0: sliding window; 0 = causal, full      */
+} pkv_prefill_args;
+
+/* One kernel on `stream`; no workspace.                                    */
+int pkv_paged_prefill(const pkv_prefill_args* args, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

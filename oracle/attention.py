@@ -149,17 +149,21 @@ def prefill(pool: Pool, layer: int, tables, lengths, chunk_lens, q: np.ndarray, 
         keys = np.arange(start, n)
         allowed = (keys[None, :] <= pos[:, None]) & (keys[None, :] >= lo[:, None])
         for g in range(pool.Hkv):
-            hs = [h for h in range(g * G, (g + 1) * G)
-                  if rows is None or any((r0 + i, h) in rows for i in range(m))]
-            if not hs:
+            todo = {}
+            for h in range(g * G, (g + 1) * G):
+                idx = np.arange(m) if rows is None else np.array(
+                    [i for i in range(m) if (r0 + i, h) in rows], dtype=np.int64)
+                if idx.size:
+                    todo[h] = idx
+            if not todo:
                 continue
             Kc, Vc = pool.gather(layer, tables[s], n, g, start=start)
-            for h in hs:
-                X = (q[r0:r0 + m, h] @ Kc.T) * scale
-                X = np.where(allowed, X, -np.inf)
+            for h, idx in todo.items():
+                X = (q[r0 + idx, h] @ Kc.T) * scale
+                X = np.where(allowed[idx], X, -np.inf)
                 X = X - X.max(axis=1, keepdims=True)
                 P = np.exp(X)
-                out[r0:r0 + m, h] = (P @ Vc) / P.sum(axis=1, keepdims=True)
+                out[r0 + idx, h] = (P @ Vc) / P.sum(axis=1, keepdims=True)
         r0 += m
     return out
 

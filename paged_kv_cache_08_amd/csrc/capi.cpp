@@ -562,4 +562,46 @@ int pkv_paged_attention_decode(const pkv_decode_args* a, void* stream) {
   return from_hip(pkv::launch_decode_reduce(p, kind, st), "decode_reduce");
 }
 
+int pkv_paged_prefill(const pkv_prefill_args* a, void* stream) {
+  if (!a) return fail(PKV_ERR_INVALID, "prefill: null args");
+  if (a->dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "prefill: bf16 only");
+  if (a->num_seqs < 1 || a->num_kv_heads < 1 || a->num_q_heads < 1 || a->head_dim < 1 || a->block_size < 1 ||
+      a->num_blocks < 1 || a->max_blocks < 1 || a->max_seq_len < 1 || a->max_query_len < 0)
+    return fail(PKV_ERR_INVALID, "prefill: sizes must be positive");
+  if (a->num_q_heads % a->num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "prefill: num_q_heads must be a multiple of num_kv_heads");
+  if (a->window < 0) return fail(PKV_ERR_INVALID, "prefill: window must be >= 0");
+  if (!pkv::prefill_shape_supported(a->head_dim, a->block_size))
+    return fail(PKV_ERR_UNSUPPORTED, "prefill: supported shapes are block_size 16, head_dim 64 or 128");
+  if (!a->q || !a->out || !a->k_cache || !a->v_cache || !a->block_tables || !a->seq_lens || !a->query_start)
+    return fail(PKV_ERR_INVALID, "prefill: null device pointer");
+  if (!aligned16(a->q) || !aligned16(a->out) || !aligned16(a->k_cache) || !aligned16(a->v_cache))
+    return fail(PKV_ERR_INVALID, "prefill: q, out and caches must be 16-byte aligned");
+  const int64_t G = a->num_q_heads / a->num_kv_heads;
+  const int64_t tiles = (static_cast<int64_t>(a->max_query_len) * G + 255) / 256;
+  if (tiles > 0x7fffffffLL || a->num_seqs > 65535 || a->num_kv_heads > 65535)
+    return fail(PKV_ERR_INVALID, "prefill: grid too large");
+  if (a->max_query_len == 0) return PKV_OK;
+  pkv::PrefillParams p{};
+  p.q = a->q;
+  p.out = a->out;
+  p.k_cache = a->k_cache;
+  p.v_cache = a->v_cache;
+  p.block_tables = a->block_tables;
+  p.seq_lens = a->seq_lens;
+  p.query_start = a->query_start;
+  p.S = a->num_seqs;
+  p.Hq = a->num_q_heads;
+  p.Hkv = a->num_kv_heads;
+  p.G = static_cast<int32_t>(G);
+  p.d = a->head_dim;
+  p.num_blocks = a->num_blocks;
+  p.max_blocks = a->max_blocks;
+  p.max_seq_len = a->max_seq_len;
+  p.max_query_len = a->max_query_len;
+  p.window = a->window;
+  p.scale_log2 = a->scale * 1.4426950408889634f;
+  return from_hip(pkv::launch_prefill(p, static_cast<hipStream_t>(stream)), "prefill");
+}
+
 }  // extern "C"

@@ -34,15 +34,11 @@
 #include <cstdlib>
 #include <type_traits>
 
+#include "device_util.hpp"
 #include "kernels.hpp"
 
 namespace pkv {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBlock = 16;   // tokens per block on the decode path
 #ifndef PKV_DEPTH
@@ -54,39 +50,11 @@ constexpr int kDepth = PKV_DEPTH;  // blocks in flight per wave on the bf16 deco
 #endif
 constexpr int kDepthFp8 = PKV_DEPTH_FP8;  // the same on the 8-bit cache path
 
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
 // K/V tiles are read exactly once per decode call: stream them with the
 // non-temporal hint so they do not displace reusable lines.  On MI355X this
 // lifts a 4 KiB-tile gather from about 6.1 to about 6.85 TB/s.
 template <typename T>
 __device__ __forceinline__ T stream_load(const T* p) { return __builtin_nontemporal_load(p); }
-
-// Reductions over the four lanes l, l^16, l^32, l^48 (one MFMA column), with
-// the gfx950 row-swap permutes (no LDS round trip): permlane32_swap exchanges
-// the two 32-lane halves, permlane16_swap exchanges rows 0<->1 and 2<->3.
-__device__ __forceinline__ float max_over_rows(float x) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float sum_over_rows(float x) {
-  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m);
-  return x;
-}
 
 // ---------------------------------------------------------------------------
 // kv_append
@@ -341,7 +309,6 @@ __device__ __forceinline__ int block_id(int id0, int id1, int id2, int id3, int 
 // value is rescaled.  Tile t = 4a+b holds value column 64a+4c+b in row c;
 // lane l accumulates columns 64a+16g+4j+b (j = 0..3).
 // ---------------------------------------------------------------------------
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 template <int D, bool kFp8>
 struct BlockRegs;

@@ -65,7 +65,23 @@ struct DecodeParams {
   float scale_log2;      // scale * log2(e): scores are kept in base-2 units
 };
 
+struct PrefillParams {
+  const void* q;                 // [T][Hq][d] bf16, sequence s's rows from query_start[s]
+  void* out;                     // [T][Hq][d] bf16
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;   // [S][max_blocks]
+  const int32_t* seq_lens;       // [S] tokens in the cache, the chunk included
+  const int32_t* query_start;    // [S + 1] prefix sums of the chunk lengths
+  int32_t S, Hq, Hkv, G, d;
+  int32_t num_blocks, max_blocks, max_seq_len, max_query_len;
+  int32_t window;                // > 0: a query attends to its last `window` positions
+  float scale_log2;
+};
+
 hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+bool prefill_shape_supported(int head_dim, int block_size);
 // Copies n_tab table entries and n_len lengths from a device-visible pinned
 // host buffer (tables first, lengths right after) into device arrays.
 hipError_t launch_table_upload(const int32_t* host_src, int32_t* dev_tables, int64_t n_tab, int32_t* dev_lens,

@@ -160,6 +160,22 @@ class PagedDecodeEngine:
         P.pkv_paged_attention_decode(a, stream)
         return out
 
+    def prefill(self, layer: int, q: torch.Tensor, chunk_lens: Sequence[int], max_seq_len: int,
+                out: Optional[torch.Tensor] = None, scale: Optional[float] = None, window: int = 0,
+                stream=None) -> torch.Tensor:
+        """Chunked prefill of the synced batch: q [sum chunk_lens][Hq][d], the
+        rows of batch entry i being its last chunk_lens[i] tokens (already
+        written).  Returns out, shaped like q."""
+        if out is None:
+            out = torch.empty_like(q)
+        qs = np.zeros(len(chunk_lens) + 1, dtype=np.int32)
+        qs[1:] = np.cumsum(chunk_lens)
+        self.query_start = torch.from_numpy(qs).to(self.device)
+        a = P.prefill_args(q, out, self.k[layer], self.v[layer], self.tables, self.lens, self.query_start,
+                           self.Hkv, self.N, max_seq_len, int(max(chunk_lens)), scale, window, self.B)
+        P.pkv_paged_prefill(a, stream)
+        return out
+
     def snapshot(self):
         return P.pkv_pool_snapshot(self.pool)
 

@@ -62,6 +62,15 @@ class pkv_decode_args(ctypes.Structure):
                 ("k_scale", _vp), ("v_scale", _vp), ("kv_dtype", _i32), ("window", _i32)]
 
 
+class pkv_prefill_args(ctypes.Structure):
+    _fields_ = [("q", _vp), ("out", _vp), ("k_cache", _vp), ("v_cache", _vp),
+                ("block_tables", _vp), ("seq_lens", _vp), ("query_start", _vp),
+                ("num_seqs", _i32), ("num_q_heads", _i32), ("num_kv_heads", _i32),
+                ("head_dim", _i32), ("block_size", _i32), ("num_blocks", _i32),
+                ("max_blocks", _i32), ("max_seq_len", _i32), ("max_query_len", _i32),
+                ("dtype", _i32), ("scale", ctypes.c_float), ("window", _i32)]
+
+
 _lib = None
 
 # (name, restype, argtypes) of every exported entry point
@@ -90,6 +99,7 @@ SIGNATURES = [
     ("pkv_paged_attention_decode", ctypes.c_int, [_P(pkv_decode_args), _vp]),
     ("pkv_paged_decode_partial", ctypes.c_int, [_P(pkv_decode_args), _vp]),
     ("pkv_paged_decode_reduce", ctypes.c_int, [_P(pkv_decode_args), _vp]),
+    ("pkv_paged_prefill", ctypes.c_int, [_P(pkv_prefill_args), _vp]),
 ]
 
 
@@ -378,3 +388,28 @@ def pkv_paged_decode_partial(args: pkv_decode_args, stream=None) -> None:
 
 def pkv_paged_decode_reduce(args: pkv_decode_args, stream=None) -> None:
     _check(lib().pkv_paged_decode_reduce(ctypes.byref(args), _stream(stream)))
+
+
+def prefill_args(q, out, k_cache, v_cache, block_tables, seq_lens, query_start, num_kv_heads: int,
+                 num_blocks: int, max_seq_len: int, max_query_len: int, scale: Optional[float] = None,
+                 window: int = 0, block_size: int = 16) -> pkv_prefill_args:
+    """Pack a pkv_prefill_args from tensors: q/out [T][Hq][d] bf16,
+    query_start int32 [S + 1] (device), seq_lens int32 [S] (device)."""
+    T, Hq, d = q.shape
+    a = pkv_prefill_args()
+    a.q, a.out, a.k_cache, a.v_cache = _ptr(q), _ptr(out), _ptr(k_cache), _ptr(v_cache)
+    a.block_tables, a.seq_lens, a.query_start = _ptr(block_tables), _ptr(seq_lens), _ptr(query_start)
+    a.num_seqs = seq_lens.shape[0]
+    a.num_q_heads, a.num_kv_heads, a.head_dim = Hq, num_kv_heads, d
+    a.block_size, a.num_blocks = block_size, num_blocks
+    a.max_blocks = block_tables.shape[1]
+    a.max_seq_len, a.max_query_len = max_seq_len, max_query_len
+    a.dtype = PKV_BF16
+    a.scale = 1.0 / math.sqrt(d) if scale is None else scale
+    a.window = window
+    return a
+
+
+def pkv_paged_prefill(args: pkv_prefill_args, stream=None) -> None:
+    _check(lib().pkv_paged_prefill(ctypes.byref(args), _stream(stream)))
+
