@@ -160,6 +160,148 @@ class DecodeBench:
         self.step_idx += 1
 
 
+class PrefillBench:
+    """Chunked prefill: the setup writes every sequence's context and chunk
+    through the library; a step writes the chunk's K/V again (kv_append, the
+    same slots) and runs the prefill attention over it, per layer."""
+
+    def __init__(self, wl, device="cuda", window: int = 0):
+        import numpy as np
+        import torch
+        from paged_kv_cache_08_amd import pkv as P
+        from paged_kv_cache_08_amd.engine import PagedDecodeEngine
+
+        self.P, self.torch, self.wl, self.window = P, torch, wl, window
+        self.dev = torch.device(device)
+        self.eng = PagedDecodeEngine(wl.layers, wl.Hkv, wl.d, wl.num_blocks, wl.cache_dtype, init_perm=wl.perm,
+                                     device=device)
+        log = self.eng.run_script(wl.setup_ops + wl.step_ops, None)          # allocator only
+        offs = wl.offsets
+        self.k, self.v, self.q, self.chunk_slots = [], [], [], None
+        chunk_rows, chunk_slots = [], []
+        for layer in range(wl.layers):
+            _, k, v = wl.tensors(layer, device=device)
+            for (kind, sid, slots, cow), op in zip(log, [o for o in wl.setup_ops + wl.step_ops if o[0] == "extend"]):
+                _, _, cnt, src, pos = op
+                rows = torch.arange(offs[src] + pos, offs[src] + pos + cnt, device=self.dev)
+                dslots = torch.from_numpy(np.ascontiguousarray(slots)).to(self.dev)
+                P.pkv_kv_append(self.eng.pool, layer, k.index_select(0, rows), v.index_select(0, rows), dslots)
+                if layer == 0 and op in wl.step_ops:
+                    chunk_rows.append(rows)
+                    chunk_slots.append(dslots)
+            rows = torch.cat(chunk_rows)
+            self.k.append(k.index_select(0, rows).contiguous())             # the chunk's new K/V
+            self.v.append(v.index_select(0, rows).contiguous())
+            self.q.append(wl.prefill_queries(layer, device=device))
+            del k, v
+        self.chunk_slots = torch.cat(chunk_slots).contiguous()
+        self.eng.sync(wl.seq_ids)
+        self.out = [torch.empty_like(self.q[l]) for l in range(wl.layers)]
+        self.chunks = list(map(int, wl.chunk_lens))
+        qs = np.zeros(len(self.chunks) + 1, dtype=np.int32)
+        qs[1:] = np.cumsum(self.chunks)
+        self.query_start = torch.from_numpy(qs).to(self.dev)
+        self.args = [P.prefill_args(self.q[l], self.out[l], self.eng.k[l], self.eng.v[l], self.eng.tables,
+                                    self.eng.lens, self.query_start, wl.Hkv, wl.num_blocks, wl.max_len,
+                                    max(self.chunks), window=window) for l in range(wl.layers)]
+        torch.cuda.synchronize()
+        self.events = []
+
+    def step(self, record_events: bool):
+        P, torch = self.P, self.torch
+        for l in range(self.wl.layers):
+            P.pkv_kv_append(self.eng.pool, l, self.k[l], self.v[l], self.chunk_slots)
+            if record_events:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+            P.pkv_paged_prefill(self.args[l])
+            if record_events:
+                e1.record()
+                self.events.append((e0, e1))
+
+
+def prefill_cpu_baseline(wl, seconds: float, window: int = 0):
+    """The oracle's prefill on a bounded sample: the first sequence of the
+    batch, one query head per KV head... repeated over its KV heads until the
+    time is spent; rate in TFLOP/s of the same causal pairs."""
+    import numpy as np
+    import workloads
+    from oracle import attention as OA
+    from oracle.pool import to_f64
+    from oracle.replay import Replay
+    import torch
+
+    def bits(t):
+        return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    one = workloads.prefill_chunks(wl.lengths[:1] - wl.chunk_lens[:1], wl.chunk_lens[:1], wl.Hq, wl.Hkv, wl.d,
+                                   wl.dtype, wl.seed)
+    q = one.prefill_queries()
+    _, k, v = one.tensors()
+    rp = Replay(one).run(one.setup_ops + one.step_ops, {0: (bits(k), bits(v))})
+    q64 = to_f64(bits(q), one.dtype)
+    G = one.Hq // one.Hkv
+    m = int(one.chunk_lens[0])
+    heads, t = 0, 0.0
+    while t < seconds or heads == 0:
+        h = (heads * G) % one.Hq                          # one query head of each KV head in turn
+        rows = {(i, h) for i in range(m)}
+        t0 = time.perf_counter()
+        OA.prefill(rp.pool, 0, rp.tables(), rp.lengths(), one.chunk_lens, q64, one.Hq, window=window, rows=rows)
+        t += time.perf_counter() - t0
+        heads += 1
+    flops = one.prefill_flops(window) / one.Hq * heads
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"sequence 0 of the batch ({m} new tokens over {int(one.lengths[0])}), "
+                      f"{heads} query heads one at a time, {t:.1f} s"}
+
+
+def run_prefill(args, wl):
+    import torch
+    log(f"setup {wl.description}")
+    bench = PrefillBench(wl, window=args.window)
+    for _ in range(args.warmup):
+        bench.step(record_events=False)
+    torch.cuda.synchronize()
+    log("timed steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        bench.step(record_events=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    flops_step = wl.prefill_flops(args.window) * wl.layers
+    k_ms = [a.elapsed_time(b) for a, b in bench.events]
+    k_avg = sum(k_ms) / len(k_ms) / 1e3
+    achieved = wl.prefill_flops(args.window) / k_avg / 1e12
+    value = flops_step * args.steps / elapsed / 1e12
+    peak = 2500.0
+    result = {
+        "metric": "paged prefill attention: TFLOP/s (causal QK and PV) and prefill tokens/s",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "description": wl.description, "layers": wl.layers, "S": wl.S,
+                   "Hq": wl.Hq, "Hkv": wl.Hkv, "d": wl.d, "block": wl.block, "window": args.window,
+                   "chunk_mean": float(wl.chunk_lens.mean()), "length_mean": float(wl.lengths.mean())},
+        "prefill_tokens_per_s": round(float(wl.chunk_lens.sum()) * args.steps / elapsed, 1),
+        "roofline": {"bound": "mfma", "kernel": "prefill_bf16", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "avg_launch_us": round(k_avg * 1e6, 2),
+                     "algorithmic_flops_per_launch": wl.prefill_flops(args.window)},
+    }
+    log(f"timed {args.steps} steps: {value:.1f} TFLOP/s; prefill kernel {k_avg * 1e6:.1f} us")
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = prefill_cpu_baseline(wl, args.cpu_seconds, args.window)
+    print(json.dumps(result), flush=True)
+
+
 def cpu_baseline(wl_name: str, seconds: float, window: int = 0):
     """The oracle (unchanged) on a bounded sample of the same workload:
     a few of its sequences, one decode step at a time (allocator append,
@@ -261,6 +403,9 @@ def main():
         __graft_entry__.build()
 
     wl = workloads.CONFIGS[args.config]()
+    if wl.chunk is not None:
+        run_prefill(args, wl)
+        return
     total = args.warmup + args.steps
     log(f"setup {wl.description}")
     bench = DecodeBench(wl, total, partition=args.partition, window=args.window)
