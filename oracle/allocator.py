@@ -37,6 +37,33 @@ positions all lie before ``pos``, walking the table in logical order as a
 release does; its table entry becomes ``HOLE`` (-1) so the table stays
 indexed by position.  ``pos`` may not exceed the length, so the block being
 filled is never released.
+
+Prefix cache («Servicio…presupuesto de memoria» §8: reusing the KV state of
+identical prefixes saves repeated work; the cache key must identify every
+input that shapes the state, model version and configuration included;
+reused pages must not expose or let anyone change another request's private
+continuation; cancelling and evicting drop references without freeing pages
+in use.  «PagedAttention e vLLM»: a long shared system prompt is processed
+once, not again for every request).  Readings taken:
+
+* only full blocks are cached (a partial block is still being written);
+* an entry is keyed exactly by (namespace, parent entry, the block's B token
+  ids) — the namespace stands for the model version and configuration, the
+  parent for everything before the block — and holds one reference to its
+  block;
+* ``prefix_register(sid, tokens, ns)`` walks the sequence's full blocks from
+  position 0: a known key is touched (and, if it names another block with
+  the same content, kept), an unknown key becomes a new entry for the
+  sequence's block; it stops at a released block (a hole);
+* ``prefix_match(tokens, ns)`` creates a sequence made of the longest chain
+  of cached blocks that matches the tokens' leading full blocks (one more
+  reference per block, as a fork) and touches the chain; the new sequence's
+  next token starts a fresh block, so cached blocks are never written;
+* ``prefix_evict(k)`` repeatedly drops the least recently used entry among
+  those with no child entry whose block only the cache holds (count 1),
+  deeper entries first on equal use, until k blocks are free again or none
+  qualifies; ``prefix_clear()`` drops every entry;
+* use is a logical clock that advances once per register or match call.
 """
 from __future__ import annotations
 
@@ -78,6 +105,12 @@ class Allocator:
         self.ref: List[int] = [0] * num_blocks
         self.seqs: Dict[int, Tuple[int, List[int]]] = {}
         self.next_id = 0
+        # prefix cache: key (ns, parent entry, tokens) -> entry index;
+        # entry index -> [key, block, last_use, depth, children]
+        self.pc_index: Dict[tuple, int] = {}
+        self.pc: Dict[int, list] = {}
+        self.pc_next = 0
+        self.pc_clock = 0
 
     # -- sequences ---------------------------------------------------------
     def create(self) -> int:
@@ -163,6 +196,96 @@ class Allocator:
             self.free, self.ref, self.seqs, self.next_id = saved
             raise
 
+    # -- prefix cache --------------------------------------------------------
+    def prefix_register(self, sid: int, tokens: Sequence[int], ns: int) -> int:
+        """Enter the full blocks of ``sid`` (token ids ``tokens`` for its
+        positions 0..) into the cache; returns the number of new entries."""
+        if sid not in self.seqs:
+            raise BadSeq(sid)
+        n, table = self.seqs[sid]
+        tokens = [int(t) for t in tokens]
+        if len(tokens) < n:
+            raise Invalid("fewer token ids than the sequence holds")
+        self.pc_clock += 1
+        parent, added = -1, 0
+        for i in range(n // self.B):
+            b = table[i]
+            if b == HOLE:
+                break
+            key = (int(ns), parent, tuple(tokens[i * self.B:(i + 1) * self.B]))
+            e = self.pc_index.get(key)
+            if e is None:
+                e = self.pc_next
+                self.pc_next += 1
+                self.pc_index[key] = e
+                self.pc[e] = [key, b, self.pc_clock, i, 0]
+                if parent >= 0:
+                    self.pc[parent][4] += 1
+                self.ref[b] += 1
+                added += 1
+            else:
+                self.pc[e][2] = self.pc_clock
+            parent = e
+        return added
+
+    def prefix_match(self, tokens: Sequence[int], ns: int) -> Tuple[int, int]:
+        """New sequence sharing the longest cached chain of the tokens'
+        leading full blocks; returns (sequence id, matched tokens)."""
+        tokens = [int(t) for t in tokens]
+        self.pc_clock += 1
+        parent, chain = -1, []
+        for i in range(len(tokens) // self.B):
+            e = self.pc_index.get((int(ns), parent, tuple(tokens[i * self.B:(i + 1) * self.B])))
+            if e is None:
+                break
+            chain.append(e)
+            parent = e
+        table = []
+        for e in chain:
+            self.pc[e][2] = self.pc_clock
+            b = self.pc[e][1]
+            self.ref[b] += 1
+            table.append(b)
+        sid = self.next_id
+        self.next_id += 1
+        self.seqs[sid] = (len(table) * self.B, table)
+        return sid, len(table) * self.B
+
+    def _pc_drop(self, e: int) -> None:
+        key, b, _, _, _ = self.pc.pop(e)
+        del self.pc_index[key]
+        if key[1] >= 0:
+            self.pc[key[1]][4] -= 1
+        self.ref[b] -= 1
+        if self.ref[b] == 0:
+            self.free.append(b)
+
+    def prefix_evict(self, k: int) -> int:
+        """Free up to k blocks held only by the cache (LRU leaves first);
+        returns the number freed."""
+        if k < 0:
+            raise Invalid("negative count")
+        freed = 0
+        while freed < k:
+            cands = [(v[2], -v[3], e) for e, v in self.pc.items() if v[4] == 0 and self.ref[v[1]] == 1]
+            if not cands:
+                break
+            self._pc_drop(min(cands)[2])
+            freed += 1
+        return freed
+
+    def prefix_clear(self) -> int:
+        """Drop every entry (children before parents); returns how many."""
+        n = 0
+        for e in sorted(self.pc, key=lambda e: (-self.pc[e][3], e)):
+            self._pc_drop(e)
+            n += 1
+        return n
+
+    def prefix_snapshot(self):
+        """[(entry, ns, parent, tokens, block, last_use)] by entry index."""
+        return [(e, v[0][0], v[0][1], list(v[0][2]), v[1], v[2]) for e, v in sorted(self.pc.items())]
+
     def append(self, ids: Sequence[int]):
         """One token for each id, in order.  Returns (slots, cow_pairs)."""
         ids = [int(i) for i in ids]
@@ -213,7 +336,7 @@ class Allocator:
 
     def check_invariants(self) -> None:
         """Raise AssertionError if the state breaks a pool invariant."""
-        assert sum(self.ref) == sum(sum(1 for b in t if b != HOLE) for _, t in self.seqs.values())
+        assert sum(self.ref) == sum(sum(1 for b in t if b != HOLE) for _, t in self.seqs.values()) + len(self.pc)
         live = {b for b in range(self.N) if self.ref[b] > 0}
         assert len(set(self.free)) == len(self.free)
         assert live.isdisjoint(self.free)
@@ -231,7 +354,16 @@ class Allocator:
             live_from = next((i for i, b in enumerate(t) if b != HOLE), len(t))
             assert all(b != HOLE for b in t[live_from:])
             assert n % self.B == 0 or live_from < len(t)
+        for v in self.pc.values():
+            counts[v[1]] += 1
         assert counts == self.ref
+        # every entry's parent exists and counts it as a child
+        kids = {e: 0 for e in self.pc}
+        for e, v in self.pc.items():
+            if v[0][1] >= 0:
+                assert v[0][1] in self.pc
+                kids[v[0][1]] += 1
+        assert all(kids[e] == self.pc[e][4] for e in self.pc)
 
     def clone(self) -> "Allocator":
         return copy.deepcopy(self)
@@ -253,6 +385,22 @@ def run_script(alloc: Allocator, ops, on_slots=None):
             alloc.release_before(op[1], op[2])
         elif kind == "window":              # keep the last op[2] positions
             alloc.release_before(op[1], max(0, alloc.length(op[1]) - op[2]))
+        elif kind == "register":            # ("register", sid, tokens, ns)
+            alloc.prefix_register(op[1], op[2], op[3])
+        elif kind == "match":               # ("match", tokens, ns)
+            alloc.prefix_match(op[1], op[2])
+        elif kind == "evict":
+            alloc.prefix_evict(op[1])
+        elif kind == "clear":
+            alloc.prefix_clear()
+        elif kind == "register_stream":     # ("register_stream", sid, stream, ns)
+            from workloads import stream_tokens
+            if op[1] not in alloc.seqs:
+                raise BadSeq(op[1])
+            alloc.prefix_register(op[1], stream_tokens(op[2], alloc.length(op[1])), op[3])
+        elif kind == "match_stream":        # ("match_stream", stream, n, ns)
+            from workloads import stream_tokens
+            alloc.prefix_match(stream_tokens(op[1], op[2]), op[3])
         elif kind == "extend":
             slots, cow = alloc.extend(op[1], op[2])
             if on_slots:

@@ -15,9 +15,20 @@ with open(os.path.join(GOLDEN, "allocator_scripts.json")) as f:
 ERR = {"NO_BLOCKS": A.NoBlocks, "INVALID": A.Invalid, "BAD_SEQ": A.BadSeq}
 
 
-def run_golden_steps(alloc, steps):
-    for st in steps:
-        op = st["op"]
+def _tokens(sc, name):
+    toks = sc.get("tokens", {})
+    if name in toks:
+        return toks[name]
+    return toks[name[0]][:int(name[1:])]          # e.g. "B10": the first 10 of B
+
+
+def run_golden_steps(alloc, steps, sc=None):
+    for k, st in enumerate(steps):
+        op = list(st["op"])
+        if op[0] == "register":
+            op[2] = _tokens(sc, op[2])
+        elif op[0] == "match":
+            op[1] = _tokens(sc, op[1])
         before = alloc.snapshot()
         if "error" in st:
             with pytest.raises(ERR[st["error"]]):
@@ -29,6 +40,14 @@ def run_golden_steps(alloc, steps):
             assert res == st["id"]
         if "released" in st:
             assert res == st["released"], op
+        if "added" in st:
+            assert res == st["added"], op
+        if "freed" in st:
+            assert res == st["freed"], op
+        if "match" in st:
+            assert list(res) == st["match"], op
+        if sc is not None and str(k) in sc.get("cache_after_step", {}):
+            assert [list(e) for e in alloc.prefix_snapshot()] == sc["cache_after_step"][str(k)], k
         if "slots" in st:
             slots, cow = res
             assert slots == st["slots"], op
@@ -50,17 +69,23 @@ def _apply(alloc, op):
         return alloc.append(op[1])
     if k == "release":
         return alloc.release_before(op[1], op[2])
+    if k == "register":
+        return alloc.prefix_register(op[1], op[2], op[3])
+    if k == "match":
+        return alloc.prefix_match(op[1], op[2])
+    if k == "evict":
+        return alloc.prefix_evict(op[1])
     raise ValueError(k)
 
 
 SCRIPTED = {sc["name"]: sc for sc in GOLD["scenarios"] if "steps" in sc}
 
 
-@pytest.mark.parametrize("which", ["fork_cow_free_oom", "sliding_window_release"])
+@pytest.mark.parametrize("which", ["fork_cow_free_oom", "sliding_window_release", "prefix_cache"])
 def test_golden_scenarios(which):
     sc = SCRIPTED[which]
     alloc = A.Allocator(sc["num_blocks"], sc["block"], sc["perm"])
-    run_golden_steps(alloc, sc["steps"])
+    run_golden_steps(alloc, sc["steps"], sc)
     free, ref, seqs, next_id = alloc.snapshot()
     assert free == sc["final"]["free"]
     assert ref == sc["final"]["ref"]
@@ -140,9 +165,10 @@ def test_oom_rolls_back_whole_batch():
     assert alloc.snapshot() == before
 
 
-@pytest.mark.parametrize("seed,windows", [(0, False), (1, False), (2, True), (3, True)])
-def test_random_ops_invariants(seed, windows):
-    ops = workloads.random_op_script(seed, 2500, windows=windows)
+@pytest.mark.parametrize("seed,windows,prefix", [(0, False, False), (1, False, False), (2, True, False),
+                                                 (3, True, False), (4, False, True), (5, True, True)])
+def test_random_ops_invariants(seed, windows, prefix):
+    ops = workloads.random_op_script(seed, 2500, windows=windows, prefix=prefix)
     alloc = A.Allocator(24, 4, np.random.default_rng(seed).permutation(24))
     fails = 0
     for op in ops:
@@ -162,3 +188,51 @@ def test_random_ops_invariants(seed, windows):
             assert alloc.snapshot() == before
         alloc.check_invariants()
     assert fails > 0, "the script should exhaust the small pool sometimes"
+
+
+def test_prefix_cache_namespace_and_exact_keys():
+    """A different namespace (model version / configuration) or a different
+    earlier block never matches, even with identical block tokens."""
+    alloc = A.Allocator(12, 4)
+    a = alloc.create()
+    alloc.extend(a, 12)
+    toks = list(range(100, 112))
+    assert alloc.prefix_register(a, toks, ns=1) == 3
+    _, got = alloc.prefix_match(toks, ns=2)
+    assert got == 0
+    _, got = alloc.prefix_match([0, 0, 0, 0] + toks[4:], ns=1)     # same blocks 1-2, other first block
+    assert got == 0
+    _, got = alloc.prefix_match(toks[:11], ns=1)                   # only full blocks match
+    assert got == 8
+    alloc.check_invariants()
+
+
+def test_prefix_cache_shared_blocks_are_never_written():
+    """A sequence built from cached blocks writes its next token into a
+    fresh block: no copy-on-write pair, no slot inside a cached block."""
+    alloc = A.Allocator(16, 4)
+    a = alloc.create()
+    alloc.extend(a, 10)
+    alloc.prefix_register(a, list(range(10)), ns=0)
+    cached = {v[1] for v in alloc.pc.values()}
+    sid, got = alloc.prefix_match(list(range(10)) + [77, 78], ns=0)
+    assert got == 8
+    slots, cow = alloc.extend(sid, 5)
+    assert cow == [] and not any(s // 4 in cached for s in slots)
+    slots, cow = alloc.append([sid, a])
+    assert cow == [] and not any(s // 4 in cached for s in slots)
+    alloc.check_invariants()
+
+
+def test_prefix_evict_never_frees_blocks_in_use():
+    alloc = A.Allocator(8, 4)
+    a = alloc.create()
+    alloc.extend(a, 8)
+    alloc.prefix_register(a, list(range(8)), ns=0)
+    assert alloc.prefix_evict(5) == 0            # the sequence still holds both blocks
+    alloc.free_seq(a)
+    assert alloc.prefix_evict(1) == 1            # the leaf goes first
+    assert [e[3] for e in alloc.prefix_snapshot()] == [[0, 1, 2, 3]]
+    assert alloc.prefix_clear() == 1
+    assert len(alloc.free) == 8
+    alloc.check_invariants()

@@ -25,6 +25,12 @@ Script operations (ids are assigned 0, 1, 2, ... in create/fork order):
 * ``("release", sid, pos)``            sliding window: give back the blocks
   holding only positions < pos
 * ``("window", sid, W)``               the same with pos = max(0, length - W)
+* ``("register", sid, tokens, ns)``    enter sid's full blocks into the prefix
+  cache under token ids ``tokens`` and namespace ``ns``
+* ``("match", tokens, ns)``            new sequence from the cached chain
+* ``("evict", k)`` / ``("clear",)``    prefix-cache eviction
+* ``("register_stream", sid, stream, ns)`` / ``("match_stream", stream, n, ns)``
+  the same with the token ids of a synthetic stream (``stream_tokens``)
 """
 from __future__ import annotations
 
@@ -344,7 +350,15 @@ CONFIGS = {
 }
 
 
-def random_op_script(seed: int, n_ops: int, max_live: int = 12, max_extend: int = 40, windows: bool = False):
+def stream_tokens(stream: int, n: int) -> List[int]:
+    """Synthetic token ids: stream k shares its first 12·(k + 1) tokens with
+    every other stream, then continues with ids of its own."""
+    shared = 12 * (stream + 1)
+    return [p % 97 if p < shared else 1000 * (stream + 1) + p for p in range(n)]
+
+
+def random_op_script(seed: int, n_ops: int, max_live: int = 12, max_extend: int = 40, windows: bool = False,
+                     prefix: bool = False):
     """A random allocator-only script (no tensor values) for allocator tests:
     create / extend / fork / free / batched append (and, with ``windows``,
     sliding-window releases), ids valid at issue time."""
@@ -372,6 +386,19 @@ def random_op_script(seed: int, n_ops: int, max_live: int = 12, max_extend: int 
             live.remove(sid)
         elif windows and r < 0.74:
             ops.append(("window", int(rng.choice(live)), int(rng.integers(0, 3 * max_extend))))
+        elif prefix and r < 0.84:
+            q = rng.random()
+            ns = int(rng.integers(0, 2))
+            if q < 0.4:
+                ops.append(("register_stream", int(rng.choice(live)), int(rng.integers(0, 4)), ns))
+            elif q < 0.75 and len(live) < max_live:
+                ops.append(("match_stream", int(rng.integers(0, 4)), int(rng.integers(0, 3 * max_extend)), ns))
+                live.append(next_id)
+                next_id += 1
+            elif q < 0.95:
+                ops.append(("evict", int(rng.integers(0, 6))))
+            else:
+                ops.append(("clear",))
         else:
             k = int(rng.integers(1, len(live) + 1))
             ids = [int(x) for x in rng.choice(live, size=k, replace=False)]
