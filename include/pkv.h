@@ -120,8 +120,9 @@ int pkv_seq_create(pkv_pool* pool, int64_t* seq_id);
 /* New sequence sharing every block of `parent` (each block's reference count
  * +1), with the parent's length.                                            */
 int pkv_seq_fork(pkv_pool* pool, int64_t parent, int64_t* child);
-/* Release a sequence: walk its table in logical order, decrement each
- * block's count and push blocks that reach 0 onto the free list.           */
+/* Release a sequence (finished or cancelled): walk its table in logical
+ * order, decrement each block's count and push blocks that reach 0 onto the
+ * free list (blocks the prefix cache or other sequences hold stay).        */
 int pkv_seq_free(pkv_pool* pool, int64_t seq_id);
 
 /* Sliding window: give back every block of a sequence that holds only
@@ -133,6 +134,43 @@ int pkv_seq_free(pkv_pool* pool, int64_t seq_id);
  * PKV_ERR_INVALID.  *n_released (may be NULL) gets the number of blocks
  * released by this call.                                                   */
 int pkv_seq_release_before(pkv_pool* pool, int64_t seq_id, int32_t pos, int32_t* n_released);
+
+/* ---- prefix cache ------------------------------------------------------
+ * «Servicio…presupuesto de memoria» §8: a cache key names every input that
+ * shapes the KV state (the namespace `ns` stands for model version and
+ * configuration); reused pages never expose or let anyone change another
+ * request's private continuation; eviction drops references without freeing
+ * pages still in use.  «PagedAttention e vLLM»: a shared system prompt is
+ * processed once.  Only full blocks are cached.  An entry is keyed exactly
+ * by (ns, parent entry, the block's B token ids) and holds one reference to
+ * its block.  "Use" is a logical clock advanced by each register or match. */
+
+/* Enter the full blocks of a sequence, walked from position 0, under the
+ * token ids tokens[0 .. n_tokens) (n_tokens >= its length, else
+ * PKV_ERR_INVALID): a known key is touched (an entry naming another block
+ * of the same content is kept), an unknown one becomes an entry for the
+ * sequence's block (one more reference).  Stops at a released block.
+ * *n_added (may be NULL) gets the number of new entries.                  */
+int pkv_prefix_register(pkv_pool* pool, int64_t seq_id, const int32_t* tokens, int32_t n_tokens, uint64_t ns,
+                        int32_t* n_added);
+/* New sequence made of the longest cached chain matching the leading full
+ * blocks of tokens[0 .. n_tokens): one more reference per block (as a
+ * fork), length = matched tokens (*n_matched, a multiple of B, may be 0).
+ * Its next token starts a fresh block, so cached blocks are never written. */
+int pkv_prefix_match(pkv_pool* pool, const int32_t* tokens, int32_t n_tokens, uint64_t ns, int64_t* seq_id,
+                     int32_t* n_matched);
+/* Free up to max_blocks blocks: repeatedly drop the least recently used
+ * entry that has no child entry and whose block only the cache holds
+ * (deeper entries first on equal use); the block returns to the free list.
+ * Blocks still used by a sequence are never freed.  *n_freed may be NULL. */
+int pkv_prefix_evict(pkv_pool* pool, int32_t max_blocks, int32_t* n_freed);
+/* Drop every entry (deepest first), e.g. after a model or configuration
+ * change; blocks only the cache held return to the free list.             */
+int pkv_prefix_clear(pkv_pool* pool, int32_t* n_dropped);
+/* Cache entries by index: first call with NULL arrays for *n_entries, then
+ * with arrays of that size (tokens_out: [n_entries][B]).  Host only.       */
+int pkv_prefix_snapshot(const pkv_pool* pool, int64_t* n_entries, int64_t* entry_out, uint64_t* ns_out,
+                        int64_t* parent_out, int32_t* block_out, int64_t* last_use_out, int32_t* tokens_out);
 
 /* Reserve `ntok` >= 0 consecutive slots for one sequence (bulk prefill).
  * slots_out: host int32[ntok].  cow_pairs_out: host int32[2] receiving at

@@ -187,6 +187,145 @@ Status BlockPool::append(const int64_t* ids, int32_t n, int32_t* slots, int32_t*
   return Status::Ok;
 }
 
+size_t PrefixKeyHash::operator()(const PrefixKey& k) const {
+  // FNV-1a over the key's words (only a bucket choice: keys compare exactly)
+  uint64_t h = 1469598103934665603ull;
+  auto mix = [&h](uint64_t w) {
+    for (int i = 0; i < 8; ++i) {
+      h ^= (w >> (8 * i)) & 0xFFu;
+      h *= 1099511628211ull;
+    }
+  };
+  mix(k.ns);
+  mix(static_cast<uint64_t>(k.parent));
+  for (int32_t t : k.tokens) mix(static_cast<uint32_t>(t));
+  return static_cast<size_t>(h);
+}
+
+Status BlockPool::prefix_register(int64_t id, const int32_t* tokens, int32_t n_tokens, uint64_t ns,
+                                  int32_t* added) {
+  *added = 0;
+  auto it = seqs_.find(id);
+  if (it == seqs_.end()) {
+    err_ = "prefix_register: unknown sequence id " + std::to_string(id);
+    return Status::BadSeq;
+  }
+  Sequence& seq = it->second;
+  if (n_tokens < seq.len || (n_tokens > 0 && !tokens)) {
+    err_ = "prefix_register: fewer token ids than the sequence holds";
+    return Status::Invalid;
+  }
+  pc_clock_ += 1;
+  int64_t parent = -1;
+  for (int32_t i = 0; i < seq.len / block_; ++i) {
+    const int32_t b = seq.table[i];
+    if (b == kHole) break;
+    PrefixKey key{ns, parent, std::vector<int32_t>(tokens + static_cast<size_t>(i) * block_,
+                                                   tokens + static_cast<size_t>(i + 1) * block_)};
+    auto f = pc_index_.find(key);
+    int64_t e;
+    if (f == pc_index_.end()) {
+      e = pc_next_++;
+      PrefixEntry ent;
+      ent.key = key;
+      ent.block = b;
+      ent.last_use = pc_clock_;
+      ent.depth = i;
+      pc_index_.emplace(std::move(key), e);
+      pc_.emplace(e, std::move(ent));
+      if (parent >= 0) pc_[parent].children += 1;
+      ref_[b] += 1;
+      *added += 1;
+    } else {
+      e = f->second;
+      pc_[e].last_use = pc_clock_;
+    }
+    parent = e;
+  }
+  return Status::Ok;
+}
+
+Status BlockPool::prefix_match(const int32_t* tokens, int32_t n_tokens, uint64_t ns, int64_t* id,
+                               int32_t* matched) {
+  *matched = 0;
+  if (n_tokens < 0 || (n_tokens > 0 && !tokens)) {
+    err_ = "prefix_match: bad token array";
+    return Status::Invalid;
+  }
+  pc_clock_ += 1;
+  Sequence seq;
+  int64_t parent = -1;
+  std::vector<int64_t> chain;
+  for (int32_t i = 0; i < n_tokens / block_; ++i) {
+    PrefixKey key{ns, parent, std::vector<int32_t>(tokens + static_cast<size_t>(i) * block_,
+                                                   tokens + static_cast<size_t>(i + 1) * block_)};
+    auto f = pc_index_.find(key);
+    if (f == pc_index_.end()) break;
+    chain.push_back(f->second);
+    parent = f->second;
+  }
+  for (int64_t e : chain) {
+    PrefixEntry& ent = pc_[e];
+    ent.last_use = pc_clock_;
+    ref_[ent.block] += 1;
+    seq.table.push_back(ent.block);
+  }
+  seq.len = static_cast<int32_t>(chain.size()) * block_;
+  const int64_t sid = next_id_++;
+  *matched = seq.len;
+  seqs_.emplace(sid, std::move(seq));
+  *id = sid;
+  return Status::Ok;
+}
+
+void BlockPool::drop_entry(int64_t e) {
+  auto it = pc_.find(e);
+  const PrefixEntry& ent = it->second;
+  if (ent.key.parent >= 0) pc_[ent.key.parent].children -= 1;
+  if (--ref_[ent.block] == 0) free_.push_back(ent.block);
+  pc_index_.erase(ent.key);
+  pc_.erase(it);
+}
+
+Status BlockPool::prefix_evict(int32_t k, int32_t* freed) {
+  *freed = 0;
+  if (k < 0) {
+    err_ = "prefix_evict: negative count";
+    return Status::Invalid;
+  }
+  while (*freed < k) {
+    // least recently used leaf held only by the cache; deeper first, then lower index
+    int64_t best = -1;
+    for (const auto& kv : pc_) {
+      const PrefixEntry& ent = kv.second;
+      if (ent.children != 0 || ref_[ent.block] != 1) continue;
+      if (best < 0) {
+        best = kv.first;
+        continue;
+      }
+      const PrefixEntry& b = pc_[best];
+      if (ent.last_use < b.last_use || (ent.last_use == b.last_use && ent.depth > b.depth)) best = kv.first;
+    }
+    if (best < 0) break;
+    drop_entry(best);
+    *freed += 1;
+  }
+  return Status::Ok;
+}
+
+Status BlockPool::prefix_clear(int32_t* dropped) {
+  *dropped = 0;
+  std::vector<std::pair<int32_t, int64_t>> order;       // (-depth, entry): children first
+  order.reserve(pc_.size());
+  for (const auto& kv : pc_) order.emplace_back(-kv.second.depth, kv.first);
+  std::sort(order.begin(), order.end());
+  for (const auto& o : order) {
+    drop_entry(o.second);
+    *dropped += 1;
+  }
+  return Status::Ok;
+}
+
 const Sequence* BlockPool::find(int64_t id) const {
   auto it = seqs_.find(id);
   return it == seqs_.end() ? nullptr : &it->second;

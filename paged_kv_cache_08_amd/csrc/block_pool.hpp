@@ -23,9 +23,22 @@
 // release_before gives back the blocks that hold only positions before the
 // window and marks their table entries kHole, so tables stay indexed by
 // position.
+//
+// Prefix cache («Servicio…presupuesto de memoria» §8: the key identifies every
+// input that shapes the state, model version and configuration included; no
+// request may see or change another's continuation; eviction drops
+// references without freeing pages in use.  «PagedAttention e vLLM»: a shared
+// system prompt is processed once): only full blocks are cached; an entry is
+// keyed exactly by (namespace, parent entry, the block's token ids) and holds
+// one reference to its block.  A match builds a new sequence from the longest
+// cached chain (a block per matched full block, one more reference each);
+// eviction drops the least recently used leaf entry whose block only the
+// cache holds (deeper entries first on equal use), one at a time.  Use is a
+// logical clock advanced once per register or match call.
 #pragma once
 
 #include <cstdint>
+#include <map>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -39,6 +52,25 @@ constexpr int32_t kHole = -1;   // table entry of a block given back by release_
 struct Sequence {
   int32_t len = 0;
   std::vector<int32_t> table;
+};
+
+struct PrefixKey {
+  uint64_t ns = 0;
+  int64_t parent = -1;                 // entry index of the previous block, -1 at position 0
+  std::vector<int32_t> tokens;         // the block's token ids
+  bool operator==(const PrefixKey& o) const { return ns == o.ns && parent == o.parent && tokens == o.tokens; }
+};
+
+struct PrefixKeyHash {
+  size_t operator()(const PrefixKey& k) const;
+};
+
+struct PrefixEntry {
+  PrefixKey key;
+  int32_t block = 0;
+  int64_t last_use = 0;
+  int32_t depth = 0;                   // block index in the chain
+  int32_t children = 0;                // entries whose parent this is
 };
 
 class BlockPool {
@@ -59,6 +91,13 @@ class BlockPool {
   // one slot per id, in order.
   Status append(const int64_t* ids, int32_t n, int32_t* slots, int32_t* cow, int32_t* n_cow);
 
+  // Prefix cache.
+  Status prefix_register(int64_t id, const int32_t* tokens, int32_t n_tokens, uint64_t ns, int32_t* added);
+  Status prefix_match(const int32_t* tokens, int32_t n_tokens, uint64_t ns, int64_t* id, int32_t* matched);
+  Status prefix_evict(int32_t k, int32_t* freed);
+  Status prefix_clear(int32_t* dropped);
+  const std::map<int64_t, PrefixEntry>& prefix_entries() const { return pc_; }
+
   const Sequence* find(int64_t id) const;
   const std::vector<int32_t>& free_stack() const { return free_; }
   const std::vector<int32_t>& refcounts() const { return ref_; }
@@ -72,6 +111,7 @@ class BlockPool {
   // already checked that enough free blocks exist.
   int32_t take_slot(Sequence& seq, int32_t* cow, int32_t* n_cow);
   int32_t pop_free();
+  void drop_entry(int64_t e);
 
   int32_t num_blocks_;
   int32_t block_;
@@ -79,6 +119,10 @@ class BlockPool {
   std::vector<int32_t> ref_;
   std::unordered_map<int64_t, Sequence> seqs_;
   int64_t next_id_ = 0;
+  std::unordered_map<PrefixKey, int64_t, PrefixKeyHash> pc_index_;
+  std::map<int64_t, PrefixEntry> pc_;  // by entry index
+  int64_t pc_next_ = 0;
+  int64_t pc_clock_ = 0;
   std::string err_;
 };
 

@@ -288,6 +288,55 @@ int pkv_seq_release_before(pkv_pool* pool, int64_t id, int32_t pos, int32_t* n_r
   return guarded([&] { return from_alloc(pool->alloc.release_before(id, pos, n_released ? n_released : &dummy), pool); });
 }
 
+int pkv_prefix_register(pkv_pool* pool, int64_t id, const int32_t* tokens, int32_t n_tokens, uint64_t ns,
+                        int32_t* n_added) {
+  if (!pool) return fail(PKV_ERR_INVALID, "prefix_register: null pool");
+  int32_t dummy = 0;
+  return guarded([&] {
+    return from_alloc(pool->alloc.prefix_register(id, tokens, n_tokens, ns, n_added ? n_added : &dummy), pool);
+  });
+}
+
+int pkv_prefix_match(pkv_pool* pool, const int32_t* tokens, int32_t n_tokens, uint64_t ns, int64_t* seq_id,
+                     int32_t* n_matched) {
+  if (!pool || !seq_id) return fail(PKV_ERR_INVALID, "prefix_match: null argument");
+  int32_t dummy = 0;
+  return guarded([&] {
+    return from_alloc(pool->alloc.prefix_match(tokens, n_tokens, ns, seq_id, n_matched ? n_matched : &dummy), pool);
+  });
+}
+
+int pkv_prefix_evict(pkv_pool* pool, int32_t max_blocks, int32_t* n_freed) {
+  if (!pool) return fail(PKV_ERR_INVALID, "prefix_evict: null pool");
+  int32_t dummy = 0;
+  return guarded([&] { return from_alloc(pool->alloc.prefix_evict(max_blocks, n_freed ? n_freed : &dummy), pool); });
+}
+
+int pkv_prefix_clear(pkv_pool* pool, int32_t* n_dropped) {
+  if (!pool) return fail(PKV_ERR_INVALID, "prefix_clear: null pool");
+  int32_t dummy = 0;
+  return guarded([&] { return from_alloc(pool->alloc.prefix_clear(n_dropped ? n_dropped : &dummy), pool); });
+}
+
+int pkv_prefix_snapshot(const pkv_pool* pool, int64_t* n_entries, int64_t* entry_out, uint64_t* ns_out,
+                        int64_t* parent_out, int32_t* block_out, int64_t* last_use_out, int32_t* tokens_out) {
+  if (!pool || !n_entries) return fail(PKV_ERR_INVALID, "prefix_snapshot: null size pointer");
+  const auto& pc = pool->alloc.prefix_entries();
+  *n_entries = static_cast<int64_t>(pc.size());
+  const int32_t B = pool->alloc.block_size();
+  int64_t i = 0;
+  for (const auto& kv : pc) {
+    if (entry_out) entry_out[i] = kv.first;
+    if (ns_out) ns_out[i] = kv.second.key.ns;
+    if (parent_out) parent_out[i] = kv.second.key.parent;
+    if (block_out) block_out[i] = kv.second.block;
+    if (last_use_out) last_use_out[i] = kv.second.last_use;
+    if (tokens_out) std::copy(kv.second.key.tokens.begin(), kv.second.key.tokens.end(), tokens_out + i * B);
+    ++i;
+  }
+  return PKV_OK;
+}
+
 int pkv_seq_extend(pkv_pool* pool, int64_t id, int32_t ntok, int32_t* slots, int32_t* cow,
                    int32_t* n_cow) {
   if (!pool || !n_cow || !cow || (ntok > 0 && !slots)) return fail(PKV_ERR_INVALID, "seq_extend: null argument");

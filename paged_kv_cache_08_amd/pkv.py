@@ -84,6 +84,12 @@ SIGNATURES = [
     ("pkv_seq_fork", ctypes.c_int, [_vp, _i64, _P(_i64)]),
     ("pkv_seq_free", ctypes.c_int, [_vp, _i64]),
     ("pkv_seq_release_before", ctypes.c_int, [_vp, _i64, _i32, _P(_i32)]),
+    ("pkv_prefix_register", ctypes.c_int, [_vp, _i64, _P(_i32), _i32, ctypes.c_uint64, _P(_i32)]),
+    ("pkv_prefix_match", ctypes.c_int, [_vp, _P(_i32), _i32, ctypes.c_uint64, _P(_i64), _P(_i32)]),
+    ("pkv_prefix_evict", ctypes.c_int, [_vp, _i32, _P(_i32)]),
+    ("pkv_prefix_clear", ctypes.c_int, [_vp, _P(_i32)]),
+    ("pkv_prefix_snapshot", ctypes.c_int, [_vp, _P(_i64), _P(_i64), _P(ctypes.c_uint64), _P(_i64), _P(_i32),
+                                           _P(_i64), _P(_i32)]),
     ("pkv_seq_extend", ctypes.c_int, [_vp, _i64, _i32, _P(_i32), _P(_i32), _P(_i32)]),
     ("pkv_append_slots", ctypes.c_int, [_vp, _P(_i64), _i32, _P(_i32), _P(_i32), _P(_i32)]),
     ("pkv_seq_length", ctypes.c_int, [_vp, _i64, _P(_i32)]),
@@ -237,6 +243,55 @@ def pkv_seq_release_before(pool: PoolHandle, seq_id: int, pos: int) -> int:
     out = _i32()
     _check(lib().pkv_seq_release_before(pool.ptr, seq_id, pos, ctypes.byref(out)))
     return out.value
+
+
+def pkv_prefix_register(pool: PoolHandle, seq_id: int, tokens: Sequence[int], ns: int) -> int:
+    """Enter seq_id's full blocks into the prefix cache; returns new entries."""
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    out = _i32()
+    _check(lib().pkv_prefix_register(pool.ptr, seq_id, _as_i32p(t) if len(t) else None, len(t), ns,
+                                     ctypes.byref(out)))
+    return out.value
+
+
+def pkv_prefix_match(pool: PoolHandle, tokens: Sequence[int], ns: int) -> Tuple[int, int]:
+    """New sequence from the cached chain; returns (seq id, matched tokens)."""
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    sid, got = _i64(), _i32()
+    _check(lib().pkv_prefix_match(pool.ptr, _as_i32p(t) if len(t) else None, len(t), ns, ctypes.byref(sid),
+                                  ctypes.byref(got)))
+    return sid.value, got.value
+
+
+def pkv_prefix_evict(pool: PoolHandle, max_blocks: int) -> int:
+    out = _i32()
+    _check(lib().pkv_prefix_evict(pool.ptr, max_blocks, ctypes.byref(out)))
+    return out.value
+
+
+def pkv_prefix_clear(pool: PoolHandle) -> int:
+    out = _i32()
+    _check(lib().pkv_prefix_clear(pool.ptr, ctypes.byref(out)))
+    return out.value
+
+
+def pkv_prefix_snapshot(pool: PoolHandle):
+    """[(entry, ns, parent, tokens, block, last_use)] by entry index."""
+    n = _i64()
+    L = lib()
+    _check(L.pkv_prefix_snapshot(pool.ptr, ctypes.byref(n), None, None, None, None, None, None))
+    k = n.value
+    B = pool.desc["block_size"]
+    e = np.zeros(max(k, 1), dtype=np.int64)
+    ns = np.zeros(max(k, 1), dtype=np.uint64)
+    par = np.zeros(max(k, 1), dtype=np.int64)
+    blk = _i32buf(k)
+    use = np.zeros(max(k, 1), dtype=np.int64)
+    tok = _i32buf(k * B)
+    _check(L.pkv_prefix_snapshot(pool.ptr, ctypes.byref(n), _as_i64p(e), ns.ctypes.data_as(_P(ctypes.c_uint64)),
+                                 _as_i64p(par), _as_i32p(blk), _as_i64p(use), _as_i32p(tok)))
+    return [(int(e[i]), int(ns[i]), int(par[i]), [int(x) for x in tok[i * B:(i + 1) * B]], int(blk[i]), int(use[i]))
+            for i in range(k)]
 
 
 def _pairs(cow: np.ndarray, n: int) -> List[Tuple[int, int]]:

@@ -39,6 +39,17 @@ def apply_both(pool, alloc, op):
         elif kind == "window":
             res_o = alloc.release_before(op[1], max(0, alloc.length(op[1]) - op[2])) if op[1] in alloc.seqs else \
                 alloc.release_before(op[1], 0)
+        elif kind in ("register", "register_stream"):
+            toks = op[2] if kind == "register" else (
+                workloads.stream_tokens(op[2], alloc.length(op[1])) if op[1] in alloc.seqs else [])
+            res_o = alloc.prefix_register(op[1], toks, op[3])
+        elif kind in ("match", "match_stream"):
+            toks = op[1] if kind == "match" else workloads.stream_tokens(op[1], op[2])
+            res_o = alloc.prefix_match(toks, op[-1])
+        elif kind == "evict":
+            res_o = alloc.prefix_evict(op[1])
+        elif kind == "clear":
+            res_o = alloc.prefix_clear()
     except A.AllocError as e:
         err_o = ERR[type(e)]
     err_l = res_l = None
@@ -63,6 +74,22 @@ def apply_both(pool, alloc, op):
             except P.PkvError:
                 n = 0
             res_l = P.pkv_seq_release_before(pool, op[1], max(0, n - op[2]))
+        elif kind in ("register", "register_stream"):
+            if kind == "register":
+                toks = op[2]
+            else:
+                try:
+                    toks = workloads.stream_tokens(op[2], P.pkv_seq_length(pool, op[1]))
+                except P.PkvError:
+                    toks = []
+            res_l = P.pkv_prefix_register(pool, op[1], toks, op[3])
+        elif kind in ("match", "match_stream"):
+            toks = op[1] if kind == "match" else workloads.stream_tokens(op[1], op[2])
+            res_l = P.pkv_prefix_match(pool, toks, op[-1])
+        elif kind == "evict":
+            res_l = P.pkv_prefix_evict(pool, op[1])
+        elif kind == "clear":
+            res_l = P.pkv_prefix_clear(pool)
     except P.PkvError as e:
         err_l = e.status
     assert err_o == err_l, (op, err_o, err_l)
@@ -70,29 +97,37 @@ def apply_both(pool, alloc, op):
         assert res_l[0] == res_o[0], op
         assert res_l[1] == [tuple(p) for p in res_o[1]], op
     elif err_o is None:
-        assert res_l == res_o
+        assert res_l == (tuple(res_o) if isinstance(res_o, tuple) else res_o), (op, res_l, res_o)
     assert P.pkv_pool_snapshot(pool) == tuple(alloc.snapshot()), op
+    assert P.pkv_prefix_snapshot(pool) == [tuple(e) for e in alloc.prefix_snapshot()], op
 
 
-@pytest.mark.parametrize("name", ["fork_cow_free_oom", "sliding_window_release"])
+def _golden_tokens(sc, name):
+    toks = sc.get("tokens", {})
+    return toks[name] if name in toks else toks[name[0]][:int(name[1:])]
+
+
+@pytest.mark.parametrize("name", ["fork_cow_free_oom", "sliding_window_release", "prefix_cache"])
 def test_golden_scenario_matches(name):
     with open(os.path.join(GOLDEN, "allocator_scripts.json")) as f:
         sc = {s["name"]: s for s in json.load(f)["scenarios"]}[name]
     pool = lib_pool(sc["num_blocks"], sc["block"], sc["perm"])
     alloc = A.Allocator(sc["num_blocks"], sc["block"], sc["perm"])
     for st in sc["steps"]:
-        op = st["op"]
-        if op[0] == "append":
-            op = ["append", op[1]]
+        op = list(st["op"])
+        if op[0] == "register":
+            op[2] = _golden_tokens(sc, op[2])
+        elif op[0] == "match":
+            op[1] = _golden_tokens(sc, op[1])
         apply_both(pool, alloc, op)
     free, ref, seqs, next_id = P.pkv_pool_snapshot(pool)
     assert free == sc["final"]["free"] and ref == sc["final"]["ref"]
     assert [[i, n, t] for i, n, t in seqs] == sc["final"]["seqs"] and next_id == sc["final"]["next_id"]
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(12))
 def test_random_scripts(seed):
-    ops = workloads.random_op_script(seed, 1500, windows=seed >= 4)
+    ops = workloads.random_op_script(seed, 1500, windows=4 <= seed < 8 or seed >= 10, prefix=seed >= 8)
     nb, B = (24, 4) if seed % 2 == 0 else (40, 16)
     perm = np.random.default_rng(seed).permutation(nb).astype(np.int32)
     pool = lib_pool(nb, B, perm)
