@@ -627,8 +627,8 @@ int pkv_paged_prefill(const pkv_prefill_args* a, void* stream) {
   if (!aligned16(a->q) || !aligned16(a->out) || !aligned16(a->k_cache) || !aligned16(a->v_cache))
     return fail(PKV_ERR_INVALID, "prefill: q, out and caches must be 16-byte aligned");
   const int64_t G = a->num_q_heads / a->num_kv_heads;
-  const int64_t tiles = (static_cast<int64_t>(a->max_query_len) * G + 255) / 256;
-  if (tiles > 0x7fffffffLL || a->num_seqs > 65535 || a->num_kv_heads > 65535)
+  const int64_t tiles = (static_cast<int64_t>(a->max_query_len) * G + 63) / 64;   // >= the real count
+  if (tiles > 65535 || static_cast<int64_t>(a->num_seqs) * a->num_kv_heads > 0x7fffffffLL)
     return fail(PKV_ERR_INVALID, "prefill: grid too large");
   if (a->max_query_len == 0) return PKV_OK;
   pkv::PrefillParams p{};

@@ -10,9 +10,9 @@
 // las cabezas KV").  Prefill work has many queries per KV token, so unlike
 // decode it is bound by the matrix cores, not by HBM.
 //
-// One workgroup = 4 waves = 256 query rows of one (sequence, KV head).  A row
+// One workgroup = 8 waves = 256 query rows of one (sequence, KV head).  A row
 // is one (query position, query head of the group) pair, position-major, so
-// the group's heads share every K/V tile.  Each wave owns 64 rows (four
+// the group's heads share every K/V tile.  Each wave owns 32 rows (two
 // 16-row blocks).  K/V are streamed in tiles of 64 tokens (four 16-token
 // blocks gathered through the block table) into LDS:
 //   K  [64 tokens][D + 8]   (token rows, 16 bytes of padding against bank
@@ -41,46 +41,63 @@ namespace pkv {
 namespace {
 
 constexpr int kTok = 16;                 // tokens per cache block
-constexpr int kTile = 64;                // tokens per K/V tile
-constexpr int kWaves = 4;
-constexpr int kRB = 4;                   // 16-row blocks per wave
+constexpr int kTile = 64;                // tokens per K/V tile (four blocks)
+
+// 8 waves of 32 rows: 166 registers, no accumulator traffic between AGPRs
+// and VGPRs, two waves per SIMD so one wave's softmax overlaps another's
+// MFMAs (4 waves of 64 rows measured 40% slower).
+#ifndef PKV_PREFILL_WAVES
+#define PKV_PREFILL_WAVES 8
+#endif
+#ifndef PKV_PREFILL_RB
+#define PKV_PREFILL_RB 2
+#endif
+constexpr int kWaves = PKV_PREFILL_WAVES;   // waves per workgroup
+constexpr int kRB = PKV_PREFILL_RB;         // 16-row blocks per wave
 constexpr int kRowsWG = kWaves * kRB * 16;
 
+// LDS holds two tiles (double buffer).  A tile is four K block tiles in the
+// cache's own order ([D/8][16 tokens][8]: a lane's A operand is one 16-byte
+// chunk, 16 lanes read 16 consecutive chunks) and four V block tiles stored
+// half-major ([2 token halves][D columns][8 tokens]: 16 lanes read 8 bytes
+// from 16 consecutive chunks).  Both are filled by direct global-to-LDS
+// loads (lane i writes bytes 16i..16i+15 of each 1 KiB run).
 template <int D>
 struct PrefillShape {
-  static constexpr int kRow = D + 8;                     // K row, bf16 elements
-  static constexpr int vRow = kTile + 4;                 // Vt row, bf16 elements
-  static constexpr int kElems = kTile * kRow;
-  static constexpr int vElems = D * vRow;
-  static constexpr size_t bytes = static_cast<size_t>(kElems + vElems) * 2;
+  static constexpr int blk = kTok * D;                   // bf16 elements of one block tile
+  static constexpr int tile = 8 * blk;                   // K and V of four blocks
+  static constexpr size_t bytes = static_cast<size_t>(2 * tile) * 2;
 };
 
 template <int D>
 __device__ __forceinline__ void write_nan_rows(const PrefillParams& p, int q0, int m, int row_lo, int row_hi,
                                                int kvh) {
   __bf16* out = static_cast<__bf16*>(p.out);
-  for (int r = row_lo + static_cast<int>(threadIdx.x) / (D / 8); r < row_hi; r += 256 / (D / 8)) {
+  constexpr int per_row = D / 8;
+  for (int r = row_lo + static_cast<int>(threadIdx.x) / per_row; r < row_hi; r += kWaves * 64 / per_row) {
     const int qi = r / p.G, g = r - (r / p.G) * p.G;
     if (qi >= m) continue;
-    __bf16* o = out + (static_cast<size_t>(q0 + qi) * p.Hq + kvh * p.G + g) * D + (threadIdx.x % (D / 8)) * 8;
+    __bf16* o = out + (static_cast<size_t>(q0 + qi) * p.Hq + kvh * p.G + g) * D + (threadIdx.x % per_row) * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = static_cast<__bf16>(NAN);
   }
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void prefill_bf16(PrefillParams p) {
+__global__ __launch_bounds__(kWaves * 64) void prefill_bf16(PrefillParams p) {
   using Sh = PrefillShape<D>;
   constexpr int KC = D / 32;             // QK k-steps
   constexpr int VT = D / 16;             // value-column tiles
+  constexpr int kPieces = 8 / kWaves;    // block tiles (K or V) each wave loads per tile
   extern __shared__ __bf16 lds[];
-  __bf16* Kl = lds;
-  __bf16* Vl = lds + Sh::kElems;
 
-  const int s = blockIdx.y;
-  const int kvh = blockIdx.z;
+  // blockIdx.x = (sequence, KV head), blockIdx.y = row tile counted from the
+  // last one: workgroups are dispatched x first, so the longest causal row
+  // tiles of every (sequence, KV head) start before any shorter one.
+  const int s = blockIdx.x / p.Hkv;
+  const int kvh = blockIdx.x - s * p.Hkv;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int c16 = lane & 15;
   const int g4 = lane >> 4;
@@ -91,8 +108,8 @@ __global__ __launch_bounds__(256) void prefill_bf16(PrefillParams p) {
   const int G = p.G;
   if (m < 1) return;
   const int tiles = (m * G + kRowsWG - 1) / kRowsWG;
-  if (static_cast<int>(blockIdx.x) >= tiles) return;
-  const int tile = tiles - 1 - static_cast<int>(blockIdx.x);   // the longest (last) rows first
+  if (static_cast<int>(blockIdx.y) >= tiles) return;
+  const int tile = tiles - 1 - static_cast<int>(blockIdx.y);   // the longest (last) rows first
   const int wg_row0 = tile * kRowsWG;
   const int wg_row1 = min(m * G, wg_row0 + kRowsWG);
   if (n < m || n > p.max_seq_len || n > p.max_blocks * kTok) {
@@ -101,7 +118,6 @@ __global__ __launch_bounds__(256) void prefill_bf16(PrefillParams p) {
   }
   const int c = n - m;                                         // cached context
 
-  // Positions covered by the workgroup and by this wave.
   const int wg_pos_lo = c + wg_row0 / G;
   const int wg_pos_hi = c + (wg_row1 - 1) / G;
   const int w_row0 = wg_row0 + wave * kRB * 16;
@@ -110,7 +126,6 @@ __global__ __launch_bounds__(256) void prefill_bf16(PrefillParams p) {
   const int w_pos_lo = c + w_row0 / G;
   const int w_pos_hi = c + max(w_row0, w_row_last) / G;
 
-  // Rows of this lane (one per row block) and their Q^T operands.
   int pos[kRB];
   bool row_ok[kRB];
   bf16x8 qreg[kRB][KC];
@@ -130,10 +145,66 @@ __global__ __launch_bounds__(256) void prefill_bf16(PrefillParams p) {
     }
   }
 
-  // Key range of the workgroup: [key_lo, wg_pos_hi].
   const int key_lo = p.window > 0 ? max(0, wg_pos_lo - p.window + 1) : 0;
   const int kt_first = key_lo / kTile;
   const int kt_last = wg_pos_hi / kTile;
+
+  const size_t tile_elems = static_cast<size_t>(kTok) * D;
+  const size_t blk_stride = static_cast<size_t>(p.Hkv) * tile_elems;
+  const __bf16* kc_base = static_cast<const __bf16*>(p.k_cache) + kvh * tile_elems;
+  const __bf16* vc_base = static_cast<const __bf16*>(p.v_cache) + kvh * tile_elems;
+  const int32_t* table = p.block_tables + static_cast<size_t>(s) * p.max_blocks;
+  bool bad = false;                                            // wave-uniform
+
+  // Start the loads of tile kt into buffer `buf`: this wave's pieces.
+  auto issue = [&](int kt, int buf) {
+    __bf16* base = lds + buf * Sh::tile;
+#pragma unroll
+    for (int pc = 0; pc < kPieces; ++pc) {
+      const int piece = wave * kPieces + pc;                   // 0..3: K of block piece; 4..7: V of block piece-4
+      const bool is_v = piece >= 4;
+      const int tb = piece & 3;
+      const int bi = kt * (kTile / kTok) + tb;
+      const int tok0 = bi * kTok;
+      __bf16* dst = base + (is_v ? 4 * Sh::blk : 0) + tb * Sh::blk;
+      const bool needed = tok0 < n && tok0 + kTok > key_lo;
+      int b = needed ? table[bi] : 0;
+      if (static_cast<unsigned>(b) >= static_cast<unsigned>(p.num_blocks)) {
+        bad = true;
+        b = 0;
+      }
+      if (!needed) {                                           // nothing to read: zeros
+#pragma unroll
+        for (int u = 0; u < D / 32; ++u)
+          *reinterpret_cast<u32x4*>(dst + (64 * u + lane) * 8) = u32x4{0, 0, 0, 0};
+        continue;
+      }
+      const __bf16* src = (is_v ? vc_base : kc_base) + static_cast<size_t>(b) * blk_stride;
+#pragma unroll
+      for (int u = 0; u < D / 32; ++u) {
+        const int ci = 64 * u + lane;                          // LDS chunk of this lane
+        // K keeps the cache order; V chunk ci holds (half ci / D, column ci % D),
+        // which is cache chunk 2 * column + half
+        const int gi = is_v ? 2 * (ci % D) + ci / D : ci;
+        __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(gi) * 8, dst + 64 * u * 8, 16, 0, 0);
+      }
+    }
+  };
+  // After this wave's loads of tile kt landed: zero V tokens at or past n
+  // (free or poisoned slots) in the block that holds token n - 1.
+  auto fix_tail = [&](int kt, int buf) {
+#pragma unroll
+    for (int pc = 0; pc < kPieces; ++pc) {
+      const int piece = wave * kPieces + pc;
+      if (piece < 4) continue;
+      const int tb = piece & 3;
+      const int tok0 = (kt * (kTile / kTok) + tb) * kTok;
+      if (tok0 >= n || tok0 + kTok <= n) continue;
+      __bf16* dst = lds + buf * Sh::tile + 4 * Sh::blk + tb * Sh::blk;
+      for (int e = lane; e < D; e += 64)
+        for (int t = n - tok0; t < kTok; ++t) dst[((t >> 3) * D + e) * 8 + (t & 7)] = static_cast<__bf16>(0.f);
+    }
+  };
 
   f32x4 acc[kRB][VT];
 #pragma unroll
@@ -147,149 +218,101 @@ __global__ __launch_bounds__(256) void prefill_bf16(PrefillParams p) {
     l_run[rb] = 0.f;
   }
 
-  const size_t tile_elems = static_cast<size_t>(kTok) * D;                // one (block, head) tile
-  const size_t blk_stride = static_cast<size_t>(p.Hkv) * tile_elems;
-  const __bf16* kc_base = static_cast<const __bf16*>(p.k_cache) + kvh * tile_elems;
-  const __bf16* vc_base = static_cast<const __bf16*>(p.v_cache) + kvh * tile_elems;
-  const int32_t* table = p.block_tables + static_cast<size_t>(s) * p.max_blocks;
-
+  issue(kt_first, 0);
+  int buf = 0;
   for (int kt = kt_first; kt <= kt_last; ++kt) {
-    // ---- gather the tile's four blocks into LDS (all 256 threads) ----
-    __syncthreads();                                   // the previous tile is consumed
-    const int tb = tid >> 6;                           // block of the tile this thread copies
-    const int bi = kt * (kTile / kTok) + tb;           // logical block
-    const int tok0 = bi * kTok;
-    bool bad = false;
-    const bool needed = tok0 < n && tok0 + kTok > key_lo;
-    int b = 0;
-    if (needed) {
-      b = table[bi];
-      bad = static_cast<unsigned>(b) >= static_cast<unsigned>(p.num_blocks);
-    }
-    if (__syncthreads_or(bad)) {
-      write_nan_rows<D>(p, q0, m, wg_row0, wg_row1, kvh);
-      return;
-    }
-    const __bf16* kb = kc_base + static_cast<size_t>(b) * blk_stride;
-    const __bf16* vb = vc_base + static_cast<size_t>(b) * blk_stride;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    fix_tail(kt, buf);
+    __syncthreads();                   // tile kt is in LDS; tile kt-1 is consumed by every wave
+    if (kt < kt_last) issue(kt + 1, buf ^ 1);
+    const __bf16* Kt = lds + buf * Sh::tile;
+    const __bf16* Vt = Kt + 4 * Sh::blk;
+    buf ^= 1;
+    if (!wave_active) continue;
+
 #pragma unroll
-    for (int u = 0; u < D / 32; ++u) {
-      const int ci = lane + 64 * u;                    // 16-byte chunk of the block's K / V tile
-      u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-      if (needed) {
-        kv = *reinterpret_cast<const u32x4*>(kb + static_cast<size_t>(ci) * 8);
-        vv = *reinterpret_cast<const u32x4*>(vb + static_cast<size_t>(ci) * 8);
-      }
-      // K chunk ci = (head-dim chunk ci / 16, token ci % 16)
-      const int kt_tok = ci & 15, kt_c = ci >> 4;
-      if (tok0 + kt_tok >= n) kv = u32x4{0, 0, 0, 0};
-      *reinterpret_cast<u32x4*>(Kl + (tb * kTok + kt_tok) * Sh::kRow + 8 * kt_c) = kv;
-      // V chunk ci = (value column ci / 2, tokens 8 (ci % 2) .. +7)
-      const int ve = ci >> 1, vh = ci & 1;
-      const int vtok = tok0 + 8 * vh;
-      if (vtok + 8 > n) {
-        // zero the tokens at or past the sequence end (free or poisoned slots)
-        uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+    for (int hh = 0; hh < 2; ++hh) {                           // 32-token halves of the tile
+      const int t_lo = kt * kTile + 32 * hh, t_hi = t_lo + 31;
+      if (t_lo > w_pos_hi) break;
+      if (p.window > 0 && t_hi < w_pos_lo - p.window + 1) continue;
+      const bool masked = t_hi > w_pos_lo || (p.window > 0 && t_lo < w_pos_hi - p.window + 1);
+
+      f32x4 S[kRB][2];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = (vtok + 2 * e < n) ? 0x0000FFFFu : 0u;
-          const uint32_t hi = (vtok + 2 * e + 1 < n) ? 0xFFFF0000u : 0u;
-          w[e] &= lo | hi;
+      for (int tl = 0; tl < 2; ++tl) {
+        const __bf16* kb = Kt + (2 * hh + tl) * Sh::blk;
+        bf16x8 ka[KC];
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+          ka[kc] = *reinterpret_cast<const bf16x8*>(kb + ((4 * kc + g4) * kTok + c16) * 8);
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+          f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kc], qreg[rb][kc], sc, 0, 0, 0);
+          S[rb][tl] = sc;
         }
-        vv = u32x4{w[0], w[1], w[2], w[3]};
       }
-      *reinterpret_cast<u32x2*>(Vl + ve * Sh::vRow + tb * kTok + 8 * vh) = u32x2{vv.x, vv.y};
-      *reinterpret_cast<u32x2*>(Vl + ve * Sh::vRow + tb * kTok + 8 * vh + 4) = u32x2{vv.z, vv.w};
-    }
-    __syncthreads();
 
-    // ---- this wave's rows against the tile ----
-    const int t_lo = kt * kTile, t_hi = t_lo + kTile - 1;
-    if (!wave_active || t_lo > w_pos_hi) continue;
-    if (p.window > 0 && t_hi < w_pos_lo - p.window + 1) continue;
-    const bool masked = t_hi > w_pos_lo || (p.window > 0 && t_lo < w_pos_hi - p.window + 1);
-
-    f32x4 S[kRB][4];
-#pragma unroll
-    for (int tb2 = 0; tb2 < 4; ++tb2) {
-      bf16x8 ka[KC];
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
-        ka[kc] = *reinterpret_cast<const bf16x8*>(Kl + (tb2 * kTok + c16) * Sh::kRow + 32 * kc + 8 * g4);
+      // Scores stay in raw units; exp2(x * scale_log2 - m * scale_log2) is
+      // one fused multiply-add per score (scale_log2 > 0 keeps the max).
+      bf16x8 pb[kRB];
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) {
-        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+        float x[8];
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kc], qreg[rb][kc], sc, 0, 0, 0);
-        S[rb][tb2] = sc;
-      }
-    }
-
-    bf16x8 pb[kRB][2];
+        for (int j = 0; j < 8; ++j) x[j] = S[rb][j >> 2][j & 3];
+        if (masked) {
+          const int lo = p.window > 0 ? pos[rb] - p.window + 1 : 0;
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) {
-      float x[4][4];
-#pragma unroll
-      for (int tb2 = 0; tb2 < 4; ++tb2)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[tb2][j] = S[rb][tb2][j] * p.scale_log2;
-      if (masked) {
-        const int lo = p.window > 0 ? pos[rb] - p.window + 1 : 0;
-#pragma unroll
-        for (int tb2 = 0; tb2 < 4; ++tb2)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int t = t_lo + tb2 * kTok + 4 * g4 + j;
-            if (t > pos[rb] || t < lo) x[tb2][j] = -INFINITY;
+          for (int j = 0; j < 8; ++j) {
+            const int t = t_lo + (j >> 2) * kTok + 4 * g4 + (j & 3);
+            if (t > pos[rb] || t < lo) x[j] = -INFINITY;
           }
-      }
-      float mx = -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        mx = max_over_rows(mx);
+        const float m_new = fmaxf(m_run[rb], mx);
+        if (__any(m_new > m_run[rb])) {
+          // Rows of one block have different masks: a row whose maximum did
+          // not grow keeps alpha = 1 (also with no key yet, m = -inf).
+          const float alpha = m_new > m_run[rb] ? exp2_fast((m_run[rb] - m_new) * p.scale_log2) : 1.f;
+          l_run[rb] *= alpha;
 #pragma unroll
-      for (int tb2 = 0; tb2 < 4; ++tb2)
-        mx = fmaxf(mx, fmaxf(fmaxf(x[tb2][0], x[tb2][1]), fmaxf(x[tb2][2], x[tb2][3])));
-      mx = max_over_rows(mx);
-      const float m_new = fmaxf(m_run[rb], mx);
-      if (__any(m_new > m_run[rb])) {
-        // Rows of one block have different masks: a row whose maximum did not
-        // grow keeps alpha = 1 (also when it has seen no key yet, m = -inf).
-        const float alpha = m_new > m_run[rb] ? exp2_fast(m_run[rb] - m_new) : 1.f;
-        l_run[rb] *= alpha;
-#pragma unroll
-        for (int t = 0; t < VT; ++t) acc[rb][t] *= alpha;
-        m_run[rb] = m_new;
-      }
-      // A row with no key in this tile yet keeps m = -inf: its terms are 0.
-      const float m_use = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
-      float ps = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+          for (int t = 0; t < VT; ++t) acc[rb][t] *= alpha;
+          m_run[rb] = m_new;
+        }
+        // A row with no key yet keeps m = -inf: its terms are 0.
+        const float neg_m = m_run[rb] == -INFINITY ? 0.f : -m_run[rb] * p.scale_log2;
+        float ps = 0.f;
         bf16x8 v;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const __bf16 e = static_cast<__bf16>(exp2_fast(x[2 * ks + (j >> 2)][j & 3] - m_use));
-          v[j] = e;
-          ps += static_cast<float>(e);
+          const float e = exp2_fast(__builtin_fmaf(x[j], p.scale_log2, neg_m));
+          v[j] = static_cast<__bf16>(e);
+          ps += e;
         }
-        pb[rb][ks] = v;
+        pb[rb] = v;
+        l_run[rb] += ps;
       }
-      l_run[rb] += ps;
-    }
 
+      const __bf16* v0 = Vt + (2 * hh) * Sh::blk + ((g4 >> 1) * D + c16) * 8 + 4 * (g4 & 1);
 #pragma unroll
-    for (int t = 0; t < VT; ++t) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const __bf16* vr = Vl + (16 * t + c16) * Sh::vRow + 32 * ks + 4 * g4;
-        const u32x2 a0 = *reinterpret_cast<const u32x2*>(vr);
-        const u32x2 a1 = *reinterpret_cast<const u32x2*>(vr + kTok);
+      for (int t = 0; t < VT; ++t) {
+        const u32x2 a0 = *reinterpret_cast<const u32x2*>(v0 + 16 * t * 8);
+        const u32x2 a1 = *reinterpret_cast<const u32x2*>(v0 + Sh::blk + 16 * t * 8);
         const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{a0.x, a0.y, a1.x, a1.y});
 #pragma unroll
         for (int rb = 0; rb < kRB; ++rb)
-          acc[rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rb][ks], acc[rb][t], 0, 0, 0);
+          acc[rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rb], acc[rb][t], 0, 0, 0);
       }
     }
   }
 
+  if (__syncthreads_or(bad)) {
+    write_nan_rows<D>(p, q0, m, wg_row0, wg_row1, kvh);
+    return;
+  }
   if (!wave_active) return;
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
@@ -318,11 +341,11 @@ bool prefill_shape_supported(int head_dim, int block_size) {
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   if (p.S <= 0 || p.max_query_len <= 0) return hipSuccess;
   const long long tiles = (static_cast<long long>(p.max_query_len) * p.G + kRowsWG - 1) / kRowsWG;
-  dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(p.S), static_cast<unsigned>(p.Hkv));
+  dim3 grid(static_cast<unsigned>(p.S * p.Hkv), static_cast<unsigned>(tiles));
   if (p.d == 128)
-    hipLaunchKernelGGL(prefill_bf16<128>, grid, dim3(256), PrefillShape<128>::bytes, stream, p);
+    hipLaunchKernelGGL(prefill_bf16<128>, grid, dim3(kWaves * 64), PrefillShape<128>::bytes, stream, p);
   else if (p.d == 64)
-    hipLaunchKernelGGL(prefill_bf16<64>, grid, dim3(256), PrefillShape<64>::bytes, stream, p);
+    hipLaunchKernelGGL(prefill_bf16<64>, grid, dim3(kWaves * 64), PrefillShape<64>::bytes, stream, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
