@@ -75,7 +75,16 @@ def copy_calibration(reps: int = 5, nbytes: int = 1 << 30) -> None:
 
 
 class DecodeBench:
-    """Builds the batch through the library, then runs timed decode steps."""
+    """Builds the batch through the library, then runs timed decode steps.
+
+    The part of step i that does not depend on the step's data — the host
+    slot reservation and the block-table upload — runs on a second stream
+    while step i-1's attention still runs on the main stream, as a serving
+    loop can do, since block placement does not depend on token values.  The
+    new K/V append, copy-on-write copies and attention stay on the main
+    stream, in step order.  Device tables are double-buffered (step i uses
+    buffer i % 2): the side stream waits until the step that last read its
+    buffer has finished, and the main stream waits for the upload."""
 
     def __init__(self, wl, steps_total: int, partition: int = 0, device="cuda", window: int = 0):
         import numpy as np
@@ -108,9 +117,16 @@ class DecodeBench:
         self.lengths = [int(n) - 1 for n in wl.lengths]        # current lengths
         self.max_len = max(self.lengths) + steps_total
         self.max_blocks = -(-self.max_len // wl.block)
-        self.eng.tables = torch.empty((len(self.ids), self.max_blocks), dtype=torch.int32, device=self.dev)
-        self.eng.lens = torch.empty((len(self.ids),), dtype=torch.int32, device=self.dev)
+        self.tables = [torch.empty((len(self.ids), self.max_blocks), dtype=torch.int32, device=self.dev)
+                       for _ in range(2)]
+        self.lens = [torch.empty((len(self.ids),), dtype=torch.int32, device=self.dev) for _ in range(2)]
         self.eng.host_lens = np.zeros(len(self.ids), dtype=np.int32)
+        self.main = torch.cuda.current_stream()
+        self.side = torch.cuda.Stream()          # default priority
+        self.ready = [torch.cuda.Event() for _ in range(2)]
+        self.done = [torch.cuda.Event() for _ in range(2)]
+        for e in self.done:
+            e.record(self.main)
         # per-step inputs: new K/V per layer and the step's queries
         g = torch.Generator(device=self.dev)
         g.manual_seed(wl.seed * 7919 + 1)
@@ -122,8 +138,12 @@ class DecodeBench:
                      for _ in range(wl.layers)]
         self.q = [torch.randn((S, wl.Hq, wl.d), generator=g, device=self.dev).to(dt) for _ in range(wl.layers)]
         self.out = [torch.empty_like(self.q[l]) for l in range(wl.layers)]
-        self.args = [self.eng.decode_args(l, self.q[l], self.out[l], self.max_len, window=window)
-                     for l in range(wl.layers)]
+        self.args = []
+        for b in range(2):
+            self.eng.tables, self.eng.lens = self.tables[b], self.lens[b]
+            self.args.append([self.eng.decode_args(l, self.q[l], self.out[l], self.max_len, window=window)
+                              for l in range(wl.layers)])
+        torch.cuda.synchronize()      # the side stream's first step reads the inputs made above
         self.step_idx = 0
         self.kv_bytes = []            # attention KV bytes of each step (all layers)
         self.events = []              # (k3 start, k3 end) per layer per step
@@ -131,9 +151,10 @@ class DecodeBench:
     def step(self, record_events: bool):
         P, torch = self.P, self.torch
         j = self.step_idx
+        b = j % 2
+        side = self.side
+        side.wait_event(self.done[b])        # the step that last used these tables has finished
         slots, cow = P.pkv_append_slots(self.eng.pool, self.ids)
-        if cow:
-            P.pkv_copy_blocks(self.eng.pool, cow)
         for i in range(len(self.lengths)):
             self.lengths[i] += 1
         if self.window:                  # a block that has just left the window goes back to the pool
@@ -142,18 +163,23 @@ class DecodeBench:
                 start = n - self.window
                 if start > 0 and start % B == 0:
                     P.pkv_seq_release_before(self.eng.pool, sid, start)
-        P.pkv_sync_tables(self.eng.pool, self.ids, self.eng.tables, self.eng.lens, self.eng.host_lens)
+        P.pkv_sync_tables(self.eng.pool, self.ids, self.tables[b], self.lens[b], self.eng.host_lens, side)
+        self.ready[b].record(side)
+        self.main.wait_event(self.ready[b])
+        if cow:
+            P.pkv_copy_blocks(self.eng.pool, cow)
         for l in range(self.layers):
-            P.pkv_kv_append_last(self.eng.pool, l, self.knew[l][j], self.vnew[l][j], self.eng.tables, self.eng.lens)
+            P.pkv_kv_append_last(self.eng.pool, l, self.knew[l][j], self.vnew[l][j], self.tables[b], self.lens[b])
             if record_events:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record()
-            P.pkv_paged_decode_partial(self.args[l])
+            P.pkv_paged_decode_partial(self.args[b][l])
             if record_events:
                 e1.record()
                 self.events.append((e0, e1))
-            P.pkv_paged_decode_reduce(self.args[l])
+            P.pkv_paged_decode_reduce(self.args[b][l])
+        self.done[b].record(self.main)
         wl = self.wl
         attended = sum(min(n, self.window) if self.window else n for n in self.lengths)
         self.kv_bytes.append(attended * wl.Hkv * wl.kv_bytes_per_token_head() * self.layers)

@@ -29,7 +29,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
+#include <cstdio>
 #include <cstdint>
 #include <cstdlib>
 #include <type_traits>
@@ -41,14 +43,30 @@ namespace pkv {
 namespace {
 
 constexpr int kBlock = 16;   // tokens per block on the decode path
+// Blocks in flight per wave.  Two streaming waves on one SIMD do not share
+// it evenly: the arbiter favours the older wave (about 3.5 : 1 in measured
+// per-wave end times), so with equal work the younger wave streams alone for
+// the second half of a launch.  The deep variant keeps twice the bytes in
+// flight from a single wave per SIMD (the register file it needs allows no
+// second one), which has no partner to wait for; the bf16 cache uses it for
+// every batch.  The 8-bit cache does more conversion work per byte and
+// measured faster with two shallow waves per SIMD.
 #ifndef PKV_DEPTH
 #define PKV_DEPTH 3
 #endif
-constexpr int kDepth = PKV_DEPTH;  // blocks in flight per wave on the bf16 decode path
+#ifndef PKV_DEPTH_DEEP
+#define PKV_DEPTH_DEEP 5
+#endif
 #ifndef PKV_DEPTH_FP8
 #define PKV_DEPTH_FP8 4
 #endif
-constexpr int kDepthFp8 = PKV_DEPTH_FP8;  // the same on the 8-bit cache path
+#ifndef PKV_DEPTH_FP8_DEEP
+#define PKV_DEPTH_FP8_DEEP 8
+#endif
+constexpr int kDepth = PKV_DEPTH;                 // bf16 cache: 12 loads per block
+constexpr int kDepthDeep = PKV_DEPTH_DEEP;        // (vmcnt counts at most 63 loads)
+constexpr int kDepthFp8 = PKV_DEPTH_FP8;          // 8-bit cache: 6 loads per block
+constexpr int kDepthFp8Deep = PKV_DEPTH_FP8_DEEP;
 
 // K/V tiles are read exactly once per decode call: stream them with the
 // non-temporal hint so they do not displace reusable lines.  On MI355X this
@@ -176,8 +194,10 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyBlocksParams p) {
 // decode: shared prologue
 // ---------------------------------------------------------------------------
 // A wave streams a run of up to `ppw` consecutive partitions of one
-// (sequence, KV head, query-head group): at most kMaxWaveBlocks blocks.
-constexpr int kMaxWaveBlocks = 256;
+// (sequence, KV head, query-head group); the last run of a sequence may also
+// take the partitions left over after whole runs.  At most kMaxWaveBlocks
+// blocks (five id registers of 64 lanes).
+constexpr int kMaxWaveBlocks = 320;
 
 // Partitions are aligned to absolute positions (partition k holds tokens
 // [k·P, (k+1)·P)); with a sliding window they are numbered from the first
@@ -189,7 +209,7 @@ struct WaveTask {
   int t_lo, t_end;              // the wave's tokens: [t_lo, t_end)
   int blk_first, nblk;          // first logical block and block count
   int boundary0;                // wave-local block count that closes its first partition
-  int id0, id1, id2, id3;       // lane l of idC holds block blk_first + 64C + l
+  int id0, id1, id2, id3, id4;  // lane l of idC holds block blk_first + 64C + l
 };
 
 // First partition overlapping the window of a sequence of length n, and the
@@ -240,13 +260,13 @@ __device__ __forceinline__ bool setup_task(const DecodeParams& p, WaveTask& w) {
   window_partitions(p, w.n, t0, pf, w.P);
   w.part0 = grp * p.ppw;
   if (w.part0 >= w.P) return false;
-  w.part_end = min(w.P, w.part0 + p.ppw);
+  w.part_end = grp == p.groups - 1 ? w.P : min(w.P, w.part0 + p.ppw);
   w.t_lo = max(t0, (pf + w.part0) * p.partition);
   w.t_end = min(w.n, (pf + w.part_end) * p.partition);
   w.blk_first = w.t_lo / kBlock;
   w.nblk = (w.t_end - w.blk_first * kBlock + kBlock - 1) / kBlock;
   w.boundary0 = (pf + w.part0 + 1) * (p.partition / kBlock) - w.blk_first;
-  bool bad = w.blk_first + w.nblk > p.max_blocks;
+  bool bad = w.blk_first + w.nblk > p.max_blocks || w.nblk > kMaxWaveBlocks;
   bool bad_lane = false;
   const int32_t* row = p.block_tables + static_cast<size_t>(w.s) * p.max_blocks + w.blk_first;
   auto fetch = [&](int c) {
@@ -261,6 +281,7 @@ __device__ __forceinline__ bool setup_task(const DecodeParams& p, WaveTask& w) {
   w.id1 = fetch(1);
   w.id2 = fetch(2);
   w.id3 = fetch(3);
+  w.id4 = fetch(4);
   bad = bad || __any(bad_lane);
   if (bad) {
     if (w.P == 1) write_nan_rows<T, D>(p, w.s, w.h0, w.nh);
@@ -272,9 +293,9 @@ __device__ __forceinline__ bool setup_task(const DecodeParams& p, WaveTask& w) {
 
 // Physical id of a wave's i-th block (i wave-uniform) from the four id
 // registers.
-__device__ __forceinline__ int block_id(int id0, int id1, int id2, int id3, int i) {
+__device__ __forceinline__ int block_id(int id0, int id1, int id2, int id3, int id4, int i) {
   const int c = i >> 6;
-  const int v = c == 0 ? id0 : c == 1 ? id1 : c == 2 ? id2 : id3;
+  const int v = c == 0 ? id0 : c == 1 ? id1 : c == 2 ? id2 : c == 3 ? id3 : id4;
   return __builtin_amdgcn_readlane(v, i & 63);
 }
 
@@ -348,13 +369,13 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
   // stream ends: a global store in the middle of the stream would make every
   // later wait drain all loads in flight (stores and loads share vmcnt).
   extern __shared__ float staged[];
-  int s_, kvh, h0, nh, P, part0, part_end, t_lo, t_end, blk_first, nblk, boundary0, id0, id1, id2, id3;
+  int s_, kvh, h0, nh, P, part0, part_end, t_lo, t_end, blk_first, nblk, boundary0, id0, id1, id2, id3, id4;
   {
     WaveTask w;
     if (!setup_task<__bf16, D>(p, w)) return;
     s_ = w.s; kvh = w.kvh; h0 = w.h0; nh = w.nh; P = w.P; part0 = w.part0; part_end = w.part_end;
     t_lo = w.t_lo; t_end = w.t_end; blk_first = w.blk_first; nblk = w.nblk; boundary0 = w.boundary0;
-    id0 = w.id0; id1 = w.id1; id2 = w.id2; id3 = w.id3;
+    id0 = w.id0; id1 = w.id1; id2 = w.id2; id3 = w.id3; id4 = w.id4;
   }
   const int lane = threadIdx.x;
   const int c16 = lane & 15;
@@ -383,7 +404,7 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
   const uint32_t v_off = kFp8 ? static_cast<uint32_t>(lane) * 16u : static_cast<uint32_t>(c16 * 4 + g4) * 8u;
 
   auto load_block = [&](BlockRegs<D, kFp8>& r, int i) {
-    const size_t b = static_cast<size_t>(block_id(id0, id1, id2, id3, i));
+    const size_t b = static_cast<size_t>(block_id(id0, id1, id2, id3, id4, i));
     const u32x4* kp = reinterpret_cast<const u32x4*>(kc_b + b * blk_bytes + k_off);
     if constexpr (kFp8) {
       const u32x4* vp = reinterpret_cast<const u32x4*>(vc_b + b * blk_bytes + v_off);
@@ -644,13 +665,13 @@ template <int D>
 __global__ __launch_bounds__(64) void decode_partial_f32(DecodeParams p) {
   constexpr int KC = D / 16;
   constexpr int NT = D / 16;
-  int s_, kvh, h0, nh, P, part0, t_lo, t_end, blk_first, nblk, id0, id1, id2, id3;
+  int s_, kvh, h0, nh, P, part0, t_lo, t_end, blk_first, nblk, id0, id1, id2, id3, id4;
   {
     WaveTask w;
     if (!setup_task<float, D>(p, w)) return;
     s_ = w.s; kvh = w.kvh; h0 = w.h0; nh = w.nh; P = w.P; part0 = w.part0;
     t_lo = w.t_lo; t_end = w.t_end; blk_first = w.blk_first; nblk = w.nblk;
-    id0 = w.id0; id1 = w.id1; id2 = w.id2; id3 = w.id3;
+    id0 = w.id0; id1 = w.id1; id2 = w.id2; id3 = w.id3; id4 = w.id4;
   }
   const int lane = threadIdx.x;
   const int c16 = lane & 15;
@@ -678,7 +699,7 @@ __global__ __launch_bounds__(64) void decode_partial_f32(DecodeParams p) {
   float l_run = 0.f;
 
   for (int i = 0; i < nblk; ++i) {    // one partition per wave (ppw = 1)
-    const int b = block_id(id0, id1, id2, id3, i);
+    const int b = block_id(id0, id1, id2, id3, id4, i);
     const f32x4* kp = reinterpret_cast<const f32x4*>(kc + b * blk_stride) + lane;
     const f32x4* vp = reinterpret_cast<const f32x4*>(vc + b * blk_stride) + c16 * 4 + g4;
     f32x4 kr[KC], vr[NT];
@@ -856,67 +877,128 @@ bool decode_shape_supported(int kind, int head_dim, int block_size) {
   return false;
 }
 
-// Partitions per wave for the bf16-query kernels.  Each wave streams a run of
-// consecutive partitions; for long batches runs are made as long as possible
-// while the grid still fills every resident wave slot once (one round:
-// equal-length runs then finish together instead of leaving a partly filled
-// last round).
-// PKV_WAVE_PARTITIONS overrides the choice.
+// Resident waves of one decode variant on this device, and the LDS each of
+// them may take for staged partials without lowering that residency.
+struct Residency {
+  int waves;
+  int lds_per_wave;
+};
+
 template <int D, int NBUF, bool kFp8>
-static int pick_partitions_per_wave(const DecodeParams& p) {
-  static int slots = 0;   // resident waves on the device (per kernel variant)
-  static int forced = -1;
-  if (forced < 0) {
-    const char* e = std::getenv("PKV_WAVE_PARTITIONS");
-    forced = e ? std::max(0, std::atoi(e)) : 0;
-  }
-  const int rows = std::min(16, p.G);
-  int max_ppw = std::min(p.pmax, kMaxWaveBlocks * kBlock / p.partition);
-  // LDS for the staged partials stays within 20 KiB per wave, so eight
-  // resident waves still fit in a CU's 160 KiB and LDS never lowers occupancy
-  const int lds_row = (p.d + 2) * static_cast<int>(sizeof(float));
-  max_ppw = std::max(1, std::min(max_ppw, 1 + (20 * 1024) / (rows * lds_row)));
-  if (forced > 0) return std::min(forced, max_ppw);
-  if (slots == 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_partial_bf16<D, NBUF, kFp8>, 64, 0) !=
-            hipSuccess || per_cu <= 0)
-      per_cu = 8;
-    slots = cus * per_cu;
-  }
-  // Long runs pay only for batches of equal-length sequences with at least
-  // three rounds of work; mixed lengths balance better with one partition
-  // per wave.  Without the caller's length hint nothing is known: one.
-  if (p.tasks_hint <= 0 || !p.uniform_hint || p.tasks_hint < 3LL * slots) return 1;
-  return static_cast<int>(std::min<long long>(p.tasks_hint / slots, max_ppw));
+static Residency query_residency() {
+  int dev = 0, cus = 0, per_cu = 0, lds = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+      lds <= 0)
+    lds = 64 * 1024;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_partial_bf16<D, NBUF, kFp8>, 64, 0) !=
+          hipSuccess || per_cu <= 0)
+    per_cu = 8;
+  return Residency{cus * per_cu, lds / per_cu};
 }
 
 template <int D, int NBUF, bool kFp8>
-static hipError_t launch_bf16q(DecodeParams p, hipStream_t stream) {
-  p.ppw = pick_partitions_per_wave<D, NBUF, kFp8>(p);
-  const long long groups = (p.pmax + p.ppw - 1) / p.ppw;
-  dim3 grid(static_cast<unsigned>(groups * p.S * p.Hkv), (p.G + 15) / 16);
-  const size_t shmem = static_cast<size_t>(p.ppw - 1) * std::min(16, p.G) * (p.d + 2) * sizeof(float);
+static const Residency& residency() {
+  static const Residency r = query_residency<D, NBUF, kFp8>();
+  return r;
+}
+
+static int env_int(const char* name) {
+  const char* e = std::getenv(name);
+  return e ? std::max(0, std::atoi(e)) : -1;
+}
+
+// Long runs pay only for batches of equal-length sequences (per the caller's
+// length hint) with at least three rounds of work for `waves` resident waves;
+// mixed lengths balance better with one partition per wave, and without the
+// hint nothing is known.
+static bool long_uniform(const DecodeParams& p, int waves) {
+  return p.tasks_hint > 0 && p.uniform_hint && p.tasks_hint >= 3LL * waves;
+}
+
+// Partitions per wave.  Each wave streams a run of consecutive partitions;
+// for long uniform batches runs are made as long as possible while the grid
+// still fills every resident wave slot once (one round: equal-length runs then
+// finish together instead of leaving a partly filled last round).  A run's
+// staged partials must fit the wave's LDS share and its blocks the four id
+// registers.  PKV_WAVE_PARTITIONS overrides the choice.
+// Largest run (in partitions) that fits the id registers and the wave's LDS
+// share for staged partials.
+static int max_run(const DecodeParams& p, const Residency& r) {
+  const int rows = std::min(16, p.G);
+  const int lds_row = (p.d + 2) * static_cast<int>(sizeof(float));
+  const int by_ids = kMaxWaveBlocks * kBlock / p.partition;
+  return std::max(1, std::min(by_ids, 1 + r.lds_per_wave / (rows * lds_row)));
+}
+
+static int pick_partitions_per_wave(const DecodeParams& p, const Residency& r) {
+  static const int forced = env_int("PKV_WAVE_PARTITIONS");
+  // leave room for a short remainder to join the last run
+  const int max_ppw = std::min(p.pmax, std::max(1, max_run(p, r) - 1));
+  if (forced > 0) return std::min(forced, max_ppw);
+  if (!long_uniform(p, r.waves)) return 1;
+  return static_cast<int>(std::min<long long>(p.tasks_hint / r.waves, max_ppw));
+}
+
+// Runs of ppw partitions; partitions left over after whole runs join the last
+// run when that run still fits (a short leftover run would otherwise wait for
+// a free slot and finish last), else they form one more run.
+static void set_runs(DecodeParams& p, const Residency& r) {
+  p.ppw = pick_partitions_per_wave(p, r);
+  const int whole = p.pmax / p.ppw;
+  const int rest = p.pmax - whole * p.ppw;
+  p.groups = (rest == 0 || (whole > 0 && p.ppw + rest <= max_run(p, r))) ? std::max(1, whole) : whole + 1;
+}
+
+// Longest run of a launch, in partitions.
+static int longest_run(const DecodeParams& p) {
+  return std::max(p.ppw, p.pmax - (p.groups - 1) * p.ppw);
+}
+
+template <int D, int NBUF, bool kFp8>
+static hipError_t launch_variant(DecodeParams p, hipStream_t stream) {
+  const Residency& r = residency<D, NBUF, kFp8>();
+  set_runs(p, r);
+  dim3 grid(static_cast<unsigned>(static_cast<long long>(p.groups) * p.S * p.Hkv), (p.G + 15) / 16);
+  const size_t shmem =
+      static_cast<size_t>(longest_run(p) - 1) * std::min(16, p.G) * (p.d + 2) * sizeof(float);
+  static const int trace = env_int("PKV_TRACE_SCHEDULE");   // print the first choice of each variant
+  static std::atomic<bool> traced{false};
+  if (trace > 0 && !traced.exchange(true))
+    std::fprintf(stderr, "decode_partial<d=%d, depth=%d, fp8=%d>: %d resident waves, %d B LDS each; ppw=%d, "
+                 "grid=%ux%u, %zu B LDS\n", D, NBUF, kFp8 ? 1 : 0, r.waves, r.lds_per_wave, p.ppw, grid.x, grid.y,
+                 shmem);
   hipLaunchKernelGGL((decode_partial_bf16<D, NBUF, kFp8>), grid, dim3(64), shmem, stream, p);
   return hipGetLastError();
+}
+
+// bf16 cache: the deep variant; 8-bit cache: the shallow one
+// (PKV_DECODE_DEEP=0/1 forces the choice).
+template <int D, bool kFp8>
+static hipError_t launch_bf16q(const DecodeParams& p, hipStream_t stream) {
+  constexpr int kShallow = kFp8 ? kDepthFp8 : kDepth;
+  constexpr int kDeep = kFp8 ? kDepthFp8Deep : kDepthDeep;
+  static const int forced = env_int("PKV_DECODE_DEEP");
+  const bool deep = forced >= 0 ? forced > 0 : !kFp8;
+  return deep ? launch_variant<D, kDeep, kFp8>(p, stream) : launch_variant<D, kShallow, kFp8>(p, stream);
 }
 
 hipError_t launch_decode_partial(const DecodeParams& p0, int kind, hipStream_t stream) {
   DecodeParams p = p0;
   switch (kind) {
     case kDecodeBF16:
-      if (p.d == 128) return launch_bf16q<128, kDepth, false>(p, stream);
-      if (p.d == 64) return launch_bf16q<64, kDepth, false>(p, stream);
+      if (p.d == 128) return launch_bf16q<128, false>(p, stream);
+      if (p.d == 64) return launch_bf16q<64, false>(p, stream);
       return hipErrorInvalidValue;
     case kDecodeFP8KV:
-      if (p.d == 128) return launch_bf16q<128, kDepthFp8, true>(p, stream);
-      if (p.d == 64) return launch_bf16q<64, kDepthFp8, true>(p, stream);
+      if (p.d == 128) return launch_bf16q<128, true>(p, stream);
+      if (p.d == 64) return launch_bf16q<64, true>(p, stream);
       return hipErrorInvalidValue;
     case kDecodeF32: {
       p.ppw = 1;
+      p.groups = p.pmax;
       dim3 grid(static_cast<unsigned>(static_cast<long long>(p.pmax) * p.S * p.Hkv), (p.G + 15) / 16);
       if (p.d == 128) hipLaunchKernelGGL(decode_partial_f32<128>, grid, dim3(64), 0, stream, p);
       else if (p.d == 64) hipLaunchKernelGGL(decode_partial_f32<64>, grid, dim3(64), 0, stream, p);
