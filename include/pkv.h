@@ -345,7 +345,8 @@ typedef struct pkv_prefill_args {
   int32_t max_seq_len;        /* upper bound of seq_lens                    */
   int32_t max_query_len;      /* upper bound of the chunk sizes (grid)      */
   int32_t dtype;              /* PKV_BF16                                   */
-  float scale;                /* score scale, e.g. 1/sqrt(d)                */
+  float scale;                /* score scale, e.g. 1/sqrt(d); positive and  */
+                              /*   finite (else PKV_ERR_INVALID)            */
   int32_t window;             /* > 0: sliding window; 0 = causal, full      */
 } pkv_prefill_args;
 

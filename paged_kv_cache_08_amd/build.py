@@ -40,6 +40,11 @@ def build(verbose: bool = False) -> str:
         if src.endswith(".hip"):
             # packed fp32 VALU forms are kept off; the device pass honours this flag
             cmd += [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+            if src == "prefill.hip":
+                # The prefill kernel handles NaN explicitly (masked scores are
+                # selected to -inf, bad blocks write NaN rows), so its maxima
+                # need no NaN canonicalization of every MFMA result.
+                cmd += ["-fno-honor-nans"]
         else:
             cmd += ["-D__HIP_PLATFORM_AMD__"]
         cmd += ["-c", os.path.join(CSRC, src), "-o", obj]

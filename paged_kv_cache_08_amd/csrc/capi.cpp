@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <cmath>
 #include <cstring>
 #include <exception>
 #include <new>
@@ -620,6 +621,8 @@ int pkv_paged_prefill(const pkv_prefill_args* a, void* stream) {
   if (a->num_q_heads % a->num_kv_heads != 0)
     return fail(PKV_ERR_INVALID, "prefill: num_q_heads must be a multiple of num_kv_heads");
   if (a->window < 0) return fail(PKV_ERR_INVALID, "prefill: window must be >= 0");
+  if (!(a->scale > 0.f) || !(a->scale < INFINITY))
+    return fail(PKV_ERR_INVALID, "prefill: scale must be positive and finite");
   if (!pkv::prefill_shape_supported(a->head_dim, a->block_size))
     return fail(PKV_ERR_UNSUPPORTED, "prefill: supported shapes are block_size 16, head_dim 64 or 128");
   if (!a->q || !a->out || !a->k_cache || !a->v_cache || !a->block_tables || !a->seq_lens || !a->query_start)

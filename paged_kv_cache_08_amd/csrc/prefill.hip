@@ -18,15 +18,19 @@
 //   K  [64 tokens][D + 8]   (token rows, 16 bytes of padding against bank
 //                            conflicts),
 //   Vt [D][64 + 4]          (value-column rows, tokens fastest, padded).
-// Per tile and wave, with lane l = 16*g + c (g = l/16, c = l%16):
-//   S^T = K · Q^T   v_mfma_f32_16x16x32_bf16, A = K (row = token c of a
-//                   16-token block, k = head-dim values 32kc+8g..+7),
-//                   B = Q^T (column = row c of a row block; held in
-//                   registers); lane l gets tokens 4g..4g+3 of row c.
-//   O^T += Vt · P   v_mfma_f32_16x16x32_bf16 over 32 tokens (two 16-token
-//                   blocks b0, b1): k-slot 8g+j is token 16*b0+4g+j (j < 4)
-//                   or 16*b1+4g+j-4, so B = P is the lane's own eight
-//                   probabilities and A = two 8-byte runs of a Vt row.
+// Per 32-token half tile (cache blocks b0, b1) and wave, with lane
+// l = 16*g + c (g = l/16, c = l%16), lane group g owns the eight tokens
+// tau(g, j) = 16*(g/2) + 8*(g%2) + j, j = 0..7 (block g/2, half g%2):
+//   S^T = K · Q^T   two v_mfma_f32_16x16x32_bf16 (m = 0, 1) per head-dim
+//                   slice, A = K rows permuted so that output row 4g+i is
+//                   token tau(g, 4m+i) (A row c = token 16*(c/8) +
+//                   8*((c/4)%2) + 4m + c%4, k = head-dim values 32kc+8g..+7),
+//                   B = Q^T (column = row c of a row block; in registers);
+//                   lane l gets tokens tau(g, 4m..4m+3) of row c.
+//   O^T += Vt · P   v_mfma_f32_16x16x32_bf16 over the 32 tokens, k-slot
+//                   8g+j = token tau(g, j): B = P is the lane's own eight
+//                   probabilities and A is one 16-byte chunk of V (value
+//                   column 16t+c, half g%2 of block g/2).
 //                   Lane l accumulates value columns 16t+4g..+3 of row c.
 #include <hip/hip_runtime.h>
 
@@ -52,21 +56,29 @@ constexpr int kTile = 64;                // tokens per K/V tile (four blocks)
 #ifndef PKV_PREFILL_RB
 #define PKV_PREFILL_RB 2
 #endif
+#ifndef PKV_PREFILL_BUFS
+#define PKV_PREFILL_BUFS 3
+#endif
 constexpr int kWaves = PKV_PREFILL_WAVES;   // waves per workgroup
+constexpr int kBufs = PKV_PREFILL_BUFS;     // K/V tiles in LDS: loads run kBufs - 1 tiles ahead
 constexpr int kRB = PKV_PREFILL_RB;         // 16-row blocks per wave
 constexpr int kRowsWG = kWaves * kRB * 16;
 
-// LDS holds two tiles (double buffer).  A tile is four K block tiles in the
+// LDS holds kBufs tiles (a ring: tile kt + kBufs - 1 is loaded while tile
+// kt is consumed).  A tile is four K block tiles in the
 // cache's own order ([D/8][16 tokens][8]: a lane's A operand is one 16-byte
-// chunk, 16 lanes read 16 consecutive chunks) and four V block tiles stored
-// half-major ([2 token halves][D columns][8 tokens]: 16 lanes read 8 bytes
-// from 16 consecutive chunks).  Both are filled by direct global-to-LDS
+// chunk) and four V block tiles stored half-major ([2 token halves][D
+// columns][8 tokens]: a lane's A operand is one 16-byte chunk, 16 lanes read
+// 16 consecutive chunks).  Block tiles sit 64 bytes apart beyond their 4 KiB
+// (D = 128), so the 16 lanes of a K read — eight tokens from each block of a
+// pair — fall on distinct banks.  Both are filled by direct global-to-LDS
 // loads (lane i writes bytes 16i..16i+15 of each 1 KiB run).
 template <int D>
 struct PrefillShape {
   static constexpr int blk = kTok * D;                   // bf16 elements of one block tile
-  static constexpr int tile = 8 * blk;                   // K and V of four blocks
-  static constexpr size_t bytes = static_cast<size_t>(2 * tile) * 2;
+  static constexpr int blk_stride = blk + 32;            // + 64 bytes between block tiles
+  static constexpr int tile = 8 * blk_stride;            // K and V of four blocks
+  static constexpr size_t bytes = static_cast<size_t>(kBufs * tile) * 2;
 };
 
 template <int D>
@@ -145,6 +157,14 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16(PrefillParams p) {
     }
   }
 
+  // The Q loads complete here, before the tile loop: read first inside the
+  // loop, they would make the compiler wait for every load in flight there
+  // (the next tiles' loads included) on each tile.
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, qreg[rb][kc])));
+
   const int key_lo = p.window > 0 ? max(0, wg_pos_lo - p.window + 1) : 0;
   const int kt_first = key_lo / kTile;
   const int kt_last = wg_pos_hi / kTile;
@@ -156,54 +176,55 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16(PrefillParams p) {
   const int32_t* table = p.block_tables + static_cast<size_t>(s) * p.max_blocks;
   bool bad = false;                                            // wave-uniform
 
-  // Start the loads of tile kt into buffer `buf`: this wave's pieces.
+  // Each wave loads one piece of every tile: the K (waves 0..3) or V (waves
+  // 4..7) block tile of block slot tb = wave % 4.  Block ids are read with
+  // scalar loads (the table is read-only here): they complete under
+  // lgkmcnt, so no table read sits among the tile loads that vmcnt counts.
+  static_assert(kPieces == 1, "one piece per wave and tile");
+  const int tb = wave & 3;
+  const bool is_v = wave >= 4;
+  const __attribute__((address_space(4))) int32_t* table_s =
+      (const __attribute__((address_space(4))) int32_t*)table;
+
+  // Start the loads of tile kt into buffer `buf`: this wave's piece.
+  // Returns whether a global load was issued (a piece outside the sequence
+  // or window is zero-filled instead).
   auto issue = [&](int kt, int buf) {
-    __bf16* base = lds + buf * Sh::tile;
-#pragma unroll
-    for (int pc = 0; pc < kPieces; ++pc) {
-      const int piece = wave * kPieces + pc;                   // 0..3: K of block piece; 4..7: V of block piece-4
-      const bool is_v = piece >= 4;
-      const int tb = piece & 3;
-      const int bi = kt * (kTile / kTok) + tb;
-      const int tok0 = bi * kTok;
-      __bf16* dst = base + (is_v ? 4 * Sh::blk : 0) + tb * Sh::blk;
-      const bool needed = tok0 < n && tok0 + kTok > key_lo;
-      int b = needed ? table[bi] : 0;
-      if (static_cast<unsigned>(b) >= static_cast<unsigned>(p.num_blocks)) {
-        bad = true;
-        b = 0;
-      }
-      if (!needed) {                                           // nothing to read: zeros
-#pragma unroll
-        for (int u = 0; u < D / 32; ++u)
-          *reinterpret_cast<u32x4*>(dst + (64 * u + lane) * 8) = u32x4{0, 0, 0, 0};
-        continue;
-      }
-      const __bf16* src = (is_v ? vc_base : kc_base) + static_cast<size_t>(b) * blk_stride;
-#pragma unroll
-      for (int u = 0; u < D / 32; ++u) {
-        const int ci = 64 * u + lane;                          // LDS chunk of this lane
-        // K keeps the cache order; V chunk ci holds (half ci / D, column ci % D),
-        // which is cache chunk 2 * column + half
-        const int gi = is_v ? 2 * (ci % D) + ci / D : ci;
-        __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(gi) * 8, dst + 64 * u * 8, 16, 0, 0);
-      }
+    const int bi = kt * (kTile / kTok) + tb;
+    const int tok0 = bi * kTok;
+    __bf16* dst = lds + buf * Sh::tile + (is_v ? 4 * Sh::blk_stride : 0) + tb * Sh::blk_stride;
+    const bool needed = tok0 < n && tok0 + kTok > key_lo;
+    int b = needed ? table_s[bi] : 0;
+    if (static_cast<unsigned>(b) >= static_cast<unsigned>(p.num_blocks)) {
+      bad = true;
+      b = 0;
     }
+    if (!needed) {                                             // nothing to read: zeros
+#pragma unroll
+      for (int u = 0; u < D / 32; ++u)
+        *reinterpret_cast<u32x4*>(dst + (64 * u + lane) * 8) = u32x4{0, 0, 0, 0};
+      return false;
+    }
+    const __bf16* src = (is_v ? vc_base : kc_base) + static_cast<size_t>(b) * blk_stride;
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u) {
+      const int ci = 64 * u + lane;                            // LDS chunk of this lane
+      // K keeps the cache order; V chunk ci holds (half ci / D, column ci % D),
+      // which is cache chunk 2 * column + half
+      const int gi = is_v ? 2 * (ci % D) + ci / D : ci;
+      __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(gi) * 8, dst + 64 * u * 8, 16, 0, 0);
+    }
+    return true;
   };
   // After this wave's loads of tile kt landed: zero V tokens at or past n
   // (free or poisoned slots) in the block that holds token n - 1.
   auto fix_tail = [&](int kt, int buf) {
-#pragma unroll
-    for (int pc = 0; pc < kPieces; ++pc) {
-      const int piece = wave * kPieces + pc;
-      if (piece < 4) continue;
-      const int tb = piece & 3;
-      const int tok0 = (kt * (kTile / kTok) + tb) * kTok;
-      if (tok0 >= n || tok0 + kTok <= n) continue;
-      __bf16* dst = lds + buf * Sh::tile + 4 * Sh::blk + tb * Sh::blk;
-      for (int e = lane; e < D; e += 64)
-        for (int t = n - tok0; t < kTok; ++t) dst[((t >> 3) * D + e) * 8 + (t & 7)] = static_cast<__bf16>(0.f);
-    }
+    if (!is_v) return;
+    const int tok0 = (kt * (kTile / kTok) + tb) * kTok;
+    if (tok0 >= n || tok0 + kTok <= n) return;
+    __bf16* dst = lds + buf * Sh::tile + 4 * Sh::blk_stride + tb * Sh::blk_stride;
+    for (int e = lane; e < D; e += 64)
+      for (int t = n - tok0; t < kTok; ++t) dst[((t >> 3) * D + e) * 8 + (t & 7)] = static_cast<__bf16>(0.f);
   };
 
   f32x4 acc[kRB][VT];
@@ -211,23 +232,57 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16(PrefillParams p) {
   for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
     for (int t = 0; t < VT; ++t) acc[rb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[kRB], l_run[kRB];
+  // Per 16-row block: running maxima (raw score units), -m * scale_log2 for
+  // the exp's fused multiply-add, and the maxima at which the next rescale is
+  // due.  Row sums come from one more MFMA per half tile, of the
+  // probabilities against an all-ones A operand: every element of acc_l is
+  // its row's sum of the same bf16 probabilities that weight V.
+  f32x4 acc_l[kRB];
+  float m_run[kRB], neg_ms[kRB], thr[kRB];
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
+    acc_l[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run[rb] = -INFINITY;
-    l_run[rb] = 0.f;
+    neg_ms[rb] = 0.f;
+    thr[rb] = -INFINITY;
   }
+  // Conditional rescale: the running maxima move only when some row's
+  // maximum grew by more than 8 in exp2 units.  Until then a term
+  // exp2((x - m) * scale_log2) is at most 2^8, which the fp32 sums and the
+  // bf16 probabilities hold with the same relative precision as terms below
+  // 1; the final division by the sum cancels the offset.
+  const float thr_gap = 8.f / p.scale_log2;
+  bf16x8 ones;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ones[j] = static_cast<__bf16>(1.f);
 
+  // Loads in flight are this wave's pieces of the next kBufs - 1 tiles; every
+  // wave issues the same pieces for every tile, so a wait for all but the
+  // younger tiles' loads (one piece of D/32 loads per wave and tile, when it
+  // was loaded and not zero-filled) leaves exactly tile kt complete.
+  static_assert(kPieces == 1 && kBufs == 3, "the wait counts below assume one piece per wave and three buffers");
+  constexpr int kLoadsPerTile = D / 32;
+  bool ahead = false;                  // whether tile kt + 1 issued loads (issued before the wait below)
   issue(kt_first, 0);
+  if (kt_first < kt_last) ahead = issue(kt_first + 1, 1);
   int buf = 0;
   for (int kt = kt_first; kt <= kt_last; ++kt) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (ahead) {
+      if constexpr (kLoadsPerTile == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     fix_tail(kt, buf);
-    __syncthreads();                   // tile kt is in LDS; tile kt-1 is consumed by every wave
-    if (kt < kt_last) issue(kt + 1, buf ^ 1);
+    // Tile kt is in LDS (every wave waited for its own loads of it above,
+    // and for its LDS writes here); tile kt-1 is consumed by every wave.  A
+    // plain barrier: __syncthreads() would also wait for the loads of the
+    // next tile, which must stay in flight.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    ahead = kt + 2 <= kt_last ? issue(kt + 2, buf == 0 ? 2 : buf - 1) : false;
     const __bf16* Kt = lds + buf * Sh::tile;
-    const __bf16* Vt = Kt + 4 * Sh::blk;
-    buf ^= 1;
+    const __bf16* Vt = Kt + 4 * Sh::blk_stride;
+    buf = buf == kBufs - 1 ? 0 : buf + 1;
     if (!wave_active) continue;
 
 #pragma unroll
@@ -236,76 +291,77 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16(PrefillParams p) {
       if (t_lo > w_pos_hi) break;
       if (p.window > 0 && t_hi < w_pos_lo - p.window + 1) continue;
       const bool masked = t_hi > w_pos_lo || (p.window > 0 && t_lo < w_pos_hi - p.window + 1);
-
       f32x4 S[kRB][2];
+      // A row c of MFMA mm: token 8*((c/4)%2) + 4*mm + c%4 of block 2*hh + c/8
+      const __bf16* kb = Kt + (2 * hh + (c16 >> 3)) * Sh::blk_stride + (8 * ((c16 >> 2) & 1) + (c16 & 3)) * 8;
 #pragma unroll
-      for (int tl = 0; tl < 2; ++tl) {
-        const __bf16* kb = Kt + (2 * hh + tl) * Sh::blk;
+      for (int mm = 0; mm < 2; ++mm) {
         bf16x8 ka[KC];
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc)
-          ka[kc] = *reinterpret_cast<const bf16x8*>(kb + ((4 * kc + g4) * kTok + c16) * 8);
+          ka[kc] = *reinterpret_cast<const bf16x8*>(kb + ((4 * kc + g4) * kTok + 4 * mm) * 8);
 #pragma unroll
         for (int rb = 0; rb < kRB; ++rb) {
           f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kc = 0; kc < KC; ++kc) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kc], qreg[rb][kc], sc, 0, 0, 0);
-          S[rb][tl] = sc;
+          S[rb][mm] = sc;
         }
       }
 
       // Scores stay in raw units; exp2(x * scale_log2 - m * scale_log2) is
       // one fused multiply-add per score (scale_log2 > 0 keeps the max).
       bf16x8 pb[kRB];
+      const int tok_x0 = t_lo + 16 * (g4 >> 1) + 8 * (g4 & 1);        // token of x[0]; x[j] is tok_x0 + j
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) {
         float x[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] = S[rb][j >> 2][j & 3];
         if (masked) {
-          const int lo = p.window > 0 ? pos[rb] - p.window + 1 : 0;
+          const int hi = pos[rb] - tok_x0;                           // keys j <= hi are at or before the row
+          if (p.window > 0) {
+            const int lo = pos[rb] - p.window + 1 - tok_x0;          // and j >= lo inside its window
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int t = t_lo + (j >> 2) * kTok + 4 * g4 + (j & 3);
-            if (t > pos[rb] || t < lo) x[j] = -INFINITY;
+            for (int j = 0; j < 8; ++j)
+              if (j > hi || j < lo) x[j] = -INFINITY;
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              if (j > hi) x[j] = -INFINITY;
           }
         }
         float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
         mx = max_over_rows(mx);
-        const float m_new = fmaxf(m_run[rb], mx);
-        if (__any(m_new > m_run[rb])) {
+        if (__any(mx > thr[rb])) {
           // Rows of one block have different masks: a row whose maximum did
           // not grow keeps alpha = 1 (also with no key yet, m = -inf).
+          const float m_new = fmaxf(m_run[rb], mx);
           const float alpha = m_new > m_run[rb] ? exp2_fast((m_run[rb] - m_new) * p.scale_log2) : 1.f;
-          l_run[rb] *= alpha;
+          acc_l[rb] *= alpha;
 #pragma unroll
           for (int t = 0; t < VT; ++t) acc[rb][t] *= alpha;
           m_run[rb] = m_new;
+          neg_ms[rb] = m_new == -INFINITY ? 0.f : -m_new * p.scale_log2;   // no key yet: terms are 0
+          thr[rb] = m_new + thr_gap;
         }
-        // A row with no key yet keeps m = -inf: its terms are 0.
-        const float neg_m = m_run[rb] == -INFINITY ? 0.f : -m_run[rb] * p.scale_log2;
-        float ps = 0.f;
         bf16x8 v;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float e = exp2_fast(__builtin_fmaf(x[j], p.scale_log2, neg_m));
-          v[j] = static_cast<__bf16>(e);
-          ps += e;
-        }
+        for (int j = 0; j < 8; ++j) v[j] = static_cast<__bf16>(exp2_fast(__builtin_fmaf(x[j], p.scale_log2, neg_ms[rb])));
         pb[rb] = v;
-        l_run[rb] += ps;
       }
 
-      const __bf16* v0 = Vt + (2 * hh) * Sh::blk + ((g4 >> 1) * D + c16) * 8 + 4 * (g4 & 1);
+      const __bf16* v0 = Vt + (2 * hh + (g4 >> 1)) * Sh::blk_stride + ((g4 & 1) * D + c16) * 8;
 #pragma unroll
       for (int t = 0; t < VT; ++t) {
-        const u32x2 a0 = *reinterpret_cast<const u32x2*>(v0 + 16 * t * 8);
-        const u32x2 a1 = *reinterpret_cast<const u32x2*>(v0 + Sh::blk + 16 * t * 8);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{a0.x, a0.y, a1.x, a1.y});
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(v0 + 16 * t * 8);
 #pragma unroll
         for (int rb = 0; rb < kRB; ++rb)
           acc[rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rb], acc[rb][t], 0, 0, 0);
       }
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb)
+        acc_l[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[rb], acc_l[rb], 0, 0, 0);
     }
   }
 
@@ -316,7 +372,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16(PrefillParams p) {
   if (!wave_active) return;
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
-    const float l_tot = sum_over_rows(l_run[rb]);
+    const float l_tot = acc_l[rb][0];
     if (!row_ok[rb]) continue;
     const int r = w_row0 + rb * 16 + c16;
     const int qi = r / G, g = r - (r / G) * G;

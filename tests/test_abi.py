@@ -130,3 +130,32 @@ def test_workspace_bytes():
     rows = 16 * 64 * 64
     ml = (rows * 8 + 255) // 256 * 256
     assert P.pkv_decode_workspace_bytes(16, 64, 128, 32768, 512) == ml + rows * 128 * 4
+
+
+def _prefill_args(**kw):
+    a = P.pkv_prefill_args()
+    base = dict(q=16, out=16, k_cache=16, v_cache=16, block_tables=16, seq_lens=16, query_start=16, num_seqs=2,
+                num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16, num_blocks=10, max_blocks=4,
+                max_seq_len=64, max_query_len=32, dtype=P.PKV_BF16, scale=0.1, window=0)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(dtype=P.PKV_F32), P.PKV_ERR_UNSUPPORTED),
+    (dict(num_q_heads=7), P.PKV_ERR_INVALID),
+    (dict(head_dim=96), P.PKV_ERR_UNSUPPORTED),
+    (dict(window=-1), P.PKV_ERR_INVALID),
+    (dict(scale=0.0), P.PKV_ERR_INVALID),         # the kernel keeps raw scores: the scale must be > 0
+    (dict(scale=-0.1), P.PKV_ERR_INVALID),
+    (dict(scale=float("inf")), P.PKV_ERR_INVALID),
+    (dict(scale=float("nan")), P.PKV_ERR_INVALID),
+    (dict(query_start=0), P.PKV_ERR_INVALID),
+    (dict(q=8), P.PKV_ERR_INVALID),                # misaligned
+])
+def test_prefill_argument_validation(bad, status):
+    with pytest.raises(P.PkvError) as e:
+        P.pkv_paged_prefill(_prefill_args(**bad), stream=0)
+    assert e.value.status == status
