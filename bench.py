@@ -288,6 +288,14 @@ def prefill_cpu_baseline(wl, seconds: float, window: int = 0):
                       f"{heads} query heads one at a time, {t:.1f} s"}
 
 
+def launch_stats_us(ms):
+    """Median, min and max of per-launch HIP event times (ms) in us."""
+    v = sorted(ms)
+    n = len(v)
+    med = v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+    return {"median": round(med * 1e3, 2), "min": round(v[0] * 1e3, 2), "max": round(v[-1] * 1e3, 2)}
+
+
 def run_prefill(args, wl):
     import torch
     log(f"setup {wl.description}")
@@ -318,7 +326,7 @@ def run_prefill(args, wl):
         "prefill_tokens_per_s": round(float(wl.chunk_lens.sum()) * args.steps / elapsed, 1),
         "roofline": {"bound": "mfma", "kernel": "prefill_bf16", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
-                     "avg_launch_us": round(k_avg * 1e6, 2),
+                     "avg_launch_us": round(k_avg * 1e6, 2), "launch_us": launch_stats_us(k_ms),
                      "algorithmic_flops_per_launch": wl.prefill_flops(args.window)},
     }
     log(f"timed {args.steps} steps: {value:.1f} TFLOP/s; prefill kernel {k_avg * 1e6:.1f} us")
@@ -478,7 +486,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "decode_partial", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "traffic_bytes_per_launch": traffic_bytes,
-                     "avg_launch_us": round(k3_avg_s * 1e6, 2),
+                     "avg_launch_us": round(k3_avg_s * 1e6, 2), "launch_us": launch_stats_us(k3_ms),
                      "algorithmic_bytes_per_launch": int(kv_per_launch)},
     }
     log(f"timed {args.steps} steps: {value:.1f} GB/s; partial kernel {k3_avg_s * 1e6:.1f} us")
