@@ -149,15 +149,16 @@ int prepare_decode(const pkv_decode_args* a, pkv::DecodeParams* p, int* kind_out
   p->uniform_hint = 0;
   if (a->host_seq_lens) {
     // exact partition count from the host copy of the lengths
+    // Uniform: every sequence attends to within 1/8 of the longest one's
+    // tokens (equal static runs then carry equal work).
     int64_t sum = 0, lo = INT64_MAX, hi = 0;
     for (int32_t i = 0; i < a->num_seqs; ++i) {
       const int32_t n = a->host_seq_lens[i];
       if (n < 1 || n > a->max_seq_len) continue;
       const int32_t t0 = a->window > 0 ? std::max(0, n - a->window) : 0;
-      const int64_t P = (n - 1) / part - t0 / part + 1;
-      sum += P;
-      lo = std::min(lo, P);
-      hi = std::max(hi, P);
+      sum += (n - 1) / part - t0 / part + 1;
+      lo = std::min<int64_t>(lo, n - t0);
+      hi = std::max<int64_t>(hi, n - t0);
     }
     const int64_t hg = (p->G + 15) / 16;
     p->tasks_hint = sum * a->num_kv_heads * hg;

@@ -48,9 +48,13 @@ constexpr int kBlock = 16;   // tokens per block on the decode path
 // per-wave end times), so with equal work the younger wave streams alone for
 // the second half of a launch.  The deep variant keeps twice the bytes in
 // flight from a single wave per SIMD (the register file it needs allows no
-// second one), which has no partner to wait for; the bf16 cache uses it for
-// every batch.  The 8-bit cache does more conversion work per byte and
-// measured faster with two shallow waves per SIMD.
+// second one), which has no partner to wait for.  The bf16 cache uses it
+// for batches with at least four partitions per deep wave slot (per the
+// caller's length hint): there most bytes stream from HBM.  Smaller batches,
+// and batches whose shared prefix is read from the caches, measured as fast
+// or faster with two shallow waves per SIMD, which overlap one wave's
+// arithmetic with the other's.  The 8-bit cache does more conversion work per
+// byte and measured faster with two shallow waves per SIMD throughout.
 #ifndef PKV_DEPTH
 #define PKV_DEPTH 3
 #endif
@@ -974,14 +978,15 @@ static hipError_t launch_variant(DecodeParams p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// bf16 cache: the deep variant; 8-bit cache: the shallow one
-// (PKV_DECODE_DEEP=0/1 forces the choice).
+// bf16 cache with at least four partitions per deep wave slot: the deep
+// variant; else the shallow one (PKV_DECODE_DEEP=0/1 forces the choice).
 template <int D, bool kFp8>
 static hipError_t launch_bf16q(const DecodeParams& p, hipStream_t stream) {
   constexpr int kShallow = kFp8 ? kDepthFp8 : kDepth;
   constexpr int kDeep = kFp8 ? kDepthFp8Deep : kDepthDeep;
   static const int forced = env_int("PKV_DECODE_DEEP");
-  const bool deep = forced >= 0 ? forced > 0 : !kFp8;
+  const bool deep = forced >= 0 ? forced > 0
+                                : !kFp8 && p.tasks_hint >= 4LL * residency<D, kDeep, kFp8>().waves;
   return deep ? launch_variant<D, kDeep, kFp8>(p, stream) : launch_variant<D, kShallow, kFp8>(p, stream);
 }
 

@@ -62,7 +62,7 @@ struct DecodeParams {
   int32_t ppw;           // partitions streamed per wave (set by the launcher)
   int32_t groups;        // runs per (sequence, KV head, head group); the last takes the rest
   int64_t tasks_hint;    // exact (sequence, KV head, head group, partition) count, 0 = unknown
-  int32_t uniform_hint;  // 1 if every sequence has about the same number of partitions
+  int32_t uniform_hint;  // 1 if every sequence attends to about the same number of tokens
   float scale_log2;      // scale * log2(e): scores are kept in base-2 units
 };
 
