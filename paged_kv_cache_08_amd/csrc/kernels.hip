@@ -384,6 +384,13 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
   const int lane = threadIdx.x;
   const int c16 = lane & 15;
   const int g4 = lane >> 4;
+  // 8-bit cache, runs of several partitions: the two waves of a SIMD swap
+  // issue priority every 2^12 ticks of the 100 MHz real-time counter (41 us),
+  // so each is favoured half the time and both end together; with plain
+  // age order the older wave finishes first and the younger streams alone.
+  // (Hardware wave slot parity from HW_ID tells the two apart.)
+  const bool prio_swap = kFp8 && p.ppw > 1;
+  const unsigned slot_bit = prio_swap ? (__builtin_amdgcn_s_getreg((31 << 11) | 4) & 1) : 0;
 
   // Q^T operand of QK MFMA c: head c16, the head-dimension values that the
   // K operand's lane holds (see above).
@@ -577,6 +584,12 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
     for (; i + 2 * NBUF <= nblk; i += NBUF) {
+      if (prio_swap) {
+        if ((static_cast<unsigned>(__builtin_amdgcn_s_memrealtime() >> 12) ^ slot_bit) & 1)
+          __builtin_amdgcn_s_setprio(1);
+        else
+          __builtin_amdgcn_s_setprio(0);
+      }
 #pragma unroll
       for (int u = 0; u < NBUF; ++u) {
         compute_block(buf[u], i + u, NoTail{});
