@@ -367,32 +367,42 @@ def cpu_baseline(wl_name: str, seconds: float, window: int = 0):
     q, k, v = wl.tensors(0, device="cpu")
     rp = Replay(wl, layers=1).run(wl.setup_ops, {0: (bits(k), bits(v))})
     g = torch.Generator().manual_seed(5)
-    lengths = [int(n) - 1 for n in wl.lengths]
     q64 = to_f64(bits(q), wl.dtype)
-    steps, kv, t = 0, 0, 0.0
-    while t < seconds or steps == 0:
-        kn = torch.randn((wl.S, wl.Hkv, wl.d), generator=g).to(q.dtype)
-        vn = torch.randn((wl.S, wl.Hkv, wl.d), generator=g).to(q.dtype)
-        t0 = time.perf_counter()
-        slots, cow = rp.alloc.append(list(wl.seq_ids))
-        for a, b in cow:
-            rp.pool.copy_block(a, b)
-        rp.pool.scatter(0, slots, bits(kn), bits(vn))
-        lengths = [n + 1 for n in lengths]
-        if window:
-            for sid, n in zip(wl.seq_ids, lengths):
-                rp.alloc.release_before(sid, max(0, n - window))
-        OA.decode(rp.pool, 0, rp.tables(), lengths, q64, wl.Hq, window=window)
-        t += time.perf_counter() - t0
-        kv += sum(min(n, window) if window else n for n in lengths) * wl.Hkv * wl.kv_bytes_per_token_head()
-        steps += 1
+    state = {"lengths": [int(n) - 1 for n in wl.lengths]}
+
+    def run(budget):
+        steps, kv, t = 0, 0, 0.0
+        while t < budget or steps == 0:
+            kn = torch.randn((wl.S, wl.Hkv, wl.d), generator=g).to(q.dtype)
+            vn = torch.randn((wl.S, wl.Hkv, wl.d), generator=g).to(q.dtype)
+            t0 = time.perf_counter()
+            slots, cow = rp.alloc.append(list(wl.seq_ids))
+            for a, b in cow:
+                rp.pool.copy_block(a, b)
+            rp.pool.scatter(0, slots, bits(kn), bits(vn))
+            lengths = state["lengths"] = [n + 1 for n in state["lengths"]]
+            if window:
+                for sid, n in zip(wl.seq_ids, lengths):
+                    rp.alloc.release_before(sid, max(0, n - window))
+            OA.decode(rp.pool, 0, rp.tables(), lengths, q64, wl.Hq, window=window)
+            t += time.perf_counter() - t0
+            kv += sum(min(n, window) if window else n for n in lengths) * wl.Hkv * wl.kv_bytes_per_token_head()
+            steps += 1
+        return steps, kv, t
+
+    steps, kv, t = run(seconds)
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = 1
+        with threadpool_limits(limits=1):
+            steps1, kv1, t1 = run(seconds / 3)
+        single = {"value": kv1 / t1 / 1e9, "cores": 1, "sample": f"{steps1} decode steps, {t1:.1f} s",
+                  "tokens_per_s": wl.S * steps1 / t1}
+    except ImportError:
+        cores, single = 1, None
     return {"value": kv / t / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{sample}; {steps} decode steps, {t:.1f} s", "tokens_per_s": wl.S * steps / t}
+            "sample": f"{sample}; {steps} decode steps, {t:.1f} s", "tokens_per_s": wl.S * steps / t,
+            "single_thread": single}
 
 
 def load_traffic(workload: str):
