@@ -443,21 +443,32 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
   const int bpp = p.partition / kBlock;        // blocks per partition
   int next_boundary = boundary0;               // block count that closes a partition
   int staged_parts = 0;
-  const int row_floats = D + 2;                // staged row: accumulator, m, l
+  // Staged partitions in LDS: accumulator rows [partition][head][D] (16-byte
+  // aligned, so staging and copying out move 16 bytes per lane), then (m, l)
+  // pairs [partition][head][2].
+  const int n_stage = part_end - part0 - 1;
+  float* staged_ml = staged + n_stage * nh * D;
 
   // Closes a partition that is not the wave's last: park (acc, m, l) in LDS
   // and restart the running statistics.
   auto stage_partition = [&]() {
     const float l_tot = sum_over_rows(l_run);
     if (c16 < nh) {
-      float* dst = staged + (staged_parts * nh + c16) * row_floats;
+      float* dst = staged + (staged_parts * nh + c16) * D;
+      if constexpr (kFp8) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+        for (int a = 0; a < D / 64; ++a)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dst[acc_column<kFp8>(t, j, g4)] = acc[t][j];
+          for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<f32x4*>(dst + acc_column<true>(4 * a, j, g4)) =
+                f32x4{acc[4 * a][j], acc[4 * a + 1][j], acc[4 * a + 2][j], acc[4 * a + 3][j]};
+      } else {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4*>(dst + acc_column<false>(t, 0, g4)) = acc[t];
+      }
       if (g4 == 0) {
-        dst[D] = m_run;
-        dst[D + 1] = l_tot;
+        staged_ml[2 * (staged_parts * nh + c16)] = m_run;
+        staged_ml[2 * (staged_parts * nh + c16) + 1] = l_tot;
       }
     }
 #pragma unroll
@@ -615,16 +626,20 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
   const float l_tot = sum_over_rows(l_run);
   if (staged_parts > 0) {
     // (LDS accesses of one wave complete in order: no barrier is needed.)
-    for (int sp = 0; sp < staged_parts; ++sp)
-      for (int h = 0; h < nh; ++h) {
-        const float* src = staged + (sp * nh + h) * row_floats;
-        const size_t row = (static_cast<size_t>(s_) * p.Hq + h0 + h) * p.pmax + part0 + sp;
-        for (int e = lane; e < D; e += 64) p.part_acc[row * D + e] = src[e];
-        if (lane == 0) {
-          p.part_ml[2 * row] = src[D];
-          p.part_ml[2 * row + 1] = src[D + 1];
-        }
+    // Lane l moves 16-byte chunks l, l + 64, ... of the nh accumulator rows.
+    const size_t row0 = (static_cast<size_t>(s_) * p.Hq + h0) * p.pmax + part0;
+    for (int sp = 0; sp < staged_parts; ++sp) {
+      for (int c = lane; c < nh * (D / 4); c += 64) {
+        const int h = c / (D / 4), e = (c % (D / 4)) * 4;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(staged + (sp * nh + h) * D + e);
+        *reinterpret_cast<f32x4*>(p.part_acc + (row0 + static_cast<size_t>(h) * p.pmax + sp) * D + e) = v;
       }
+      if (lane < nh) {
+        const size_t row = row0 + static_cast<size_t>(lane) * p.pmax + sp;
+        p.part_ml[2 * row] = staged_ml[2 * (sp * nh + lane)];
+        p.part_ml[2 * row + 1] = staged_ml[2 * (sp * nh + lane) + 1];
+      }
+    }
   }
   if (c16 >= nh) return;
   const size_t head_row = static_cast<size_t>(s_) * p.Hq + h0 + c16;
