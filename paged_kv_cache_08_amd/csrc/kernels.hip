@@ -246,8 +246,14 @@ __device__ __forceinline__ void write_nan_partials(const DecodeParams& p, const 
 // Decodes blockIdx into the wave's task, loads its block ids and validates
 // lengths and table entries.  Returns false when the wave has nothing to do
 // (after writing NaN results for an invalid sequence).
-template <typename T, int D>
-__device__ __forceinline__ bool setup_task(const DecodeParams& p, WaveTask& w) {
+// Without a window a task's first block does not depend on the length, so
+// its block ids are requested together with the length: one round trip, not
+// two, precedes the first block load.  The early ids are checked once the
+// length is known.  issue_q(w) requests the queries once the task is known
+// to be non-empty (a grid sized for the longest sequence holds many empty
+// tasks in mixed batches), so they travel with the first block loads.
+template <typename T, int D, typename IssueQ>
+__device__ __forceinline__ bool setup_task(const DecodeParams& p, WaveTask& w, IssueQ&& issue_q) {
   const int lane = threadIdx.x;
   w.kvh = blockIdx.x % p.Hkv;
   const int rest = blockIdx.x / p.Hkv;
@@ -256,6 +262,18 @@ __device__ __forceinline__ bool setup_task(const DecodeParams& p, WaveTask& w) {
   w.h0 = w.kvh * p.G + blockIdx.y * 16;
   w.nh = min(16, p.G - static_cast<int>(blockIdx.y) * 16);
   w.n = p.seq_lens[w.s];
+  const int bpp = p.partition / kBlock;
+  const bool early = p.window == 0;
+  const int early_first = grp * p.ppw * bpp;                   // = blk_first when there is no window
+  // blocks the task can hold: its run, or for the last group everything after it
+  const int early_lim = min((grp == p.groups - 1 ? p.pmax - grp * p.ppw : p.ppw) * bpp, p.max_blocks - early_first);
+  int ids[5] = {0, 0, 0, 0, 0};
+  {
+    const int32_t* row = p.block_tables + static_cast<size_t>(w.s) * p.max_blocks + early_first;
+#pragma unroll
+    for (int c = 0; c < 5; ++c)
+      if (early && 64 * c < early_lim && 64 * c + lane < early_lim) ids[c] = row[64 * c + lane];
+  }
   if (w.n < 1 || w.n > p.max_seq_len) {
     if (grp == 0) write_nan_rows<T, D>(p, w.s, w.h0, w.nh);
     return false;
@@ -264,6 +282,7 @@ __device__ __forceinline__ bool setup_task(const DecodeParams& p, WaveTask& w) {
   window_partitions(p, w.n, t0, pf, w.P);
   w.part0 = grp * p.ppw;
   if (w.part0 >= w.P) return false;
+  issue_q(w);
   w.part_end = grp == p.groups - 1 ? w.P : min(w.P, w.part0 + p.ppw);
   w.t_lo = max(t0, (pf + w.part0) * p.partition);
   w.t_end = min(w.n, (pf + w.part_end) * p.partition);
@@ -276,7 +295,7 @@ __device__ __forceinline__ bool setup_task(const DecodeParams& p, WaveTask& w) {
   auto fetch = [&](int c) {
     const int idx = 64 * c + lane;
     int b = 0;
-    if (!bad && idx < w.nblk) b = row[idx];
+    if (!bad && idx < w.nblk) b = early ? ids[c] : row[idx];
     const bool bl = static_cast<unsigned>(b) >= static_cast<unsigned>(p.num_blocks);
     bad_lane = bad_lane || bl;
     return bl ? 0 : b;
@@ -373,17 +392,30 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
   // stream ends: a global store in the middle of the stream would make every
   // later wait drain all loads in flight (stores and loads share vmcnt).
   extern __shared__ float staged[];
+  const int lane = threadIdx.x;
+  const int c16 = lane & 15;
+  const int g4 = lane >> 4;
+  // Q^T operand of QK MFMA c: head c16, the head-dimension values that the
+  // K operand's lane holds (see above).  Requested during the task set-up.
+  bf16x8 qreg[KC];
+  auto issue_q = [&](const WaveTask& wt) {
+    const __bf16* q = static_cast<const __bf16*>(p.q) + (static_cast<size_t>(wt.s) * p.Hq + wt.h0 + c16) * D;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const int off = kFp8 ? 64 * (c >> 1) + 16 * g4 + 8 * (c & 1) : 32 * c + 8 * g4;
+      u32x4 v = {0, 0, 0, 0};
+      if (c16 < wt.nh) v = *reinterpret_cast<const u32x4*>(q + off);
+      qreg[c] = __builtin_bit_cast(bf16x8, v);
+    }
+  };
   int s_, kvh, h0, nh, P, part0, part_end, t_lo, t_end, blk_first, nblk, boundary0, id0, id1, id2, id3, id4;
   {
     WaveTask w;
-    if (!setup_task<__bf16, D>(p, w)) return;
+    if (!setup_task<__bf16, D>(p, w, issue_q)) return;
     s_ = w.s; kvh = w.kvh; h0 = w.h0; nh = w.nh; P = w.P; part0 = w.part0; part_end = w.part_end;
     t_lo = w.t_lo; t_end = w.t_end; blk_first = w.blk_first; nblk = w.nblk; boundary0 = w.boundary0;
     id0 = w.id0; id1 = w.id1; id2 = w.id2; id3 = w.id3; id4 = w.id4;
   }
-  const int lane = threadIdx.x;
-  const int c16 = lane & 15;
-  const int g4 = lane >> 4;
   // 8-bit cache, runs of several partitions: the two waves of a SIMD swap
   // issue priority every 2^12 ticks of the 100 MHz real-time counter (41 us),
   // so each is favoured half the time and both end together; with plain
@@ -391,20 +423,6 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
   // (Hardware wave slot parity from HW_ID tells the two apart.)
   const bool prio_swap = kFp8 && p.ppw > 1;
   const unsigned slot_bit = prio_swap ? (__builtin_amdgcn_s_getreg((31 << 11) | 4) & 1) : 0;
-
-  // Q^T operand of QK MFMA c: head c16, the head-dimension values that the
-  // K operand's lane holds (see above).
-  bf16x8 qreg[KC];
-  {
-    const __bf16* q = static_cast<const __bf16*>(p.q) + (static_cast<size_t>(s_) * p.Hq + h0 + c16) * D;
-#pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      const int off = kFp8 ? 64 * (c >> 1) + 16 * g4 + 8 * (c & 1) : 32 * c + 8 * g4;
-      u32x4 v = {0, 0, 0, 0};
-      if (c16 < nh) v = *reinterpret_cast<const u32x4*>(q + off);
-      qreg[c] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
 
   const size_t tile_bytes = static_cast<size_t>(kBlock) * D * ELEM;  // one (block, head) tile
   const size_t blk_bytes = static_cast<size_t>(p.Hkv) * tile_bytes;
@@ -700,7 +718,7 @@ __global__ __launch_bounds__(64) void decode_partial_f32(DecodeParams p) {
   int s_, kvh, h0, nh, P, part0, t_lo, t_end, blk_first, nblk, id0, id1, id2, id3, id4;
   {
     WaveTask w;
-    if (!setup_task<float, D>(p, w)) return;
+    if (!setup_task<float, D>(p, w, [](const WaveTask&) {})) return;
     s_ = w.s; kvh = w.kvh; h0 = w.h0; nh = w.nh; P = w.P; part0 = w.part0;
     t_lo = w.t_lo; t_end = w.t_end; blk_first = w.blk_first; nblk = w.nblk;
     id0 = w.id0; id1 = w.id1; id2 = w.id2; id3 = w.id3; id4 = w.id4;
