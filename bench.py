@@ -52,6 +52,9 @@ def parse():
                     help="sliding window: attend to the last W positions and release older blocks each step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--flush", action="store_true",
+                    help="write a 1 GiB buffer before every decode step, outside its timing, to evict L2 and the "
+                         "MALL; value and step time then come from events around each step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 1 GiB device copies (known bytes) for counter scaling")
     return ap.parse_args()
@@ -147,6 +150,13 @@ class DecodeBench:
         self.step_idx = 0
         self.kv_bytes = []            # attention KV bytes of each step (all layers)
         self.events = []              # (k3 start, k3 end) per layer per step
+        self.step_events = []         # (step start, step end) when the caches are flushed
+        self.flush = None
+
+    def enable_flush(self, nbytes: int = 1 << 30):
+        """Before each step, write nbytes on the main stream (a fill kernel),
+        more than L2 and the 256 MB MALL together hold."""
+        self.flush = self.torch.empty(nbytes, dtype=self.torch.uint8, device=self.dev)
 
     def step(self, record_events: bool):
         P, torch = self.P, self.torch
@@ -154,6 +164,8 @@ class DecodeBench:
         b = j % 2
         side = self.side
         side.wait_event(self.done[b])        # the step that last used these tables has finished
+        if self.flush is not None:
+            self.flush.fill_(j & 0xFF)
         slots, cow = P.pkv_append_slots(self.eng.pool, self.ids)
         for i in range(len(self.lengths)):
             self.lengths[i] += 1
@@ -166,6 +178,9 @@ class DecodeBench:
         P.pkv_sync_tables(self.eng.pool, self.ids, self.tables[b], self.lens[b], self.eng.host_lens, side)
         self.ready[b].record(side)
         self.main.wait_event(self.ready[b])
+        if self.flush is not None and record_events:
+            s0 = torch.cuda.Event(enable_timing=True)
+            s0.record(self.main)
         if cow:
             P.pkv_copy_blocks(self.eng.pool, cow)
         for l in range(self.layers):
@@ -180,6 +195,10 @@ class DecodeBench:
                 self.events.append((e0, e1))
             P.pkv_paged_decode_reduce(self.args[b][l])
         self.done[b].record(self.main)
+        if self.flush is not None and record_events:
+            s1 = torch.cuda.Event(enable_timing=True)
+            s1.record(self.main)
+            self.step_events.append((s0, s1))
         wl = self.wl
         attended = sum(min(n, self.window) if self.window else n for n in self.lengths)
         self.kv_bytes.append(attended * wl.Hkv * wl.kv_bytes_per_token_head() * self.layers)
@@ -453,6 +472,8 @@ def main():
     total = args.warmup + args.steps
     log(f"setup {wl.description}")
     bench = DecodeBench(wl, total, partition=args.partition, window=args.window)
+    if args.flush:
+        bench.enable_flush()
     log("setup done; warmup")
     for _ in range(args.warmup):
         bench.step(record_events=False)
@@ -466,6 +487,8 @@ def main():
     elapsed = time.perf_counter() - t0
 
     kv_total = sum(bench.kv_bytes)
+    if args.flush:      # the flush writes are not part of the step
+        elapsed = sum(a.elapsed_time(b) for a, b in bench.step_events) / 1e3
     value = kv_total / elapsed / 1e9
     k3_ms = [a.elapsed_time(b) for a, b in bench.events]
     k3_avg_s = sum(k3_ms) / len(k3_ms) / 1e3
@@ -489,7 +512,7 @@ def main():
         "config": {"workload": wl.name, "description": wl.description, "kv_cache": wl.cache_dtype,
                    "layers": wl.layers,
                    "S": wl.S, "Hq": wl.Hq, "Hkv": wl.Hkv, "d": wl.d, "block": wl.block,
-                   "partition": args.partition or 512, "window": args.window,
+                   "partition": args.partition or 512, "window": args.window, "cache_flush": args.flush,
                    "start_lengths_mean": float(wl.lengths.mean())},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(wl.S * args.steps / elapsed, 1),
