@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpkv.so")
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["block_pool.cpp", "capi.cpp", "kernels.hip", "prefill.hip"]
+SOURCES = ["block_pool.cpp", "capi.cpp", "kernels.hip", "prefill.hip", "calibrate.hip"]
 
 
 def hipcc() -> str:

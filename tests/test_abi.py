@@ -159,3 +159,18 @@ def test_prefill_argument_validation(bad, status):
     with pytest.raises(P.PkvError) as e:
         P.pkv_paged_prefill(_prefill_args(**bad), stream=0)
     assert e.value.status == status
+
+
+@pytest.mark.parametrize("args", [
+    (0, 1 << 20, 0, 16, 1, 16),             # null buffer
+    (16, 1 << 20, 0, 16, 1, 0),             # null sink
+    (16, 4095, 0, 1, 1, 16),                # buffer smaller than one tile
+    (16, 1 << 20, 0, 0, 1, 16),             # no tiles
+    (16, 1 << 20, 0, 16, 0, 16),            # tiles_per_wave < 1
+    (8, 1 << 20, 0, 16, 1, 16),             # misaligned buffer
+    (16, 1 << 20, 0, 257, 1, 16),           # contiguous read past the buffer (256 tiles)
+])
+def test_read_tiles_argument_validation(args):
+    base, nbytes, order, n, tpw, sink = args
+    status = P.lib().pkv_read_tiles(base, nbytes, order, n, tpw, sink, 0)
+    assert status == P.PKV_ERR_INVALID
