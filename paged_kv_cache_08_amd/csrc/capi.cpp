@@ -7,6 +7,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <array>
 #include <climits>
 #include <cmath>
 #include <cstring>
@@ -175,6 +176,53 @@ int prepare_decode(const pkv_decode_args* a, pkv::DecodeParams* p, int* kind_out
   }
   *kind_out = kind;
   return PKV_OK;
+}
+
+// Longest-first dispatch order for the partial kernel (DecodeOrder), from
+// the host length hint: without a window, for up to kOrderMaxSeqs sequences
+// and kOrderMaxGroups partitions.  Lengths outside [1, max_seq_len] count as
+// empty.  Whatever the hint holds, the tables describe a bijection on the
+// grid's (partition, sequence) cells.
+void build_order(const pkv_decode_args* a, pkv::DecodeParams* p) {
+  pkv::DecodeOrder& o = p->order;
+  o.active = 0;
+  if (!a->host_seq_lens || a->window > 0 || p->S > pkv::kOrderMaxSeqs || p->pmax > pkv::kOrderMaxGroups) return;
+  const int S = p->S, groups = p->pmax, part = p->partition;
+  std::array<int32_t, pkv::kOrderMaxSeqs> n{};
+  std::array<int32_t, pkv::kOrderMaxSeqs> rank_seq{};
+  for (int i = 0; i < S; ++i) {
+    const int32_t v = a->host_seq_lens[i];
+    n[i] = v >= 1 && v <= a->max_seq_len ? v : 0;
+    rank_seq[i] = i;
+  }
+  std::stable_sort(rank_seq.begin(), rank_seq.begin() + S, [&](int x, int y) { return n[x] > n[y]; });
+  std::array<int32_t, pkv::kOrderMaxGroups> full{}, live{};     // per group: ranks with a full / any partition
+  std::array<int32_t, pkv::kOrderMaxSeqs> partial_rank{};
+  int n_partial = 0;
+  for (int r = 0; r < S; ++r) {
+    const int32_t len = n[rank_seq[r]];
+    const int f = len / part;                      // full partitions
+    const int np = (len + part - 1) / part;        // all partitions
+    for (int g = 0; g < f; ++g) ++full[g];
+    for (int g = 0; g < np; ++g) ++live[g];
+    if (np > f) partial_rank[n_partial++] = r;
+    o.rank_seq[r] = static_cast<uint16_t>(rank_seq[r]);
+  }
+  std::stable_sort(partial_rank.begin(), partial_rank.begin() + n_partial,
+                   [&](int x, int y) { return n[rank_seq[x]] % part > n[rank_seq[y]] % part; });
+  for (int j = 0; j < n_partial; ++j) {
+    const int r = partial_rank[j];
+    o.partial[j] = static_cast<uint16_t>(r | (n[rank_seq[r]] / part) << 9);
+  }
+  o.full_start[0] = 0;
+  o.rest_start[0] = 0;
+  for (int g = 0; g < groups; ++g) {
+    o.full_start[g + 1] = o.full_start[g] + full[g];
+    o.rest_start[g + 1] = o.rest_start[g] + (S - live[g]);
+  }
+  o.n_full = o.full_start[groups];
+  o.n_partial = n_partial;
+  o.active = 1;
 }
 
 }  // namespace
@@ -591,6 +639,7 @@ int pkv_paged_decode_partial(const pkv_decode_args* a, void* stream) {
   int kind = 0;
   const int rc = prepare_decode(a, &p, &kind);
   if (rc) return rc;
+  build_order(a, &p);
   return from_hip(pkv::launch_decode_partial(p, kind, static_cast<hipStream_t>(stream)), "decode_partial");
 }
 
@@ -607,6 +656,7 @@ int pkv_paged_attention_decode(const pkv_decode_args* a, void* stream) {
   int kind = 0;
   int rc = prepare_decode(a, &p, &kind);
   if (rc) return rc;
+  build_order(a, &p);
   hipStream_t st = static_cast<hipStream_t>(stream);
   rc = from_hip(pkv::launch_decode_partial(p, kind, st), "decode_partial");
   if (rc) return rc;

@@ -252,13 +252,42 @@ __device__ __forceinline__ void write_nan_partials(const DecodeParams& p, const 
 // length is known.  issue_q(w) requests the queries once the task is known
 // to be non-empty (a grid sized for the longest sequence holds many empty
 // tasks in mixed batches), so they travel with the first block loads.
+// Grid cell k (of S * groups) relabelled by the host-built dispatch order
+// (longest work first; a bijection on the cells).
+__device__ __forceinline__ void ordered_cell(const DecodeOrder& o, int S, int k, int& grp, int& s) {
+  int rank;
+  if (k < o.n_full) {
+    int g = 0;
+    while (g < kOrderMaxGroups - 1 && o.full_start[g + 1] <= k) ++g;
+    grp = g;
+    rank = k - o.full_start[g];
+  } else if (k < o.n_full + o.n_partial) {
+    const int e = o.partial[k - o.n_full];
+    rank = e & 511;
+    grp = e >> 9;
+  } else {
+    const int j = k - o.n_full - o.n_partial;
+    int g = 0;
+    while (g < kOrderMaxGroups - 1 && o.rest_start[g + 1] <= j) ++g;
+    grp = g;
+    rank = S - (o.rest_start[g + 1] - o.rest_start[g]) + (j - o.rest_start[g]);
+  }
+  s = o.rank_seq[rank];
+}
+
 template <typename T, int D, typename IssueQ>
 __device__ __forceinline__ bool setup_task(const DecodeParams& p, WaveTask& w, IssueQ&& issue_q) {
   const int lane = threadIdx.x;
   w.kvh = blockIdx.x % p.Hkv;
   const int rest = blockIdx.x / p.Hkv;
-  w.s = rest % p.S;
-  const int grp = rest / p.S;
+  int grp;
+  if (p.order.active) {
+    ordered_cell(p.order, p.S, rest, grp, w.s);
+    if (static_cast<unsigned>(w.s) >= static_cast<unsigned>(p.S)) return false;   // only if the tables were bad
+  } else {
+    w.s = rest % p.S;
+    grp = rest / p.S;
+  }
   w.h0 = w.kvh * p.G + blockIdx.y * 16;
   w.nh = min(16, p.G - static_cast<int>(blockIdx.y) * 16);
   w.n = p.seq_lens[w.s];
@@ -1007,10 +1036,26 @@ static int longest_run(const DecodeParams& p) {
   return std::max(p.ppw, p.pmax - (p.groups - 1) * p.ppw);
 }
 
+// The longest-first order relabels cells of one partition each; runs keep
+// the plain order.  It pays when the batch's tasks fill at most about two
+// rounds of the `waves` resident waves: then the tail is what costs, and
+// longest-first shortens it.  With many rounds the plain order is faster:
+// sequences of mixed length keep short tasks (whose time is mostly setup
+// latency) beside long ones (which keep memory busy) in every round, while
+// longest-first runs equal full partitions in lockstep and leaves the short
+// tasks to the end, where they cannot keep memory busy.  PKV_DECODE_ORDER=0
+// switches it off, =1 on whenever it applies.
+static void settle_order(DecodeParams& p, int waves) {
+  static const int forced = env_int("PKV_DECODE_ORDER");
+  const bool fits = forced > 0 || (p.tasks_hint > 0 && p.tasks_hint <= 2LL * waves);
+  if (p.ppw != 1 || p.groups != p.pmax || forced == 0 || !fits) p.order.active = 0;
+}
+
 template <int D, int NBUF, bool kFp8>
 static hipError_t launch_variant(DecodeParams p, hipStream_t stream) {
   const Residency& r = residency<D, NBUF, kFp8>();
   set_runs(p, r);
+  settle_order(p, r.waves);
   dim3 grid(static_cast<unsigned>(static_cast<long long>(p.groups) * p.S * p.Hkv), (p.G + 15) / 16);
   const size_t shmem =
       static_cast<size_t>(longest_run(p) - 1) * std::min(16, p.G) * (p.d + 2) * sizeof(float);
@@ -1018,8 +1063,8 @@ static hipError_t launch_variant(DecodeParams p, hipStream_t stream) {
   static std::atomic<bool> traced{false};
   if (trace > 0 && !traced.exchange(true))
     std::fprintf(stderr, "decode_partial<d=%d, depth=%d, fp8=%d>: %d resident waves, %d B LDS each; ppw=%d, "
-                 "grid=%ux%u, %zu B LDS\n", D, NBUF, kFp8 ? 1 : 0, r.waves, r.lds_per_wave, p.ppw, grid.x, grid.y,
-                 shmem);
+                 "grid=%ux%u, %zu B LDS, longest-first order %d\n", D, NBUF, kFp8 ? 1 : 0, r.waves, r.lds_per_wave,
+                 p.ppw, grid.x, grid.y, shmem, p.order.active);
   hipLaunchKernelGGL((decode_partial_bf16<D, NBUF, kFp8>), grid, dim3(64), shmem, stream, p);
   return hipGetLastError();
 }
@@ -1050,6 +1095,7 @@ hipError_t launch_decode_partial(const DecodeParams& p0, int kind, hipStream_t s
     case kDecodeF32: {
       p.ppw = 1;
       p.groups = p.pmax;
+      p.order.active = 0;
       dim3 grid(static_cast<unsigned>(static_cast<long long>(p.pmax) * p.S * p.Hkv), (p.G + 15) / 16);
       if (p.d == 128) hipLaunchKernelGGL(decode_partial_f32<128>, grid, dim3(64), 0, stream, p);
       else if (p.d == 64) hipLaunchKernelGGL(decode_partial_f32<64>, grid, dim3(64), 0, stream, p);

@@ -44,6 +44,29 @@ struct AppendParams {
   float* v_scale;
 };
 
+// Dispatch order of a decode launch with one partition per wave, built on
+// the host from the caller's length hint: longest work first.  The grid's
+// cells (partition index g, sequence) are relabelled by a bijection, so every
+// cell is still visited exactly once whatever the hint says; each wave then
+// takes its task from the device length as usual.  Ranks number the
+// sequences longest first.  Wave k (of the S * groups cells) takes, in order:
+//  - the full partitions: cells k < full_start[groups], group-major, ranks
+//    0 .. (full_start[g+1] - full_start[g]) - 1 of group g;
+//  - the partial last partitions, largest remainder first: partial[j] =
+//    rank | g << 9 for j < n_partial;
+//  - the remaining cells (empty by the hint): group g takes ranks
+//    S - (rest_start[g+1] - rest_start[g]) .. S - 1.
+constexpr int kOrderMaxSeqs = 512;
+constexpr int kOrderMaxGroups = 64;
+struct DecodeOrder {
+  int32_t active;
+  int32_t n_full, n_partial;
+  int32_t full_start[kOrderMaxGroups + 1];
+  int32_t rest_start[kOrderMaxGroups + 1];
+  uint16_t rank_seq[kOrderMaxSeqs];     // sequence of each rank
+  uint16_t partial[kOrderMaxSeqs];
+};
+
 struct DecodeParams {
   const void* q;
   void* out;
@@ -64,6 +87,7 @@ struct DecodeParams {
   int64_t tasks_hint;    // exact (sequence, KV head, head group, partition) count, 0 = unknown
   int32_t uniform_hint;  // 1 if every sequence attends to about the same number of tokens
   float scale_log2;      // scale * log2(e): scores are kept in base-2 units
+  DecodeOrder order;     // used by the partial kernel when order.active and ppw == 1
 };
 
 struct PrefillParams {
