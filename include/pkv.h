@@ -291,9 +291,10 @@ typedef struct pkv_decode_args {
   int32_t dtype;              /* PKV_F32 or PKV_BF16: q and out             */
   float scale;                /* score scale, e.g. 1/sqrt(d)                */
   const int32_t* host_seq_lens; /* optional host copy of seq_lens [S], read */
-                              /*   only to choose how partitions are spread */
-                              /*   over waves; NULL = unknown (results do   */
-                              /*   not depend on it)                        */
+                              /*   only to plan the launch (which waves,    */
+                              /*   how many partitions each); NULL =        */
+                              /*   unknown.  Results do not depend on it,   */
+                              /*   even when it is wrong or stale.          */
   const float* k_scale;       /* 8-bit cache: device scales of this layer,  */
   const float* v_scale;       /*   fp32 [num_blocks][Hkv][B]; else unused   */
   int32_t kv_dtype;           /* cache type: equal to dtype, or             */

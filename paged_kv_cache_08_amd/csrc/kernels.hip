@@ -30,6 +30,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <climits>
 #include <cmath>
 #include <cstdio>
 #include <cstdint>
@@ -252,50 +253,43 @@ __device__ __forceinline__ void write_nan_partials(const DecodeParams& p, const 
 // length is known.  issue_q(w) requests the queries once the task is known
 // to be non-empty (a grid sized for the longest sequence holds many empty
 // tasks in mixed batches), so they travel with the first block loads.
-// Grid cell k (of S * groups) relabelled by the host-built dispatch order
-// (longest work first; a bijection on the cells).
-__device__ __forceinline__ void ordered_cell(const DecodeOrder& o, int S, int k, int& grp, int& s) {
-  int rank;
-  if (k < o.n_full) {
-    int g = 0;
-    while (g < kOrderMaxGroups - 1 && o.full_start[g + 1] <= k) ++g;
-    grp = g;
-    rank = k - o.full_start[g];
-  } else if (k < o.n_full + o.n_partial) {
-    const int e = o.partial[k - o.n_full];
-    rank = e & 511;
-    grp = e >> 9;
-  } else {
-    const int j = k - o.n_full - o.n_partial;
-    int g = 0;
-    while (g < kOrderMaxGroups - 1 && o.rest_start[g + 1] <= j) ++g;
-    grp = g;
-    rank = S - (o.rest_start[g + 1] - o.rest_start[g]) + (j - o.rest_start[g]);
-  }
-  s = o.rank_seq[rank];
-}
-
 template <typename T, int D, typename IssueQ>
 __device__ __forceinline__ bool setup_task(const DecodeParams& p, WaveTask& w, IssueQ&& issue_q) {
   const int lane = threadIdx.x;
   w.kvh = blockIdx.x % p.Hkv;
-  const int rest = blockIdx.x / p.Hkv;
-  int grp;
+  const int cell = blockIdx.x / p.Hkv;
+  // The wave's partitions: [part0, part_lim), clipped below to the device
+  // length.
+  int part0, part_lim;
   if (p.order.active) {
-    ordered_cell(p.order, p.S, rest, grp, w.s);
-    if (static_cast<unsigned>(w.s) >= static_cast<unsigned>(p.S)) return false;   // only if the tables were bad
+    const DecodeOrder& o = p.order;
+    if (cell < o.n_list) {
+      const int e = o.list[cell];
+      w.s = e & 511;
+      part0 = e >> 9;
+      part_lim = part0 == o.hinted[w.s] - 1 ? part0 + o.run_cap : part0 + 1;
+    } else {
+      const int j = cell - o.n_list;
+      w.s = j % p.S;
+      const int c = o.sweep_c0 + j / p.S;
+      part0 = max(c * o.run_cap, o.hinted[w.s] - 1 + o.run_cap);
+      part_lim = (c + 1) * o.run_cap;
+      if (part0 >= part_lim || part0 >= p.pmax) return false;     // the hint's cells cover it
+    }
   } else {
-    w.s = rest % p.S;
-    grp = rest / p.S;
+    w.s = cell % p.S;
+    const int grp = cell / p.S;
+    part0 = grp * p.ppw;
+    part_lim = grp == p.groups - 1 ? p.pmax : part0 + p.ppw;     // the last run takes the rest
   }
+  part_lim = min(part_lim, p.pmax);
   w.h0 = w.kvh * p.G + blockIdx.y * 16;
   w.nh = min(16, p.G - static_cast<int>(blockIdx.y) * 16);
   w.n = p.seq_lens[w.s];
   const int bpp = p.partition / kBlock;
   const bool early = p.window == 0;
-  const int early_first = grp * p.ppw * bpp;                   // = blk_first when there is no window
-  // blocks the task can hold: its run, or for the last group everything after it
-  const int early_lim = min((grp == p.groups - 1 ? p.pmax - grp * p.ppw : p.ppw) * bpp, p.max_blocks - early_first);
+  const int early_first = part0 * bpp;                         // = blk_first when there is no window
+  const int early_lim = min((part_lim - part0) * bpp, p.max_blocks - early_first);   // blocks the run can hold
   int ids[5] = {0, 0, 0, 0, 0};
   {
     const int32_t* row = p.block_tables + static_cast<size_t>(w.s) * p.max_blocks + early_first;
@@ -304,15 +298,15 @@ __device__ __forceinline__ bool setup_task(const DecodeParams& p, WaveTask& w, I
       if (early && 64 * c < early_lim && 64 * c + lane < early_lim) ids[c] = row[64 * c + lane];
   }
   if (w.n < 1 || w.n > p.max_seq_len) {
-    if (grp == 0) write_nan_rows<T, D>(p, w.s, w.h0, w.nh);
+    if (part0 == 0) write_nan_rows<T, D>(p, w.s, w.h0, w.nh);   // exactly one wave per row starts at 0
     return false;
   }
   int t0, pf;
   window_partitions(p, w.n, t0, pf, w.P);
-  w.part0 = grp * p.ppw;
+  w.part0 = part0;
   if (w.part0 >= w.P) return false;
   issue_q(w);
-  w.part_end = grp == p.groups - 1 ? w.P : min(w.P, w.part0 + p.ppw);
+  w.part_end = min(w.P, part_lim);
   w.t_lo = max(t0, (pf + w.part0) * p.partition);
   w.t_end = min(w.n, (pf + w.part_end) * p.partition);
   w.blk_first = w.t_lo / kBlock;
@@ -1036,35 +1030,41 @@ static int longest_run(const DecodeParams& p) {
   return std::max(p.ppw, p.pmax - (p.groups - 1) * p.ppw);
 }
 
-// The longest-first order relabels cells of one partition each; runs keep
-// the plain order.  It pays when the batch's tasks fill at most about two
-// rounds of the `waves` resident waves: then the tail is what costs, and
-// longest-first shortens it.  With many rounds the plain order is faster:
-// sequences of mixed length keep short tasks (whose time is mostly setup
-// latency) beside long ones (which keep memory busy) in every round, while
-// longest-first runs equal full partitions in lockstep and leaves the short
-// tasks to the end, where they cannot keep memory busy.  PKV_DECODE_ORDER=0
-// switches it off, =1 on whenever it applies.
-static void settle_order(DecodeParams& p, int waves) {
+// The host's work list (one partition per wave) replaces the plain grid of
+// every (partition, sequence) cell up to max_seq_len: in a batch of mixed
+// lengths most of those cells are empty, and each empty wave still holds a
+// wave slot for a round trip to read its length.  Here the launcher fixes the
+// run capacity (the last hinted cell of a sequence and the sweep cells may
+// take several partitions) and the sweep chunks, and returns the grid's cell
+// count.  PKV_DECODE_ORDER=0 keeps the plain grid.
+static long long settle_order(DecodeParams& p, const Residency& r) {
   static const int forced = env_int("PKV_DECODE_ORDER");
-  const bool fits = forced > 0 || (p.tasks_hint > 0 && p.tasks_hint <= 2LL * waves);
-  if (p.ppw != 1 || p.groups != p.pmax || forced == 0 || !fits) p.order.active = 0;
+  DecodeOrder& o = p.order;
+  if (p.ppw != 1 || p.groups != p.pmax || forced == 0) o.active = 0;
+  if (!o.active) return static_cast<long long>(p.groups) * p.S;
+  o.run_cap = max_run(p, r);
+  int covered = INT_MAX;                 // every sequence's partitions below this have a listed wave
+  for (int s = 0; s < p.S; ++s) covered = std::min(covered, o.hinted[s] - 1 + o.run_cap);
+  o.sweep_c0 = covered / o.run_cap;
+  o.sweep_chunks = std::max(0, (p.pmax + o.run_cap - 1) / o.run_cap - o.sweep_c0);
+  return o.n_list + static_cast<long long>(p.S) * o.sweep_chunks;
 }
 
 template <int D, int NBUF, bool kFp8>
 static hipError_t launch_variant(DecodeParams p, hipStream_t stream) {
   const Residency& r = residency<D, NBUF, kFp8>();
   set_runs(p, r);
-  settle_order(p, r.waves);
-  dim3 grid(static_cast<unsigned>(static_cast<long long>(p.groups) * p.S * p.Hkv), (p.G + 15) / 16);
-  const size_t shmem =
-      static_cast<size_t>(longest_run(p) - 1) * std::min(16, p.G) * (p.d + 2) * sizeof(float);
+  const long long cells = settle_order(p, r);
+  dim3 grid(static_cast<unsigned>(cells * p.Hkv), (p.G + 15) / 16);
+  const int longest = p.order.active ? p.order.run_cap : longest_run(p);
+  const size_t shmem = static_cast<size_t>(longest - 1) * std::min(16, p.G) * (p.d + 2) * sizeof(float);
   static const int trace = env_int("PKV_TRACE_SCHEDULE");   // print the first choice of each variant
   static std::atomic<bool> traced{false};
   if (trace > 0 && !traced.exchange(true))
     std::fprintf(stderr, "decode_partial<d=%d, depth=%d, fp8=%d>: %d resident waves, %d B LDS each; ppw=%d, "
-                 "grid=%ux%u, %zu B LDS, longest-first order %d\n", D, NBUF, kFp8 ? 1 : 0, r.waves, r.lds_per_wave,
-                 p.ppw, grid.x, grid.y, shmem, p.order.active);
+                 "grid=%ux%u, %zu B LDS; work list %d (%d cells, run capacity %d, %d sweep chunks)\n", D, NBUF,
+                 kFp8 ? 1 : 0, r.waves, r.lds_per_wave, p.ppw, grid.x, grid.y, shmem, p.order.active,
+                 p.order.n_list, p.order.run_cap, p.order.sweep_chunks);
   hipLaunchKernelGGL((decode_partial_bf16<D, NBUF, kFp8>), grid, dim3(64), shmem, stream, p);
   return hipGetLastError();
 }

@@ -44,27 +44,31 @@ struct AppendParams {
   float* v_scale;
 };
 
-// Dispatch order of a decode launch with one partition per wave, built on
-// the host from the caller's length hint: longest work first.  The grid's
-// cells (partition index g, sequence) are relabelled by a bijection, so every
-// cell is still visited exactly once whatever the hint says; each wave then
-// takes its task from the device length as usual.  Ranks number the
-// sequences longest first.  Wave k (of the S * groups cells) takes, in order:
-//  - the full partitions: cells k < full_start[groups], group-major, ranks
-//    0 .. (full_start[g+1] - full_start[g]) - 1 of group g;
-//  - the partial last partitions, largest remainder first: partial[j] =
-//    rank | g << 9 for j < n_partial;
-//  - the remaining cells (empty by the hint): group g takes ranks
-//    S - (rest_start[g+1] - rest_start[g]) .. S - 1.
+// Work list of a decode launch with one partition per wave, built on the
+// host from the caller's length hint (P_h(s) = the hint's partition count of
+// sequence s, at least 1).  The grid then holds only the cells the hint
+// calls non-empty, largest first, instead of every (partition, sequence)
+// cell up to max_seq_len; whatever the hint says, every partition the device
+// lengths imply is still computed exactly once:
+//  - wave k < n_list takes cell list[k] = s | g << 9, i.e. partition g of
+//    sequence s; the cell of its last hinted partition, g = P_h(s) - 1, also
+//    takes partitions up to g + run_cap - 1 that the device length holds
+//    (one run, staged as usual);
+//  - wave n_list + j (sweep) takes, for s = j % S and chunk c = sweep_c0 +
+//    j / S, the partitions of [c * run_cap, (c + 1) * run_cap) from
+//    P_h(s) - 1 + run_cap on, as one run; a chunk that the hint already
+//    covers exits before touching memory.
+// The launcher sets run_cap (a run's capacity) and the sweep chunks.
 constexpr int kOrderMaxSeqs = 512;
 constexpr int kOrderMaxGroups = 64;
+constexpr int kOrderMaxCells = 1536;
 struct DecodeOrder {
   int32_t active;
-  int32_t n_full, n_partial;
-  int32_t full_start[kOrderMaxGroups + 1];
-  int32_t rest_start[kOrderMaxGroups + 1];
-  uint16_t rank_seq[kOrderMaxSeqs];     // sequence of each rank
-  uint16_t partial[kOrderMaxSeqs];
+  int32_t n_list;
+  int32_t run_cap;
+  int32_t sweep_c0, sweep_chunks;
+  uint8_t hinted[kOrderMaxSeqs];        // P_h(s)
+  uint16_t list[kOrderMaxCells];
 };
 
 struct DecodeParams {

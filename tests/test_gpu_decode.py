@@ -191,9 +191,11 @@ def test_wave_split_does_not_change_bits():
 
 @pytest.mark.parametrize("partition", [32, 512])
 def test_dispatch_order_does_not_change_bits(partition):
-    """Mixed lengths: the host hint orders the launch longest work first.  The
-    order is a relabelling of the grid's cells, so any hint (right, missing,
-    shuffled, reversed, out of range, all at the bound) gives the same bits."""
+    """Mixed lengths: from the host hint the launch lists only the partitions
+    the hint names, largest first; the last listed partition of a sequence
+    and sweep waves take whatever the device lengths add.  Any hint (right,
+    missing, shuffled, reversed, out of range, all at the bound, all zero)
+    must give the same bits."""
     need_gpu()
     import numpy as np
     import paged_kv_cache_08_amd.pkv as P
