@@ -52,6 +52,9 @@ def parse():
                     help="sliding window: attend to the last W positions and release older blocks each step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--separate-append", action="store_true",
+                    help="append the step's new K/V with kv_append_last before each layer's decode instead of "
+                         "in the decode kernel")
     ap.add_argument("--flush", action="store_true",
                     help="write a 1 GiB buffer before every decode step, outside its timing, to evict L2 and the "
                          "MALL; value and step time then come from events around each step")
@@ -84,12 +87,16 @@ class DecodeBench:
     slot reservation and the block-table upload — runs on a second stream
     while step i-1's attention still runs on the main stream, as a serving
     loop can do, since block placement does not depend on token values.  The
-    new K/V append, copy-on-write copies and attention stay on the main
-    stream, in step order.  Device tables are double-buffered (step i uses
+    copy-on-write copies, the new K/V append (handed to the decode call,
+    which writes it itself for batches of up to 1024 (sequence, KV head) rows
+    and runs the append kernel first above that; --separate-append calls
+    kv_append_last instead) and attention stay on the main stream, in step
+    order.  Device tables are double-buffered (step i uses
     buffer i % 2): the side stream waits until the step that last read its
     buffer has finished, and the main stream waits for the upload."""
 
-    def __init__(self, wl, steps_total: int, partition: int = 0, device="cuda", window: int = 0):
+    def __init__(self, wl, steps_total: int, partition: int = 0, device="cuda", window: int = 0,
+                 fused_append: bool = True):
         import numpy as np
         import torch
         from paged_kv_cache_08_amd import pkv as P
@@ -97,6 +104,7 @@ class DecodeBench:
 
         self.P, self.torch, self.np = P, torch, np
         self.wl = wl
+        self.fused_append = fused_append
         self.window = window
         self.dev = torch.device(device)
         self.layers = wl.layers
@@ -193,16 +201,20 @@ class DecodeBench:
                 timed = j % self.layers
             self.timed_steps += 1
         for l in range(self.layers):
-            P.pkv_kv_append_last(self.eng.pool, l, self.knew[l][j], self.vnew[l][j], self.tables[b], self.lens[b])
+            a = self.args[b][l]
+            if self.fused_append:       # the partial kernel writes the step's new token itself
+                P.set_new_token(a, self.knew[l][j], self.vnew[l][j])
+            else:
+                P.pkv_kv_append_last(self.eng.pool, l, self.knew[l][j], self.vnew[l][j], self.tables[b], self.lens[b])
             if l == timed:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record()
-            P.pkv_paged_decode_partial(self.args[b][l])
+            P.pkv_paged_decode_partial(a)
             if l == timed:
                 e1.record()
                 self.events.append((e0, e1, self.attended_bytes(l)))
-            P.pkv_paged_decode_reduce(self.args[b][l])
+            P.pkv_paged_decode_reduce(a)
         self.done[b].record(self.main)
         if self.flush is not None and record_events:
             s1 = torch.cuda.Event(enable_timing=True)
@@ -526,7 +538,8 @@ def main():
         return
     total = args.warmup + args.steps
     log(f"setup {wl.description}")
-    bench = DecodeBench(wl, total, partition=args.partition, window=args.window)
+    bench = DecodeBench(wl, total, partition=args.partition, window=args.window,
+                        fused_append=not args.separate_append)
     if args.flush:
         bench.enable_flush()
     log("setup done; warmup")
@@ -568,6 +581,7 @@ def main():
                    "layers": wl.layers,
                    "S": wl.S, "Hq": wl.Hq, "Hkv": wl.Hkv, "d": wl.d, "block": wl.block,
                    "partition": args.partition or 512, "window": args.window, "cache_flush": args.flush,
+                   "append": "separate kernel" if args.separate_append else "fused into the decode kernel",
                    "start_lengths_mean": float(wl.lengths.mean())},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(wl.S * args.steps / elapsed, 1),

@@ -272,8 +272,8 @@ int pkv_pool_snapshot(const pkv_pool* pool, int32_t* free_out, int32_t* ref_out,
 typedef struct pkv_decode_args {
   const void* q;              /* device [S][Hq][d], dtype                   */
   void* out;                  /* device [S][Hq][d], dtype                   */
-  const void* k_cache;        /* device, one layer, layout above            */
-  const void* v_cache;
+  void* k_cache;              /* device, one layer, layout above; written   */
+  void* v_cache;              /*   only by the fused append (k_new)         */
   const int32_t* block_tables;/* device [S][max_blocks]                     */
   const int32_t* seq_lens;    /* device [S]                                 */
   void* workspace;            /* device, >= pkv_decode_workspace_bytes(...) */
@@ -295,13 +295,30 @@ typedef struct pkv_decode_args {
                               /*   how many partitions each); NULL =        */
                               /*   unknown.  Results do not depend on it,   */
                               /*   even when it is wrong or stale.          */
-  const float* k_scale;       /* 8-bit cache: device scales of this layer,  */
-  const float* v_scale;       /*   fp32 [num_blocks][Hkv][B]; else unused   */
+  float* k_scale;             /* 8-bit cache: device scales of this layer,  */
+  float* v_scale;             /*   fp32 [num_blocks][Hkv][B]; else unused   */
   int32_t kv_dtype;           /* cache type: equal to dtype, or             */
                               /*   PKV_FP8_E4M3 with dtype PKV_BF16         */
   int32_t window;             /* > 0: attend to the last `window` positions */
                               /*   only; 0 = full attention                 */
+  const void* k_new;          /* optional fused append: device [S][Hkv][d], */
+  const void* v_new;          /*   16-byte aligned, in the cache dtype (bf16 */
+                              /*   for an 8-bit cache); see below; NULL =   */
+                              /*   none (both or neither)                   */
 } pkv_decode_args;
+
+/* Fused append (k_new, v_new set): before attending, the partial kernel
+ * writes row s of k_new / v_new as token seq_lens[s] - 1 of sequence s,
+ * exactly as pkv_kv_append_last with the same tables would (same bytes;
+ * an 8-bit cache quantises them the same way), so the attention sees it.
+ * The write is made by the wave that reads the sequence's last block, before
+ * it reads that block; with more than 16 query heads per KV head, or more
+ * than 1024 (sequence, KV head) rows (where a separate append is faster),
+ * the call runs the append kernel first instead.  Rows the decode cannot read (a
+ * length outside [1, max_seq_len], or a block id outside the pool among the
+ * last wave's blocks) may or may not receive the token; their outputs are
+ * NaN.  The block that receives the token must not be shared (copy it
+ * first, as for any append).  pkv_paged_decode_reduce ignores these fields. */
 
 /* Workspace bytes the decode call needs (0 when one partition suffices);
  * enough for any window, which needs at most as much.                     */

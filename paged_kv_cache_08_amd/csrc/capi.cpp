@@ -126,6 +126,10 @@ int prepare_decode(const pkv_decode_args* a, pkv::DecodeParams* p, int* kind_out
     return fail(PKV_ERR_INVALID, "decode: workspace missing or smaller than pkv_decode_workspace_bytes()");
   if (need > 0 && !aligned16(a->workspace))
     return fail(PKV_ERR_INVALID, "decode: workspace must be 16-byte aligned");
+  if ((a->k_new == nullptr) != (a->v_new == nullptr))
+    return fail(PKV_ERR_INVALID, "decode: k_new and v_new go together");
+  if (a->k_new && (!aligned16(a->k_new) || !aligned16(a->v_new)))
+    return fail(PKV_ERR_INVALID, "decode: k_new and v_new must be 16-byte aligned");
   p->q = a->q;
   p->out = a->out;
   p->k_cache = a->k_cache;
@@ -134,6 +138,8 @@ int prepare_decode(const pkv_decode_args* a, pkv::DecodeParams* p, int* kind_out
   p->seq_lens = a->seq_lens;
   p->k_scale = kind == pkv::kDecodeFP8KV ? a->k_scale : nullptr;
   p->v_scale = kind == pkv::kDecodeFP8KV ? a->v_scale : nullptr;
+  p->k_new = a->k_new;
+  p->v_new = a->v_new;
   p->S = a->num_seqs;
   p->Hq = a->num_q_heads;
   p->Hkv = a->num_kv_heads;
@@ -215,6 +221,49 @@ void build_order(const pkv_decode_args* a, pkv::DecodeParams* p) {
   o.active = 1;
 }
 
+// Largest batch, in (sequence, KV head) rows, whose new tokens the partial
+// kernel writes itself.  Each row's token is a scatter of partial-sector
+// writes; a few hundred of them cost the streaming reads little, and the
+// fused call saves the append launch and the gap after it (long context,
+// 128 rows: 1-2% of the step).  With thousands of rows (a 256-sequence
+// 32-head batch: 8192) the writes mixed into the read stream cost the
+// partial kernel 25-33 us, more than the separate append kernel (20 us)
+// and its gap.
+constexpr int64_t kFusedAppendMaxRows = 1024;
+
+// The partial kernel.  With a fused append and more than 16 query heads per
+// KV head (several waves read a sequence's last block) or more than
+// kFusedAppendMaxRows rows, the append kernel (the pkv_kv_append_last path)
+// runs first and the partial kernel only reads.
+int run_partial(const pkv_decode_args* a, pkv::DecodeParams& p, int kind, hipStream_t st) {
+  if (p.k_new && (p.G > 16 || static_cast<int64_t>(p.S) * p.Hkv > kFusedAppendMaxRows)) {
+    if (static_cast<int64_t>(a->max_blocks) * a->block_size > 0x7fffffffLL)
+      return fail(PKV_ERR_INVALID, "decode: max_blocks too large");
+    pkv::AppendParams ap{};
+    ap.k_new = a->k_new;
+    ap.v_new = a->v_new;
+    ap.slots = nullptr;
+    ap.tables = a->block_tables;
+    ap.lens = a->seq_lens;
+    ap.max_blocks = a->max_blocks;
+    ap.k_cache = a->k_cache;
+    ap.v_cache = a->v_cache;
+    ap.num_slots = static_cast<int64_t>(a->num_blocks) * a->block_size;
+    ap.n = a->num_seqs;
+    ap.num_kv_heads = a->num_kv_heads;
+    ap.head_dim = a->head_dim;
+    ap.block_size = a->block_size;
+    ap.elem_bytes = kind == pkv::kDecodeF32 ? 4 : kind == pkv::kDecodeBF16 ? 2 : 1;
+    ap.k_scale = a->k_scale;
+    ap.v_scale = a->v_scale;
+    const int rc = from_hip(pkv::launch_kv_append(ap, st), "decode: append");
+    if (rc) return rc;
+    p.k_new = nullptr;
+    p.v_new = nullptr;
+  }
+  return from_hip(pkv::launch_decode_partial(p, kind, st), "decode_partial");
+}
+
 }  // namespace
 
 extern "C" {
@@ -233,7 +282,7 @@ const char* pkv_status_string(int status) {
 
 const char* pkv_last_error(void) { return g_error.c_str(); }
 
-int pkv_version(void) { return 100; }
+int pkv_version(void) { return 200; }
 
 int pkv_pool_create(const pkv_pool_desc* d, pkv_pool** out) {
   return guarded([&]() -> int {
@@ -630,7 +679,7 @@ int pkv_paged_decode_partial(const pkv_decode_args* a, void* stream) {
   const int rc = prepare_decode(a, &p, &kind);
   if (rc) return rc;
   build_order(a, &p);
-  return from_hip(pkv::launch_decode_partial(p, kind, static_cast<hipStream_t>(stream)), "decode_partial");
+  return run_partial(a, p, kind, static_cast<hipStream_t>(stream));
 }
 
 int pkv_paged_decode_reduce(const pkv_decode_args* a, void* stream) {
@@ -648,7 +697,7 @@ int pkv_paged_attention_decode(const pkv_decode_args* a, void* stream) {
   if (rc) return rc;
   build_order(a, &p);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  rc = from_hip(pkv::launch_decode_partial(p, kind, st), "decode_partial");
+  rc = run_partial(a, p, kind, st);
   if (rc) return rc;
   return from_hip(pkv::launch_decode_reduce(p, kind, st), "decode_reduce");
 }

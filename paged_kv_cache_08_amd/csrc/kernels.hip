@@ -100,6 +100,19 @@ __device__ __forceinline__ int append_slot(const AppendParams& p, int i) {
   return slot;
 }
 
+// One wave writes token o of a (block, KV head) tile: kt / vt point at the
+// tile's K and V (layouts [d/x][B][x] and [d][B]), ks / vs at the token's d
+// values.  Shared by the append kernels and the decode kernels' fused
+// append, so both write the same bytes.
+template <typename T>
+__device__ __forceinline__ void write_token(T* kt, T* vt, const T* ks, const T* vs, int d, int B, int o) {
+  constexpr int x = 16 / sizeof(T);
+  for (int ch = threadIdx.x; ch < d / x; ch += 64)
+    *reinterpret_cast<u32x4*>(kt + (static_cast<size_t>(ch) * B + o) * x) =
+        *reinterpret_cast<const u32x4*>(ks + ch * x);
+  for (int e = threadIdx.x; e < d; e += 64) vt[static_cast<size_t>(e) * B + o] = vs[e];
+}
+
 template <typename T>
 __global__ __launch_bounds__(64) void kv_append_kernel(AppendParams p) {
   const int i = blockIdx.x;
@@ -107,19 +120,13 @@ __global__ __launch_bounds__(64) void kv_append_kernel(AppendParams p) {
   const int B = p.block_size;
   const int slot = append_slot(p, i);
   if (slot < 0) return;
-  constexpr int x = 16 / sizeof(T);
   const int d = p.head_dim;
   const int b = slot / B;
   const int o = slot - b * B;
   const T* ks = static_cast<const T*>(p.k_new) + (static_cast<size_t>(i) * p.num_kv_heads + h) * d;
   const T* vs = static_cast<const T*>(p.v_new) + (static_cast<size_t>(i) * p.num_kv_heads + h) * d;
   const size_t tile = (static_cast<size_t>(b) * p.num_kv_heads + h) * static_cast<size_t>(d) * B;
-  T* kd = static_cast<T*>(p.k_cache) + tile;
-  T* vd = static_cast<T*>(p.v_cache) + tile;
-  for (int ch = threadIdx.x; ch < d / x; ch += 64)
-    *reinterpret_cast<u32x4*>(kd + (static_cast<size_t>(ch) * B + o) * x) =
-        *reinterpret_cast<const u32x4*>(ks + ch * x);
-  for (int e = threadIdx.x; e < d; e += 64) vd[static_cast<size_t>(e) * B + o] = vs[e];
+  write_token<T>(static_cast<T*>(p.k_cache) + tile, static_cast<T*>(p.v_cache) + tile, ks, vs, d, B, o);
 }
 
 // 8-bit cache: one wave quantises one (token, KV head) row of K and of V.
@@ -132,6 +139,30 @@ __device__ __forceinline__ uint8_t e4m3_code(float v, float scale) {
   return static_cast<uint8_t>(__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.f, 0u, false) & 0xFFu);
 }
 
+// 8-bit form of write_token: row = block * num_kv_heads + head; quantises
+// the token's K and V rows and writes their codes and scales.
+__device__ __forceinline__ void write_token_fp8(uint8_t* k_cache, uint8_t* v_cache, float* k_scale, float* v_scale,
+                                                size_t row, const __bf16* ks, const __bf16* vs, int d, int o) {
+  float ka = 0.f, va = 0.f;
+  for (int e = threadIdx.x; e < d; e += 64) {
+    ka = fmaxf(ka, fabsf(static_cast<float>(ks[e])));
+    va = fmaxf(va, fabsf(static_cast<float>(vs[e])));
+  }
+  const float kscale = wave_max(ka) / 448.f;
+  const float vscale = wave_max(va) / 448.f;
+  uint8_t* kd = k_cache + row * kBlock * d;
+  uint8_t* vd = v_cache + row * kBlock * d;
+  for (int e = threadIdx.x; e < d; e += 64) {
+    kd[(e >> 4) * (kBlock * 16) + o * 16 + (e & 15)] = e4m3_code(static_cast<float>(ks[e]), kscale);
+    vd[(e >> 6) * 1024 + (o >> 2) * 256 + ((e & 63) >> 2) * 16 + (e & 3) * 4 + (o & 3)] =
+        e4m3_code(static_cast<float>(vs[e]), vscale);
+  }
+  if (threadIdx.x == 0) {
+    k_scale[row * kBlock + o] = kscale;
+    v_scale[row * kBlock + o] = vscale;
+  }
+}
+
 __global__ __launch_bounds__(64) void kv_append_fp8_kernel(AppendParams p) {
   const int i = blockIdx.x;
   const int h = blockIdx.y;
@@ -142,25 +173,8 @@ __global__ __launch_bounds__(64) void kv_append_fp8_kernel(AppendParams p) {
   const int o = slot - b * kBlock;
   const __bf16* ks = static_cast<const __bf16*>(p.k_new) + (static_cast<size_t>(i) * p.num_kv_heads + h) * d;
   const __bf16* vs = static_cast<const __bf16*>(p.v_new) + (static_cast<size_t>(i) * p.num_kv_heads + h) * d;
-  float ka = 0.f, va = 0.f;
-  for (int e = threadIdx.x; e < d; e += 64) {
-    ka = fmaxf(ka, fabsf(static_cast<float>(ks[e])));
-    va = fmaxf(va, fabsf(static_cast<float>(vs[e])));
-  }
-  const float kscale = wave_max(ka) / 448.f;
-  const float vscale = wave_max(va) / 448.f;
-  const size_t row = static_cast<size_t>(b) * p.num_kv_heads + h;
-  uint8_t* kd = static_cast<uint8_t*>(p.k_cache) + row * kBlock * d;
-  uint8_t* vd = static_cast<uint8_t*>(p.v_cache) + row * kBlock * d;
-  for (int e = threadIdx.x; e < d; e += 64) {
-    kd[(e >> 4) * (kBlock * 16) + o * 16 + (e & 15)] = e4m3_code(static_cast<float>(ks[e]), kscale);
-    vd[(e >> 6) * 1024 + (o >> 2) * 256 + ((e & 63) >> 2) * 16 + (e & 3) * 4 + (o & 3)] =
-        e4m3_code(static_cast<float>(vs[e]), vscale);
-  }
-  if (threadIdx.x == 0) {
-    p.k_scale[row * kBlock + o] = kscale;
-    p.v_scale[row * kBlock + o] = vscale;
-  }
+  write_token_fp8(static_cast<uint8_t*>(p.k_cache), static_cast<uint8_t*>(p.v_cache), p.k_scale, p.v_scale,
+                  static_cast<size_t>(b) * p.num_kv_heads + h, ks, vs, d, o);
 }
 
 // ---------------------------------------------------------------------------
@@ -345,6 +359,34 @@ __device__ __forceinline__ int block_id(int id0, int id1, int id2, int id3, int 
   return __builtin_amdgcn_readlane(v, i & 63);
 }
 
+// Fused append (p.k_new set): the wave whose partitions end at the sequence
+// end writes the step's new token, position n - 1, into block b (its last
+// block) of its KV head, before it loads that block.  Its own load then sees
+// the token (one wave's accesses to an address stay in order; the caller
+// follows the write with a compiler memory barrier so that no load is moved
+// above it), and with at most 16 query heads per KV head no other wave reads
+// that block (the host appends separately otherwise).  The bytes are those
+// the append kernels write.  ELEM: cache bytes per value (1: 8-bit codes
+// with scales).
+template <int D, int ELEM>
+__device__ __forceinline__ void append_new_token(const DecodeParams& p, int s, int kvh, int n, int b) {
+  const int o = (n - 1) % kBlock;
+  const size_t row = static_cast<size_t>(b) * p.Hkv + kvh;             // (block, KV head) tile
+  const size_t src = (static_cast<size_t>(s) * p.Hkv + kvh) * D;       // the token's row of k_new / v_new
+  if constexpr (ELEM == 1) {
+    write_token_fp8(static_cast<uint8_t*>(const_cast<void*>(p.k_cache)),
+                    static_cast<uint8_t*>(const_cast<void*>(p.v_cache)), const_cast<float*>(p.k_scale),
+                    const_cast<float*>(p.v_scale), row, static_cast<const __bf16*>(p.k_new) + src,
+                    static_cast<const __bf16*>(p.v_new) + src, D, o);
+  } else {
+    using U = std::conditional_t<ELEM == 2, uint16_t, uint32_t>;
+    U* kt = static_cast<U*>(const_cast<void*>(p.k_cache)) + row * D * kBlock;
+    U* vt = static_cast<U*>(const_cast<void*>(p.v_cache)) + row * D * kBlock;
+    write_token<U>(kt, vt, static_cast<const U*>(p.k_new) + src, static_cast<const U*>(p.v_new) + src, D, kBlock, o);
+  }
+  asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
 // decode_partial, bf16 queries (bf16 cache, or 8-bit E4M3 cache)
 //
@@ -432,9 +474,13 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
     }
   };
   int s_, kvh, h0, nh, P, part0, part_end, t_lo, t_end, blk_first, nblk, boundary0, id0, id1, id2, id3, id4;
+  int n_;
+  bool new_token;              // this wave appends the step's new token (fused append)
   {
     WaveTask w;
     if (!setup_task<__bf16, D>(p, w, issue_q)) return;
+    new_token = p.k_new != nullptr && w.part_end == w.P;
+    n_ = w.n;
     s_ = w.s; kvh = w.kvh; h0 = w.h0; nh = w.nh; P = w.P; part0 = w.part0; part_end = w.part_end;
     t_lo = w.t_lo; t_end = w.t_end; blk_first = w.blk_first; nblk = w.nblk; boundary0 = w.boundary0;
     id0 = w.id0; id1 = w.id1; id2 = w.id2; id3 = w.id3; id4 = w.id4;
@@ -626,6 +672,13 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
   using MayTail = std::integral_constant<bool, true>;
   BlockRegs<D, kFp8> buf[NBUF];
   int i = 0;
+  // The fused append's stores go after the first NBUF block loads when the
+  // last block comes later (a wait for block data also waits for every older
+  // store: stores and loads share vmcnt), else before every load.
+  auto append = [&]() {
+    append_new_token<D, kFp8 ? 1 : 2>(p, s_, kvh, n_, block_id(id0, id1, id2, id3, id4, nblk - 1));
+  };
+  if (new_token && nblk <= NBUF) append();
   if (nblk >= 2 * NBUF) {
     // Issue order matters: the loop expects buf[0] to be the oldest load in
     // flight on entry (as it is on the back edge), otherwise the wait at the
@@ -635,6 +688,7 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
       load_block(buf[u], u);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (new_token) append();
     for (; i + 2 * NBUF <= nblk; i += NBUF) {
       if (prio_swap) {
         if ((static_cast<unsigned>(__builtin_amdgcn_s_memrealtime() >> 12) ^ slot_bit) & 1)
@@ -652,6 +706,7 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
 #pragma unroll
     for (int u = 0; u < NBUF; ++u)
       if (u < nblk) load_block(buf[u], u);
+    if (new_token && nblk > NBUF) append();
   }
   for (; i < nblk; i += NBUF) {
 #pragma unroll
@@ -742,6 +797,8 @@ __global__ __launch_bounds__(64) void decode_partial_f32(DecodeParams p) {
   {
     WaveTask w;
     if (!setup_task<float, D>(p, w, [](const WaveTask&) {})) return;
+    if (p.k_new && w.part_end == w.P)        // before any block load (this kernel is not on the hot path)
+      append_new_token<D, 4>(p, w.s, w.kvh, w.n, block_id(w.id0, w.id1, w.id2, w.id3, w.id4, w.nblk - 1));
     s_ = w.s; kvh = w.kvh; h0 = w.h0; nh = w.nh; P = w.P; part0 = w.part0;
     t_lo = w.t_lo; t_end = w.t_end; blk_first = w.blk_first; nblk = w.nblk;
     id0 = w.id0; id1 = w.id1; id2 = w.id2; id3 = w.id3; id4 = w.id4;

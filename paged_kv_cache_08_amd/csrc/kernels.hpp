@@ -80,6 +80,8 @@ struct DecodeParams {
   const int32_t* seq_lens;
   const float* k_scale;  // 8-bit cache: per-slot scales [block][head][B]
   const float* v_scale;
+  const void* k_new;     // fused append: the step's new token [S][Hkv][d] (bf16 for an
+  const void* v_new;     //   8-bit cache), written at position seq_lens[s] - 1; or null
   float* part_ml;        // [S][Hq][Pmax][2]   (running max in log2 units, sum)
   float* part_acc;       // [S][Hq][Pmax][d]   unnormalised accumulators
   int32_t S, Hq, Hkv, G, d;

@@ -142,7 +142,7 @@ class PagedDecodeEngine:
         return self.tables, self.lens
 
     def decode_args(self, layer: int, q: torch.Tensor, out: torch.Tensor, max_seq_len: int,
-                    scale: Optional[float] = None, window: int = 0):
+                    scale: Optional[float] = None, window: int = 0, k_new=None, v_new=None):
         need = P.pkv_decode_workspace_bytes(q.shape[0], q.shape[1], self.d, max_seq_len, self.partition)
         if need and (self.workspace is None or self.workspace.numel() < need):
             self.workspace = torch.empty((need,), dtype=torch.uint8, device=self.device)
@@ -150,13 +150,18 @@ class PagedDecodeEngine:
                              max_seq_len, scale, self.partition, self.workspace if need else None, self.B,
                              host_seq_lens=self.host_lens,
                              k_scale=None if self.ks is None else self.ks[layer],
-                             v_scale=None if self.vs is None else self.vs[layer], window=window)
+                             v_scale=None if self.vs is None else self.vs[layer], window=window,
+                             k_new=k_new, v_new=v_new)
 
     def decode(self, layer: int, q: torch.Tensor, max_seq_len: int, out: Optional[torch.Tensor] = None,
-               scale: Optional[float] = None, stream=None, window: int = 0) -> torch.Tensor:
+               scale: Optional[float] = None, stream=None, window: int = 0, k_new=None,
+               v_new=None) -> torch.Tensor:
+        """Decode one layer of the synced batch.  k_new / v_new ([S][Hkv][d]):
+        the step's new token of each sequence, appended at its last position
+        by the decode kernel itself (in place of kv_append_last)."""
         if out is None:
             out = torch.empty_like(q)
-        a = self.decode_args(layer, q, out, max_seq_len, scale, window)
+        a = self.decode_args(layer, q, out, max_seq_len, scale, window, k_new, v_new)
         P.pkv_paged_attention_decode(a, stream)
         return out
 

@@ -59,7 +59,8 @@ class pkv_decode_args(ctypes.Structure):
                 ("head_dim", _i32), ("block_size", _i32), ("num_blocks", _i32),
                 ("max_blocks", _i32), ("max_seq_len", _i32), ("partition", _i32),
                 ("dtype", _i32), ("scale", ctypes.c_float), ("host_seq_lens", _vp),
-                ("k_scale", _vp), ("v_scale", _vp), ("kv_dtype", _i32), ("window", _i32)]
+                ("k_scale", _vp), ("v_scale", _vp), ("kv_dtype", _i32), ("window", _i32),
+                ("k_new", _vp), ("v_new", _vp)]
 
 
 class pkv_prefill_args(ctypes.Structure):
@@ -403,12 +404,14 @@ def pkv_decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, m
 def decode_args(q, out, k_cache, v_cache, block_tables, seq_lens, num_kv_heads: int, num_blocks: int,
                 max_seq_len: int, scale: Optional[float] = None, partition: int = 0, workspace=None,
                 block_size: int = 16, host_seq_lens: Optional[np.ndarray] = None,
-                k_scale=None, v_scale=None, window: int = 0) -> pkv_decode_args:
+                k_scale=None, v_scale=None, window: int = 0, k_new=None, v_new=None) -> pkv_decode_args:
     """Pack a pkv_decode_args from tensors (q/out [S][Hq][d]).  host_seq_lens:
     optional int32 numpy array [S] (kept alive by the returned object; it is
     read at every call, so it may be updated in place between calls).  The
     cache type follows the cache tensors' dtype (uint8 = 8-bit E4M3 codes,
-    which need the layer's k_scale / v_scale tensors)."""
+    which need the layer's k_scale / v_scale tensors).  k_new / v_new
+    ([S][Hkv][d]): the step's new token, appended by the partial kernel
+    (set_new_token changes them between calls)."""
     import torch
     S, Hq, d = q.shape
     dtype = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}[q.dtype]
@@ -431,7 +434,14 @@ def decode_args(q, out, k_cache, v_cache, block_tables, seq_lens, num_kv_heads: 
         assert host_seq_lens.dtype == np.int32 and host_seq_lens.flags.c_contiguous
         a.host_seq_lens = host_seq_lens.ctypes.data
         a._keep = host_seq_lens
+    set_new_token(a, k_new, v_new)
     return a
+
+
+def set_new_token(a: pkv_decode_args, k_new, v_new) -> None:
+    """Point the fused append of decode args `a` at k_new / v_new (device
+    [S][Hkv][d], contiguous), or switch it off with None."""
+    a.k_new, a.v_new = _ptr(k_new), _ptr(v_new)
 
 
 def pkv_paged_attention_decode(args: pkv_decode_args, stream=None) -> None:

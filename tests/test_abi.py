@@ -118,6 +118,9 @@ def _args(**kw):
     (dict(kv_dtype=P.PKV_FP8_E4M3), P.PKV_ERR_INVALID),  # no scale arrays
     (dict(kv_dtype=P.PKV_FP8_E4M3, k_scale=16, v_scale=8), P.PKV_ERR_INVALID),   # misaligned
     (dict(kv_dtype=P.PKV_FP8_E4M3, k_scale=16, v_scale=16, head_dim=96), P.PKV_ERR_UNSUPPORTED),
+    (dict(k_new=16), P.PKV_ERR_INVALID),                  # fused append: k_new without v_new
+    (dict(v_new=16), P.PKV_ERR_INVALID),
+    (dict(k_new=24, v_new=16), P.PKV_ERR_INVALID),        # misaligned
 ])
 def test_decode_argument_validation(bad, status):
     with pytest.raises(P.PkvError) as e:
