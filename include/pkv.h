@@ -331,6 +331,12 @@ int pkv_paged_attention_decode(const pkv_decode_args* args, void* stream);
 int pkv_paged_decode_partial(const pkv_decode_args* args, void* stream);
 /* The reduce kernel alone (no-op when one partition suffices). */
 int pkv_paged_decode_reduce(const pkv_decode_args* args, void* stream);
+/* 1 if a decode call with these arguments writes the new tokens in the
+ * partial kernel (k_new set, at most 16 query heads per KV head and at most
+ * 1024 (sequence, KV head) rows), 0 if it would run the append kernel first
+ * or has no k_new; a negative status for invalid arguments (as the decode
+ * call).  Reads nothing on the device.                                    */
+int pkv_decode_fuses_append(const pkv_decode_args* args);
 
 /* ---- paged prefill attention -------------------------------------------
  * Chunked prefill («Servicio…presupuesto de memoria» §6: exact attention,

@@ -235,8 +235,12 @@ constexpr int64_t kFusedAppendMaxRows = 1024;
 // KV head (several waves read a sequence's last block) or more than
 // kFusedAppendMaxRows rows, the append kernel (the pkv_kv_append_last path)
 // runs first and the partial kernel only reads.
+bool fuses_append(const pkv::DecodeParams& p) {
+  return p.k_new && p.G <= 16 && static_cast<int64_t>(p.S) * p.Hkv <= kFusedAppendMaxRows;
+}
+
 int run_partial(const pkv_decode_args* a, pkv::DecodeParams& p, int kind, hipStream_t st) {
-  if (p.k_new && (p.G > 16 || static_cast<int64_t>(p.S) * p.Hkv > kFusedAppendMaxRows)) {
+  if (p.k_new && !fuses_append(p)) {
     if (static_cast<int64_t>(a->max_blocks) * a->block_size > 0x7fffffffLL)
       return fail(PKV_ERR_INVALID, "decode: max_blocks too large");
     pkv::AppendParams ap{};
@@ -700,6 +704,14 @@ int pkv_paged_attention_decode(const pkv_decode_args* a, void* stream) {
   rc = run_partial(a, p, kind, st);
   if (rc) return rc;
   return from_hip(pkv::launch_decode_reduce(p, kind, st), "decode_reduce");
+}
+
+int pkv_decode_fuses_append(const pkv_decode_args* a) {
+  pkv::DecodeParams p{};
+  int kind = 0;
+  const int rc = prepare_decode(a, &p, &kind);
+  if (rc) return rc;
+  return fuses_append(p) ? 1 : 0;
 }
 
 int pkv_paged_prefill(const pkv_prefill_args* a, void* stream) {

@@ -672,13 +672,17 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
   using MayTail = std::integral_constant<bool, true>;
   BlockRegs<D, kFp8> buf[NBUF];
   int i = 0;
-  // The fused append's stores go after the first NBUF block loads when the
-  // last block comes later (a wait for block data also waits for every older
-  // store: stores and loads share vmcnt), else before every load.
+  // The fused append's stores must precede the load of the last block.  A
+  // wait for block data also waits for every older store (stores and loads
+  // share vmcnt), so they go as late as possible: an appending wave leaves
+  // its last block to the drain loop and stores just before that loop; with
+  // at most NBUF blocks the last one is among the first loads, and the
+  // stores go before them.
   auto append = [&]() {
     append_new_token<D, kFp8 ? 1 : 2>(p, s_, kvh, n_, block_id(id0, id1, id2, id3, id4, nblk - 1));
   };
   if (new_token && nblk <= NBUF) append();
+  const int nblk_steady = new_token ? nblk - 1 : nblk;   // the steady loop loads blocks below this
   if (nblk >= 2 * NBUF) {
     // Issue order matters: the loop expects buf[0] to be the oldest load in
     // flight on entry (as it is on the back edge), otherwise the wait at the
@@ -688,8 +692,7 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
       load_block(buf[u], u);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (new_token) append();
-    for (; i + 2 * NBUF <= nblk; i += NBUF) {
+    for (; i + 2 * NBUF <= nblk_steady; i += NBUF) {
       if (prio_swap) {
         if ((static_cast<unsigned>(__builtin_amdgcn_s_memrealtime() >> 12) ^ slot_bit) & 1)
           __builtin_amdgcn_s_setprio(1);
@@ -706,8 +709,10 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
 #pragma unroll
     for (int u = 0; u < NBUF; ++u)
       if (u < nblk) load_block(buf[u], u);
-    if (new_token && nblk > NBUF) append();
   }
+  // Here the blocks below i + NBUF are loaded, and the last one is not
+  // (nblk > NBUF; the steady loop stops before it).
+  if (new_token && nblk > NBUF) append();
   for (; i < nblk; i += NBUF) {
 #pragma unroll
     for (int u = 0; u < NBUF; ++u) {

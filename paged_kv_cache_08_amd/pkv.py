@@ -106,6 +106,7 @@ SIGNATURES = [
     ("pkv_paged_attention_decode", ctypes.c_int, [_P(pkv_decode_args), _vp]),
     ("pkv_paged_decode_partial", ctypes.c_int, [_P(pkv_decode_args), _vp]),
     ("pkv_paged_decode_reduce", ctypes.c_int, [_P(pkv_decode_args), _vp]),
+    ("pkv_decode_fuses_append", ctypes.c_int, [_P(pkv_decode_args)]),
     ("pkv_paged_prefill", ctypes.c_int, [_P(pkv_prefill_args), _vp]),
     ("pkv_read_tiles", ctypes.c_int, [_vp, _i64, _vp, _i64, _i32, _vp, _vp]),
 ]
@@ -454,6 +455,15 @@ def pkv_paged_decode_partial(args: pkv_decode_args, stream=None) -> None:
 
 def pkv_paged_decode_reduce(args: pkv_decode_args, stream=None) -> None:
     _check(lib().pkv_paged_decode_reduce(ctypes.byref(args), _stream(stream)))
+
+
+def pkv_decode_fuses_append(args: pkv_decode_args) -> bool:
+    """Whether a decode call with `args` writes k_new / v_new in its partial
+    kernel (else it runs the append kernel first, or has nothing to append)."""
+    status = lib().pkv_decode_fuses_append(ctypes.byref(args))
+    if status < 0:
+        _check(status)
+    return status == 1
 
 
 def prefill_args(q, out, k_cache, v_cache, block_tables, seq_lens, query_start, num_kv_heads: int,

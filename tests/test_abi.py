@@ -177,3 +177,18 @@ def test_read_tiles_argument_validation(args):
     base, nbytes, order, n, tpw, sink = args
     status = P.lib().pkv_read_tiles(base, nbytes, order, n, tpw, sink, 0)
     assert status == P.PKV_ERR_INVALID
+
+
+@pytest.mark.parametrize("kw,fused", [
+    (dict(), 0),                                          # nothing to append
+    (dict(k_new=16, v_new=16), 1),
+    (dict(k_new=16, v_new=16, num_q_heads=64), 0),        # 32 query heads per KV head: append kernel first
+    (dict(k_new=16, v_new=16, num_seqs=513), 0),          # 1026 (sequence, KV head) rows: append kernel first
+    (dict(k_new=16, v_new=16, num_seqs=512), 1),          # 1024 rows
+])
+def test_decode_fuses_append(kw, fused):
+    assert P.lib().pkv_decode_fuses_append(P.ctypes.byref(_args(**kw))) == fused
+
+
+def test_decode_fuses_append_rejects_bad_args():
+    assert P.lib().pkv_decode_fuses_append(P.ctypes.byref(_args(k_new=16))) == P.PKV_ERR_INVALID
