@@ -1131,15 +1131,19 @@ static hipError_t launch_variant(DecodeParams p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// bf16 cache with at least four partitions per deep wave slot: the deep
-// variant; else the shallow one (PKV_DECODE_DEEP=0/1 forces the choice).
+// bf16 cache with at least four partitions per deep wave slot, streamed in
+// runs (not from the work list): the deep variant; else the shallow one.
+// With the work list (one partition per wave, mixed lengths) two waves per
+// SIMD hide each other's set-up: full_step 398 -> 388 us.
+// PKV_DECODE_DEEP=0/1 forces the choice.
 template <int D, bool kFp8>
 static hipError_t launch_bf16q(const DecodeParams& p, hipStream_t stream) {
   constexpr int kShallow = kFp8 ? kDepthFp8 : kDepth;
   constexpr int kDeep = kFp8 ? kDepthFp8Deep : kDepthDeep;
   static const int forced = env_int("PKV_DECODE_DEEP");
-  const bool deep = forced >= 0 ? forced > 0
-                                : !kFp8 && p.tasks_hint >= 4LL * residency<D, kDeep, kFp8>().waves;
+  const int deep_waves = residency<D, kDeep, kFp8>().waves;
+  const bool listed = p.order.active && !long_uniform(p, deep_waves);   // would take the work list
+  const bool deep = forced >= 0 ? forced > 0 : !kFp8 && !listed && p.tasks_hint >= 4LL * deep_waves;
   return deep ? launch_variant<D, kDeep, kFp8>(p, stream) : launch_variant<D, kShallow, kFp8>(p, stream);
 }
 
