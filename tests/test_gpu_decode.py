@@ -189,8 +189,19 @@ def test_wave_split_does_not_change_bits():
     compare_out(with_hint, oracle_out(rp, wl, q))
 
 
+ORDER_CASES = {
+    "bf16, 4 heads per KV head": lambda: workloads.random_small(95, S=37, Hq=16, Hkv=4, d=128, dtype="bf16",
+                                                                max_len=1500, min_len=1),
+    "8-bit cache": lambda: workloads.fp8_cache(workloads.random_small(96, S=29, Hq=16, Hkv=2, d=128, dtype="bf16",
+                                                                      max_len=1500, min_len=1)),
+    "32 heads per KV head": lambda: workloads.random_small(97, S=11, Hq=64, Hkv=2, d=64, dtype="bf16",
+                                                           max_len=1500, min_len=1),
+}
+
+
+@pytest.mark.parametrize("case", list(ORDER_CASES))
 @pytest.mark.parametrize("partition", [32, 512])
-def test_dispatch_order_does_not_change_bits(partition):
+def test_dispatch_order_does_not_change_bits(partition, case):
     """Mixed lengths: from the host hint the launch lists only the partitions
     the hint names, largest first; the last listed partition of a sequence
     and sweep waves take whatever the device lengths add.  Any hint (right,
@@ -199,7 +210,7 @@ def test_dispatch_order_does_not_change_bits(partition):
     need_gpu()
     import numpy as np
     import paged_kv_cache_08_amd.pkv as P
-    wl = workloads.random_small(95, S=37, Hq=16, Hkv=4, d=128, dtype="bf16", max_len=1500, min_len=1)
+    wl = ORDER_CASES[case]()
     q, k, v = wl.tensors(device="cuda")
     eng, _, out = run_gpu(wl, {0: k}, {0: v}, q, partition=partition)
     ref = out[0].view(torch.int16).clone()
@@ -209,7 +220,7 @@ def test_dispatch_order_does_not_change_bits(partition):
              "reversed": lens[::-1].copy(), "out of range": np.where(lens % 3 == 0, -4, wl.max_len + 9).astype(np.int32),
              "at the bound": np.full(wl.S, wl.max_len, dtype=np.int32), "zeros": np.zeros(wl.S, dtype=np.int32)}
     for name, hint in hints.items():
-        note(f"dispatch order: partition {partition}, hint {name}")
+        note(f"dispatch order: {case}, partition {partition}, hint {name}")
         again = torch.empty_like(q)
         a = eng.decode_args(0, q, again, wl.max_len)
         a.host_seq_lens = None
