@@ -47,11 +47,13 @@ namespace {
 constexpr int kTok = 16;                 // tokens per cache block
 constexpr int kTile = 64;                // tokens per K/V tile (four blocks)
 
-// 8 waves of 32 rows: 166 registers, no accumulator traffic between AGPRs
-// and VGPRs, two waves per SIMD so one wave's softmax overlaps another's
-// MFMAs (4 waves of 64 rows measured 40% slower).
+// 12 waves of 32 rows: 168 registers, no accumulator traffic between AGPRs
+// and VGPRs, three waves per SIMD so that the others' MFMAs overlap one
+// wave's softmax, and each K/V tile in LDS serves 384 rows.  (8 waves, two
+// per SIMD: 7-14% slower; 4 waves of 64 rows: 40% slower.)  The workgroup's
+// LDS ring (three tiles, 99 KiB at d = 128) allows one workgroup per CU.
 #ifndef PKV_PREFILL_WAVES
-#define PKV_PREFILL_WAVES 8
+#define PKV_PREFILL_WAVES 12
 #endif
 #ifndef PKV_PREFILL_RB
 #define PKV_PREFILL_RB 2
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16(PrefillParams p) {
   using Sh = PrefillShape<D>;
   constexpr int KC = D / 32;             // QK k-steps
   constexpr int VT = D / 16;             // value-column tiles
-  constexpr int kPieces = 8 / kWaves;    // block tiles (K or V) each wave loads per tile
+  static_assert(kWaves >= 8, "waves 0..7 load the eight block tiles (K and V of four blocks) of a tile");
   extern __shared__ __bf16 lds[];
 
   // blockIdx.x = (sequence, KV head), blockIdx.y = row tile counted from the
@@ -176,11 +178,12 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16(PrefillParams p) {
   const int32_t* table = p.block_tables + static_cast<size_t>(s) * p.max_blocks;
   bool bad = false;                                            // wave-uniform
 
-  // Each wave loads one piece of every tile: the K (waves 0..3) or V (waves
-  // 4..7) block tile of block slot tb = wave % 4.  Block ids are read with
-  // scalar loads (the table is read-only here): they complete under
-  // lgkmcnt, so no table read sits among the tile loads that vmcnt counts.
-  static_assert(kPieces == 1, "one piece per wave and tile");
+  // Waves 0..7 load one piece of every tile: the K (waves 0..3) or V (waves
+  // 4..7) block tile of block slot tb = wave % 4; further waves only compute.
+  // Block ids are read with scalar loads (the table is read-only here): they
+  // complete under lgkmcnt, so no table read sits among the tile loads that
+  // vmcnt counts.
+  const bool loader = wave < 8;
   const int tb = wave & 3;
   const bool is_v = wave >= 4;
   const __attribute__((address_space(4))) int32_t* table_s =
@@ -190,6 +193,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16(PrefillParams p) {
   // Returns whether a global load was issued (a piece outside the sequence
   // or window is zero-filled instead).
   auto issue = [&](int kt, int buf) {
+    if (!loader) return false;
     const int bi = kt * (kTile / kTok) + tb;
     const int tok0 = bi * kTok;
     __bf16* dst = lds + buf * Sh::tile + (is_v ? 4 * Sh::blk_stride : 0) + tb * Sh::blk_stride;
@@ -219,7 +223,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16(PrefillParams p) {
   // After this wave's loads of tile kt landed: zero V tokens at or past n
   // (free or poisoned slots) in the block that holds token n - 1.
   auto fix_tail = [&](int kt, int buf) {
-    if (!is_v) return;
+    if (!loader || !is_v) return;
     const int tok0 = (kt * (kTile / kTok) + tb) * kTok;
     if (tok0 >= n || tok0 + kTok <= n) return;
     __bf16* dst = lds + buf * Sh::tile + 4 * Sh::blk_stride + tb * Sh::blk_stride;
@@ -256,11 +260,12 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16(PrefillParams p) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) ones[j] = static_cast<__bf16>(1.f);
 
-  // Loads in flight are this wave's pieces of the next kBufs - 1 tiles; every
-  // wave issues the same pieces for every tile, so a wait for all but the
-  // younger tiles' loads (one piece of D/32 loads per wave and tile, when it
-  // was loaded and not zero-filled) leaves exactly tile kt complete.
-  static_assert(kPieces == 1 && kBufs == 3, "the wait counts below assume one piece per wave and three buffers");
+  // Loads in flight are this wave's pieces of the next kBufs - 1 tiles; a
+  // loading wave issues the same piece for every tile, so a wait for all but
+  // the younger tiles' loads (one piece of D/32 loads per wave and tile, when
+  // it was loaded and not zero-filled) leaves exactly tile kt complete.  The
+  // barrier after it makes every piece visible to every wave.
+  static_assert(kBufs == 3, "the wait counts below assume three buffers");
   constexpr int kLoadsPerTile = D / 32;
   bool ahead = false;                  // whether tile kt + 1 issued loads (issued before the wait below)
   issue(kt_first, 0);
