@@ -1109,7 +1109,12 @@ static long long settle_order(DecodeParams& p, const Residency& r) {
   for (int s = 0; s < p.S; ++s) covered = std::min(covered, o.hinted[s] - 1 + o.run_cap);
   o.sweep_c0 = covered / o.run_cap;
   o.sweep_chunks = std::max(0, (p.pmax + o.run_cap - 1) / o.run_cap - o.sweep_c0);
-  return o.n_list + static_cast<long long>(p.S) * o.sweep_chunks;
+  const long long cells = o.n_list + static_cast<long long>(p.S) * o.sweep_chunks;
+  if (cells * p.Hkv > 0x7fffffffLL) {    // beyond a grid dimension: the plain grid (checked by the caller)
+    o.active = 0;
+    return static_cast<long long>(p.groups) * p.S;
+  }
+  return cells;
 }
 
 template <int D, int NBUF, bool kFp8>
