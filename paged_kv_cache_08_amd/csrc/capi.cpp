@@ -185,39 +185,44 @@ int prepare_decode(const pkv_decode_args* a, pkv::DecodeParams* p, int* kind_out
 }
 
 // The partial kernel's work list (DecodeOrder) from the host length hint:
-// without a window, for up to kOrderMaxSeqs sequences, kOrderMaxGroups
-// partitions and kOrderMaxCells listed cells.  Each sequence lists its
-// partitions by the hint (at least partition 0; lengths outside
-// [1, max_seq_len] count as 0), largest first: the launch's last waves are
-// then short ones.  Equal sizes keep partition-major order.
+// without a window, for up to kOrderMaxSeqs sequences and kOrderMaxGroups
+// partitions.  Lengths outside [1, max_seq_len] count as 0; such a sequence
+// lists partition 0 (as an empty partial one).  Full partitions come first,
+// group-major, longer sequences first within a group; then the partial
+// ones, largest first: the launch's last waves are short ones.
 void build_order(const pkv_decode_args* a, pkv::DecodeParams* p) {
   pkv::DecodeOrder& o = p->order;
   o.active = 0;
   if (!a->host_seq_lens || a->window > 0 || p->S > pkv::kOrderMaxSeqs || p->pmax > pkv::kOrderMaxGroups) return;
   const int S = p->S, part = p->partition;
   std::array<int32_t, pkv::kOrderMaxSeqs> n{};
-  int cells = 0;
+  std::array<int32_t, pkv::kOrderMaxSeqs> rank_seq{};
   for (int i = 0; i < S; ++i) {
     const int32_t v = a->host_seq_lens[i];
     n[i] = v >= 1 && v <= a->max_seq_len ? v : 0;
-    const int hinted = std::max(1, (n[i] + part - 1) / part);
-    o.hinted[i] = static_cast<uint8_t>(hinted);
-    cells += hinted;
+    o.hinted[i] = static_cast<uint8_t>(std::max(1, (n[i] + part - 1) / part));
+    rank_seq[i] = i;
   }
-  if (cells > pkv::kOrderMaxCells) return;
-  struct Cell {
-    int32_t size;
-    uint16_t code;
-  };
-  std::array<Cell, pkv::kOrderMaxCells> list;
-  int k = 0;
-  for (int g = 0; g < p->pmax; ++g)
-    for (int i = 0; i < S; ++i)
-      if (g < o.hinted[i])
-        list[k++] = Cell{std::max(0, std::min(n[i], (g + 1) * part) - g * part), static_cast<uint16_t>(i | g << 9)};
-  std::stable_sort(list.begin(), list.begin() + k, [](const Cell& x, const Cell& y) { return x.size > y.size; });
-  for (int j = 0; j < k; ++j) o.list[j] = list[j].code;
-  o.n_list = k;
+  std::stable_sort(rank_seq.begin(), rank_seq.begin() + S, [&](int x, int y) { return n[x] > n[y]; });
+  std::array<int32_t, pkv::kOrderMaxGroups> full{};              // per group: ranks with a full partition there
+  std::array<int32_t, pkv::kOrderMaxSeqs> partial_rank{};
+  int n_partial = 0;
+  for (int r = 0; r < S; ++r) {
+    const int32_t len = n[rank_seq[r]];
+    for (int g = 0; g < len / part; ++g) ++full[g];
+    if (len % part != 0 || len == 0) partial_rank[n_partial++] = r;
+    o.rank_seq[r] = static_cast<uint16_t>(rank_seq[r]);
+  }
+  std::stable_sort(partial_rank.begin(), partial_rank.begin() + n_partial,
+                   [&](int x, int y) { return n[rank_seq[x]] % part > n[rank_seq[y]] % part; });
+  for (int j = 0; j < n_partial; ++j) {
+    const int r = partial_rank[j];
+    o.partial[j] = static_cast<uint16_t>(r | (n[rank_seq[r]] / part) << 9);
+  }
+  o.full_start[0] = 0;
+  for (int g = 0; g < p->pmax; ++g) o.full_start[g + 1] = o.full_start[g] + full[g];
+  o.n_full = o.full_start[p->pmax];
+  o.n_partial = n_partial;
   o.active = 1;
 }
 

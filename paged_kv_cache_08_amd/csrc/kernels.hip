@@ -277,13 +277,19 @@ __device__ __forceinline__ bool setup_task(const DecodeParams& p, WaveTask& w, I
   int part0, part_lim;
   if (p.order.active) {
     const DecodeOrder& o = p.order;
-    if (cell < o.n_list) {
-      const int e = o.list[cell];
-      w.s = e & 511;
-      part0 = e >> 9;
+    if (cell < o.n_full) {
+      int g = 0;
+      while (g < kOrderMaxGroups - 1 && o.full_start[g + 1] <= cell) ++g;
+      w.s = o.rank_seq[cell - o.full_start[g]];
+      part0 = g;
       part_lim = part0 == o.hinted[w.s] - 1 ? part0 + o.run_cap : part0 + 1;
+    } else if (cell < o.n_full + o.n_partial) {
+      const int e = o.partial[cell - o.n_full];
+      w.s = o.rank_seq[e & 511];
+      part0 = e >> 9;
+      part_lim = part0 + o.run_cap;                  // a partial partition is the last hinted one
     } else {
-      const int j = cell - o.n_list;
+      const int j = cell - o.n_full - o.n_partial;
       w.s = j % p.S;
       const int c = o.sweep_c0 + j / p.S;
       part0 = max(c * o.run_cap, o.hinted[w.s] - 1 + o.run_cap);
@@ -1109,7 +1115,7 @@ static long long settle_order(DecodeParams& p, const Residency& r) {
   for (int s = 0; s < p.S; ++s) covered = std::min(covered, o.hinted[s] - 1 + o.run_cap);
   o.sweep_c0 = covered / o.run_cap;
   o.sweep_chunks = std::max(0, (p.pmax + o.run_cap - 1) / o.run_cap - o.sweep_c0);
-  const long long cells = o.n_list + static_cast<long long>(p.S) * o.sweep_chunks;
+  const long long cells = o.n_full + o.n_partial + static_cast<long long>(p.S) * o.sweep_chunks;
   if (cells * p.Hkv > 0x7fffffffLL) {    // beyond a grid dimension: the plain grid (checked by the caller)
     o.active = 0;
     return static_cast<long long>(p.groups) * p.S;
@@ -1129,9 +1135,9 @@ static hipError_t launch_variant(DecodeParams p, hipStream_t stream) {
   static std::atomic<bool> traced{false};
   if (trace > 0 && !traced.exchange(true))
     std::fprintf(stderr, "decode_partial<d=%d, depth=%d, fp8=%d>: %d resident waves, %d B LDS each; ppw=%d, "
-                 "grid=%ux%u, %zu B LDS; work list %d (%d cells, run capacity %d, %d sweep chunks)\n", D, NBUF,
-                 kFp8 ? 1 : 0, r.waves, r.lds_per_wave, p.ppw, grid.x, grid.y, shmem, p.order.active,
-                 p.order.n_list, p.order.run_cap, p.order.sweep_chunks);
+                 "grid=%ux%u, %zu B LDS; work list %d (%d full, %d partial cells, run capacity %d, %d sweep "
+                 "chunks)\n", D, NBUF, kFp8 ? 1 : 0, r.waves, r.lds_per_wave, p.ppw, grid.x, grid.y, shmem,
+                 p.order.active, p.order.n_full, p.order.n_partial, p.order.run_cap, p.order.sweep_chunks);
   hipLaunchKernelGGL((decode_partial_bf16<D, NBUF, kFp8>), grid, dim3(64), shmem, stream, p);
   return hipGetLastError();
 }

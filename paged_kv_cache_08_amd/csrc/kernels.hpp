@@ -49,26 +49,33 @@ struct AppendParams {
 // sequence s, at least 1).  The grid then holds only the cells the hint
 // calls non-empty, largest first, instead of every (partition, sequence)
 // cell up to max_seq_len; whatever the hint says, every partition the device
-// lengths imply is still computed exactly once:
-//  - wave k < n_list takes cell list[k] = s | g << 9, i.e. partition g of
-//    sequence s; the cell of its last hinted partition, g = P_h(s) - 1, also
-//    takes partitions up to g + run_cap - 1 that the device length holds
-//    (one run, staged as usual);
-//  - wave n_list + j (sweep) takes, for s = j % S and chunk c = sweep_c0 +
-//    j / S, the partitions of [c * run_cap, (c + 1) * run_cap) from
-//    P_h(s) - 1 + run_cap on, as one run; a chunk that the hint already
-//    covers exits before touching memory.
-// The launcher sets run_cap (a run's capacity) and the sweep chunks.
+// lengths imply is still computed exactly once.  Ranks number the sequences
+// longest first (by the hint); wave k takes:
+//  - k < n_full: a full partition, group-major: partition g of rank
+//    k - full_start[g] (full_start[g+1] - full_start[g] ranks hold more than g
+//    full partitions);
+//  - then, up to n_full + n_partial: the sequences' partial last partitions,
+//    largest first: partial[j] = rank | g << 9 (a sequence the hint calls
+//    empty lists partition 0 here, last);
+//  - then the sweep: for s = j % S and chunk c = sweep_c0 + j / S, the
+//    partitions of [c * run_cap, (c + 1) * run_cap) from P_h(s) - 1 + run_cap
+//    on, as one run; a chunk that the hint already covers exits before
+//    touching memory.
+// The wave of a sequence's last hinted partition, g = P_h(s) - 1, also takes
+// the partitions up to g + run_cap - 1 that the device length holds (one
+// run, staged as usual).  The launcher sets run_cap (a run's capacity) and
+// the sweep chunks.
 constexpr int kOrderMaxSeqs = 512;
-constexpr int kOrderMaxGroups = 64;
-constexpr int kOrderMaxCells = 1536;
+constexpr int kOrderMaxGroups = 128;
 struct DecodeOrder {
   int32_t active;
-  int32_t n_list;
+  int32_t n_full, n_partial;
   int32_t run_cap;
   int32_t sweep_c0, sweep_chunks;
+  int32_t full_start[kOrderMaxGroups + 1];
+  uint16_t rank_seq[kOrderMaxSeqs];     // sequence of each rank
+  uint16_t partial[kOrderMaxSeqs];
   uint8_t hinted[kOrderMaxSeqs];        // P_h(s)
-  uint16_t list[kOrderMaxCells];
 };
 
 struct DecodeParams {
