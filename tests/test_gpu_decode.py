@@ -196,6 +196,9 @@ ORDER_CASES = {
                                                                       max_len=1500, min_len=1)),
     "32 heads per KV head": lambda: workloads.random_small(97, S=11, Hq=64, Hkv=2, d=64, dtype="bf16",
                                                            max_len=1500, min_len=1),
+    # with 32-token partitions: up to 122 partitions, ~18k listed cells
+    "300 sequences": lambda: workloads.random_small(98, S=300, Hq=8, Hkv=2, d=64, dtype="bf16", max_len=3900,
+                                                    min_len=1),
 }
 
 
