@@ -227,6 +227,19 @@ class DecodeBench:
         self.kv_bytes.append(self.attended_bytes(0) * self.layers)
         self.step_idx += 1
 
+    def unique_bytes(self) -> int:
+        """KV bytes of the distinct pool slots one layer's decode reads at the
+        current lengths: a block shared by several sequences counts once."""
+        np = self.np
+        B = self.wl.block
+        slots = []
+        for sid, n in zip(self.ids, self.lengths):
+            table = np.asarray(self.P.pkv_seq_table(self.eng.pool, sid), dtype=np.int64)
+            t = np.arange(max(0, n - self.window) if self.window else 0, n)
+            slots.append(table[t // B] * B + t % B)
+        unique = int(np.unique(np.concatenate(slots)).size) if slots else 0
+        return unique * self.wl.Hkv * self.wl.kv_bytes_per_token_head()
+
     def attended_bytes(self, layer: int) -> int:
         """KV bytes one layer's partial kernel reads at the current lengths."""
         wl = self.wl
@@ -559,6 +572,8 @@ def main():
     elapsed = time.perf_counter() - t0
 
     kv_total = sum(bench.kv_bytes)
+    logical = bench.attended_bytes(0)              # the last step's bytes per layer, logical and unique
+    unique = bench.unique_bytes()
     if args.flush:      # the flush writes are not part of the step
         elapsed = sum(a.elapsed_time(b) for a, b in bench.step_events) / 1e3
     value = kv_total / elapsed / 1e9
@@ -588,6 +603,11 @@ def main():
                    "append": "fused into the decode kernel" if bench.fused_append else "separate kernel",
                    "start_lengths_mean": float(wl.lengths.mean())},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        # Blocks shared between sequences (a common prefix) are read by each of them; their unique bytes
+        # may stay in the MALL, so such a rate on logical bytes is cache-assisted.
+        "kv_bytes_unique_per_layer": unique,
+        "value_unique_bytes": round(value * unique / logical, 2),
+        "cache_assisted": unique < logical,
         "decode_tokens_per_s": round(wl.S * args.steps / elapsed, 1),
         "roofline": {"bound": "hbm", "kernel": "decode_partial", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
