@@ -346,7 +346,7 @@ def prefill_cpu_baseline(wl, seconds: float, window: int = 0):
         cores = 1
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"sequence 0 of the batch ({m} new tokens over {int(one.lengths[0])}), "
-                      f"{heads} query heads one at a time, {t:.1f} s"}
+                      f"{heads} query heads one at a time, {t:.1f} s", "host": host_info()}
 
 
 def read_ceiling(nbytes: int, reps: int = 5):
@@ -389,6 +389,24 @@ def read_ceiling(nbytes: int, reps: int = 5):
     del buf, order
     torch.cuda.empty_cache()
     return result
+
+
+def host_info() -> dict:
+    """The host the oracle baseline ran on: usable cores, CPU model and the
+    BLAS library numpy calls (threadpoolctl's view)."""
+    info = {"usable_cores": len(os.sched_getaffinity(0))}
+    try:
+        with open("/proc/cpuinfo") as f:
+            info["cpu_model"] = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        info["cpu_model"] = None
+    try:
+        from threadpoolctl import threadpool_info
+        info["blas"] = [{k: i.get(k) for k in ("internal_api", "version", "num_threads", "threading_layer")}
+                        for i in threadpool_info() if i.get("user_api") == "blas"]
+    except ImportError:
+        info["blas"] = None
+    return info
 
 
 def launch_stats_us(ms):
@@ -505,7 +523,7 @@ def cpu_baseline(wl_name: str, seconds: float, window: int = 0):
         cores, single = 1, None
     return {"value": kv / t / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{sample}; {steps} decode steps, {t:.1f} s", "tokens_per_s": wl.S * steps / t,
-            "single_thread": single}
+            "single_thread": single, "host": host_info()}
 
 
 def load_traffic(workload: str):
