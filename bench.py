@@ -521,9 +521,16 @@ def cpu_baseline(wl_name: str, seconds: float, window: int = 0):
                   "tokens_per_s": wl.S * steps1 / t1}
     except ImportError:
         cores, single = 1, None
-    return {"value": kv / t / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{sample}; {steps} decode steps, {t:.1f} s", "tokens_per_s": wl.S * steps / t,
-            "single_thread": single, "host": host_info()}
+    result = {"value": kv / t / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+              "sample": f"{sample}; {steps} decode steps, {t:.1f} s", "tokens_per_s": wl.S * steps / t,
+              "single_thread": single, "host": host_info()}
+    full_layers = workloads.CONFIGS[base]().layers
+    if full_layers > 1:
+        # The sample times one layer; a step of the whole model runs that many layers, each costing about
+        # the same per token (the work is proportional to the KV bytes), so tokens/s divides by the layers.
+        result["tokens_per_s_all_layers"] = result["tokens_per_s"] / full_layers
+        result["extrapolation"] = f"one-layer sample time x {full_layers} layers per step"
+    return result
 
 
 def load_traffic(workload: str):
