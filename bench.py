@@ -353,7 +353,7 @@ def read_ceiling(nbytes: int, reps: int = 5):
     """What memory delivers for the decode's access pattern without its
     arithmetic: pkv_read_tiles over a buffer of the launch's KV bytes, as
     4 KiB tiles in a seeded random order (gather) and in address order
-    (stream), best over a few wave sizes; GB/s from the median of `reps`
+    (stream), best over 16-512 tiles per wave; GB/s from the median of `reps`
     HIP-event-timed launches each."""
     import numpy as np
     import torch
@@ -367,7 +367,7 @@ def read_ceiling(nbytes: int, reps: int = 5):
     result = {"kernel": "read_tiles", "bytes": tiles * 4096, "tile_bytes": 4096}
     for mode, o in (("gather", order), ("stream", None)):
         best, best_tpw = 0.0, None
-        for tpw in (16, 64, 256):
+        for tpw in (16, 64, 256, 512):
             sink = torch.empty(-(-tiles // tpw) * 64, dtype=torch.int32, device="cuda")
             for _ in range(2):
                 P.pkv_read_tiles(buf, o, tiles, tpw, sink)
