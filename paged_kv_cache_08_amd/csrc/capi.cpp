@@ -184,45 +184,52 @@ int prepare_decode(const pkv_decode_args* a, pkv::DecodeParams* p, int* kind_out
   return PKV_OK;
 }
 
-// The partial kernel's work list (DecodeOrder) from the host length hint:
-// without a window, for up to kOrderMaxSeqs sequences and kOrderMaxGroups
-// partitions.  Lengths outside [1, max_seq_len] count as 0; such a sequence
-// lists partition 0 (as an empty partial one).  Full partitions come first,
-// group-major, longer sequences first within a group; then the partial
-// ones, largest first: the launch's last waves are short ones.
+// The partial kernel's work list (DecodeOrder) from the host length hint,
+// for up to kOrderMaxSeqs sequences and kOrderMaxGroups partitions.
+// Partitions are counted as the kernel counts them: with a window, from the
+// first one that overlaps it.  Lengths outside [1, max_seq_len] count as 0;
+// such a sequence lists partition 0.  Every partition of a sequence but its
+// last is listed as full (all hold a whole partition, except the first one of
+// a window), group-major, sequences with more partitions first; then each
+// sequence's last partition, largest first: the launch's last waves are
+// short ones.
 void build_order(const pkv_decode_args* a, pkv::DecodeParams* p) {
   pkv::DecodeOrder& o = p->order;
   o.active = 0;
-  if (!a->host_seq_lens || a->window > 0 || p->S > pkv::kOrderMaxSeqs || p->pmax > pkv::kOrderMaxGroups) return;
+  if (!a->host_seq_lens || p->S > pkv::kOrderMaxSeqs || p->pmax > pkv::kOrderMaxGroups) return;
   const int S = p->S, part = p->partition;
-  std::array<int32_t, pkv::kOrderMaxSeqs> n{};
-  std::array<int32_t, pkv::kOrderMaxSeqs> rank_seq{};
+  std::array<int32_t, pkv::kOrderMaxSeqs> parts{}, last{}, rank_seq{};   // partitions, tokens in the last one
   for (int i = 0; i < S; ++i) {
     const int32_t v = a->host_seq_lens[i];
-    n[i] = v >= 1 && v <= a->max_seq_len ? v : 0;
-    o.hinted[i] = static_cast<uint8_t>(std::max(1, (n[i] + part - 1) / part));
+    if (v >= 1 && v <= a->max_seq_len) {
+      const int32_t t0 = a->window > 0 ? std::max(0, v - a->window) : 0;
+      const int32_t pf = t0 / part;
+      parts[i] = (v - 1) / part - pf + 1;
+      last[i] = v - std::max(t0, (pf + parts[i] - 1) * part);
+    }
+    o.hinted[i] = static_cast<uint8_t>(std::max(1, parts[i]));
     rank_seq[i] = i;
   }
-  std::stable_sort(rank_seq.begin(), rank_seq.begin() + S, [&](int x, int y) { return n[x] > n[y]; });
+  std::stable_sort(rank_seq.begin(), rank_seq.begin() + S,
+                   [&](int x, int y) { return parts[x] > parts[y] || (parts[x] == parts[y] && last[x] > last[y]); });
   std::array<int32_t, pkv::kOrderMaxGroups> full{};              // per group: ranks with a full partition there
   std::array<int32_t, pkv::kOrderMaxSeqs> partial_rank{};
-  int n_partial = 0;
   for (int r = 0; r < S; ++r) {
-    const int32_t len = n[rank_seq[r]];
-    for (int g = 0; g < len / part; ++g) ++full[g];
-    if (len % part != 0 || len == 0) partial_rank[n_partial++] = r;
-    o.rank_seq[r] = static_cast<uint16_t>(rank_seq[r]);
+    const int sq = rank_seq[r];
+    for (int g = 0; g + 1 < parts[sq]; ++g) ++full[g];
+    partial_rank[r] = r;
+    o.rank_seq[r] = static_cast<uint16_t>(sq);
   }
-  std::stable_sort(partial_rank.begin(), partial_rank.begin() + n_partial,
-                   [&](int x, int y) { return n[rank_seq[x]] % part > n[rank_seq[y]] % part; });
-  for (int j = 0; j < n_partial; ++j) {
+  std::stable_sort(partial_rank.begin(), partial_rank.begin() + S,
+                   [&](int x, int y) { return last[rank_seq[x]] > last[rank_seq[y]]; });
+  for (int j = 0; j < S; ++j) {
     const int r = partial_rank[j];
-    o.partial[j] = static_cast<uint16_t>(r | (n[rank_seq[r]] / part) << 9);
+    o.partial[j] = static_cast<uint16_t>(r | (o.hinted[rank_seq[r]] - 1) << 9);
   }
   o.full_start[0] = 0;
   for (int g = 0; g < p->pmax; ++g) o.full_start[g + 1] = o.full_start[g] + full[g];
   o.n_full = o.full_start[p->pmax];
-  o.n_partial = n_partial;
+  o.n_partial = S;
   o.active = 1;
 }
 

@@ -282,12 +282,12 @@ __device__ __forceinline__ bool setup_task(const DecodeParams& p, WaveTask& w, I
       while (g < kOrderMaxGroups - 1 && o.full_start[g + 1] <= cell) ++g;
       w.s = o.rank_seq[cell - o.full_start[g]];
       part0 = g;
-      part_lim = part0 == o.hinted[w.s] - 1 ? part0 + o.run_cap : part0 + 1;
+      part_lim = part0 + 1;
     } else if (cell < o.n_full + o.n_partial) {
       const int e = o.partial[cell - o.n_full];
       w.s = o.rank_seq[e & 511];
       part0 = e >> 9;
-      part_lim = part0 + o.run_cap;                  // a partial partition is the last hinted one
+      part_lim = part0 + o.run_cap;                  // the sequence's last hinted partition
     } else {
       const int j = cell - o.n_full - o.n_partial;
       w.s = j % p.S;

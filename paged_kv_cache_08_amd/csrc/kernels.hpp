@@ -49,21 +49,23 @@ struct AppendParams {
 // sequence s, at least 1).  The grid then holds only the cells the hint
 // calls non-empty, largest first, instead of every (partition, sequence)
 // cell up to max_seq_len; whatever the hint says, every partition the device
-// lengths imply is still computed exactly once.  Ranks number the sequences
-// longest first (by the hint); wave k takes:
-//  - k < n_full: a full partition, group-major: partition g of rank
-//    k - full_start[g] (full_start[g+1] - full_start[g] ranks hold more than g
-//    full partitions);
-//  - then, up to n_full + n_partial: the sequences' partial last partitions,
-//    largest first: partial[j] = rank | g << 9 (a sequence the hint calls
-//    empty lists partition 0 here, last);
+// lengths imply is still computed exactly once.  Partitions are numbered as
+// the kernel numbers them (with a window, from the first one that overlaps
+// it).  Ranks number the sequences by hinted partition count, most first;
+// wave k takes:
+//  - k < n_full: a partition before its sequence's last, group-major:
+//    partition g of rank k - full_start[g] (full_start[g+1] - full_start[g]
+//    ranks have more than g + 1 partitions);
+//  - then, up to n_full + n_partial: each sequence's last partition, largest
+//    first: partial[j] = rank | g << 9 (a sequence the hint calls empty lists
+//    partition 0 here, last);
 //  - then the sweep: for s = j % S and chunk c = sweep_c0 + j / S, the
 //    partitions of [c * run_cap, (c + 1) * run_cap) from P_h(s) - 1 + run_cap
 //    on, as one run; a chunk that the hint already covers exits before
 //    touching memory.
-// The wave of a sequence's last hinted partition, g = P_h(s) - 1, also takes
-// the partitions up to g + run_cap - 1 that the device length holds (one
-// run, staged as usual).  The launcher sets run_cap (a run's capacity) and
+// The wave of a sequence's last hinted partition (its partial entry, g =
+// P_h(s) - 1) also takes the partitions up to g + run_cap - 1 that the
+// device length holds (one run, staged as usual).  The launcher sets run_cap (a run's capacity) and
 // the sweep chunks.
 constexpr int kOrderMaxSeqs = 512;
 constexpr int kOrderMaxGroups = 128;
