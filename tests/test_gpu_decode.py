@@ -202,30 +202,37 @@ ORDER_CASES = {
 }
 
 
+@pytest.mark.parametrize("window", [0, 700])
 @pytest.mark.parametrize("case", list(ORDER_CASES))
 @pytest.mark.parametrize("partition", [32, 512])
-def test_dispatch_order_does_not_change_bits(partition, case):
+def test_dispatch_order_does_not_change_bits(partition, case, window):
     """Mixed lengths: from the host hint the launch lists only the partitions
     the hint names, largest first; the last listed partition of a sequence
     and sweep waves take whatever the device lengths add.  Any hint (right,
     missing, shuffled, reversed, out of range, all at the bound, all zero)
-    must give the same bits."""
+    must give the bits of the launch without a hint, with and without a
+    sliding window."""
     need_gpu()
     import numpy as np
     import paged_kv_cache_08_amd.pkv as P
     wl = ORDER_CASES[case]()
     q, k, v = wl.tensors(device="cuda")
-    eng, _, out = run_gpu(wl, {0: k}, {0: v}, q, partition=partition)
-    ref = out[0].view(torch.int16).clone()
+    eng, _, _ = run_gpu(wl, {0: k}, {0: v}, partition=partition)
+    first = torch.empty_like(q)                 # without a hint: the plain grid
+    a = eng.decode_args(0, q, first, wl.max_len, window=window)
+    a.host_seq_lens = None
+    P.pkv_paged_attention_decode(a)
+    torch.cuda.synchronize()
+    ref = first.view(torch.int16).clone()
     lens = np.asarray(eng.host_lens[:wl.S], dtype=np.int32)
     rng = np.random.default_rng(3)
     hints = {"none": None, "right": lens.copy(), "shuffled": rng.permutation(lens).astype(np.int32),
              "reversed": lens[::-1].copy(), "out of range": np.where(lens % 3 == 0, -4, wl.max_len + 9).astype(np.int32),
              "at the bound": np.full(wl.S, wl.max_len, dtype=np.int32), "zeros": np.zeros(wl.S, dtype=np.int32)}
     for name, hint in hints.items():
-        note(f"dispatch order: {case}, partition {partition}, hint {name}")
+        note(f"dispatch order: {case}, partition {partition}, window {window}, hint {name}")
         again = torch.empty_like(q)
-        a = eng.decode_args(0, q, again, wl.max_len)
+        a = eng.decode_args(0, q, again, wl.max_len, window=window)
         a.host_seq_lens = None
         if hint is not None:
             a.host_seq_lens, a._keep = hint.ctypes.data, hint
@@ -233,7 +240,7 @@ def test_dispatch_order_does_not_change_bits(partition, case):
         torch.cuda.synchronize()
         assert torch.equal(again.view(torch.int16), ref), name
     rp = oracle_replay(wl, {0: k}, {0: v})
-    compare_out(out[0], oracle_out(rp, wl, q))
+    compare_out(first, oracle_out(rp, wl, q, window=window))
 
 
 @pytest.mark.parametrize("make", [workloads.tiny, lambda: _cow_workload(),
