@@ -32,13 +32,18 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention: KV GB/s read and % of HBM peak; decode tokens/s"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_08_amd", "csrc", "kernels.hip")
+# the decode kernels' sources: the kernels, and the header with the wave's cell decoding
+KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_cache_08_amd", "csrc", f)
+               for f in ("kernels.hip", "kernels.hpp", "device_util.hpp")]
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for src in KERNEL_SRCS:
+        with open(src, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def parse():

@@ -338,6 +338,40 @@ int pkv_paged_decode_reduce(const pkv_decode_args* args, void* stream);
  * call).  Reads nothing on the device.                                    */
 int pkv_decode_fuses_append(const pkv_decode_args* args);
 
+/* The partial kernel's launch as a decode call with these arguments would
+ * make it, planned on the host; nothing runs and nothing on the device is
+ * read.  The grid is cells x num_kv_heads waves by head_groups; cell c's
+ * waves read sequence s and its partitions [first, end) (numbered from the
+ * first partition that overlaps the window, clipped on the device to the
+ * partitions the device length has), so that every partition a sequence
+ * has is read by exactly one cell and exactly one cell per sequence starts
+ * at partition 0, whatever the host lengths say.  The order of cells is the
+ * launch order.  (The split into partitions merged by running statistics is
+ * «Servicio…presupuesto de memoria» §6's blockwise attention; which wave
+ * takes which partitions is this library's own scheduling.)
+ *   info   out: the plan (below).
+ *   cells  out, optional: 3 int32 per cell, (s, first, end), for the first
+ *          min(cap, info->cells) cells; first == end == partitions_bound for
+ *          a cell whose waves exit at once (a sweep range the host lengths
+ *          already cover).
+ * Returns PKV_OK or the decode call's status for invalid arguments.        */
+typedef struct pkv_decode_plan_info {
+  int64_t cells;
+  int64_t listed_cells;         /* work list: the cells it names (the rest sweep partitions past
+                                   the host lengths, in case the device lengths are longer) */
+  int32_t head_groups;          /* grid y: query heads of a KV head, 16 per wave */
+  int32_t pipeline_depth;       /* blocks in flight per wave in the chosen kernel */
+  int32_t resident_waves;       /* wave slots of that kernel on the device (0: not queried) */
+  int32_t partitions_per_wave;  /* plain grid: partitions per run; 1 with the work list */
+  int32_t work_list;            /* 1 if cells follow the host lengths' work list */
+  int32_t run_cap;              /* work list: most partitions one cell may take */
+  int32_t max_wave_blocks;      /* most blocks one wave streams */
+  int32_t fused_append;         /* 1 if the partial kernel writes k_new / v_new */
+  int32_t partitions_bound;     /* partitions of max_seq_len (of the window, with one) */
+  int32_t lds_bytes;            /* dynamic LDS per wave */
+} pkv_decode_plan_info;
+int pkv_decode_plan(const pkv_decode_args* args, pkv_decode_plan_info* info, int32_t* cells, int64_t cap);
+
 /* ---- paged prefill attention -------------------------------------------
  * Chunked prefill («Servicio…presupuesto de memoria» §6: exact attention,
  * blockwise with running statistics; §2/§4: prefill work has another shape

@@ -726,6 +726,41 @@ int pkv_decode_fuses_append(const pkv_decode_args* a) {
   return fuses_append(p) ? 1 : 0;
 }
 
+int pkv_decode_plan(const pkv_decode_args* a, pkv_decode_plan_info* info, int32_t* cells, int64_t cap) {
+  if (!info) return fail(PKV_ERR_INVALID, "decode_plan: null info");
+  if (cap < 0 || (cap > 0 && !cells)) return fail(PKV_ERR_INVALID, "decode_plan: bad cells buffer");
+  pkv::DecodeParams p{};
+  int kind = 0;
+  const int rc = prepare_decode(a, &p, &kind);
+  if (rc) return rc;
+  build_order(a, &p);
+  pkv::DecodeLaunchPlan plan{};
+  const int prc = from_hip(pkv::plan_decode_partial(p, kind, &plan), "decode_plan");
+  if (prc) return prc;
+  const pkv::DecodeParams& q = plan.params;
+  info->cells = plan.cells;
+  info->listed_cells = q.order.active ? q.order.n_full + q.order.n_partial : 0;
+  info->head_groups = plan.grid_y;
+  info->pipeline_depth = plan.depth;
+  info->resident_waves = plan.resident_waves;
+  info->partitions_per_wave = q.ppw;
+  info->work_list = q.order.active;
+  info->run_cap = q.order.active ? q.order.run_cap : 0;
+  info->max_wave_blocks = plan.max_wave_blocks;
+  info->fused_append = fuses_append(p) ? 1 : 0;
+  info->partitions_bound = q.pmax;
+  info->lds_bytes = static_cast<int32_t>(plan.lds_bytes);
+  const int64_t n = std::min<int64_t>(cap, plan.cells);
+  for (int64_t c = 0; c < n; ++c) {
+    int s = 0, part0 = 0, part_lim = 0;
+    if (!pkv::decode_cell(q, static_cast<int>(c), s, part0, part_lim)) part0 = part_lim = q.pmax;
+    cells[3 * c] = s;
+    cells[3 * c + 1] = part0;
+    cells[3 * c + 2] = part_lim;
+  }
+  return PKV_OK;
+}
+
 int pkv_paged_prefill(const pkv_prefill_args* a, void* stream) {
   if (!a) return fail(PKV_ERR_INVALID, "prefill: null args");
   if (a->dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "prefill: bf16 only");

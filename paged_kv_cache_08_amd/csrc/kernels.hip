@@ -275,34 +275,7 @@ __device__ __forceinline__ bool setup_task(const DecodeParams& p, WaveTask& w, I
   // The wave's partitions: [part0, part_lim), clipped below to the device
   // length.
   int part0, part_lim;
-  if (p.order.active) {
-    const DecodeOrder& o = p.order;
-    if (cell < o.n_full) {
-      int g = 0;
-      while (g < kOrderMaxGroups - 1 && o.full_start[g + 1] <= cell) ++g;
-      w.s = o.rank_seq[cell - o.full_start[g]];
-      part0 = g;
-      part_lim = part0 + 1;
-    } else if (cell < o.n_full + o.n_partial) {
-      const int e = o.partial[cell - o.n_full];
-      w.s = o.rank_seq[e & 511];
-      part0 = e >> 9;
-      part_lim = part0 + o.run_cap;                  // the sequence's last hinted partition
-    } else {
-      const int j = cell - o.n_full - o.n_partial;
-      w.s = j % p.S;
-      const int c = o.sweep_c0 + j / p.S;
-      part0 = max(c * o.run_cap, o.hinted[w.s] - 1 + o.run_cap);
-      part_lim = (c + 1) * o.run_cap;
-      if (part0 >= part_lim || part0 >= p.pmax) return false;     // the hint's cells cover it
-    }
-  } else {
-    w.s = cell % p.S;
-    const int grp = cell / p.S;
-    part0 = grp * p.ppw;
-    part_lim = grp == p.groups - 1 ? p.pmax : part0 + p.ppw;     // the last run takes the rest
-  }
-  part_lim = min(part_lim, p.pmax);
+  if (!decode_cell(p, cell, w.s, part0, part_lim)) return false;   // a sweep chunk the hint covers
   w.h0 = w.kvh * p.G + blockIdx.y * 16;
   w.nh = min(16, p.G - static_cast<int>(blockIdx.y) * 16);
   w.n = p.seq_lens[w.s];
@@ -1033,7 +1006,7 @@ static Residency query_residency() {
     cus = 256;
   if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
       lds <= 0)
-    lds = 64 * 1024;
+    lds = 160 * 1024;                      // a gfx950 CU's LDS
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_partial_bf16<D, NBUF, kFp8>, 64, 0) !=
           hipSuccess || per_cu <= 0)
     per_cu = 8;
@@ -1123,14 +1096,20 @@ static long long settle_order(DecodeParams& p, const Residency& r) {
   return cells;
 }
 
+// With `dry` the launch is only planned: the plan goes there and nothing
+// runs on the device.
 template <int D, int NBUF, bool kFp8>
-static hipError_t launch_variant(DecodeParams p, hipStream_t stream) {
+static hipError_t launch_variant(DecodeParams p, hipStream_t stream, DecodeLaunchPlan* dry) {
   const Residency& r = residency<D, NBUF, kFp8>();
   set_runs(p, r);
   const long long cells = settle_order(p, r);
   dim3 grid(static_cast<unsigned>(cells * p.Hkv), (p.G + 15) / 16);
   const int longest = p.order.active ? p.order.run_cap : longest_run(p);
   const size_t shmem = static_cast<size_t>(longest - 1) * std::min(16, p.G) * (p.d + 2) * sizeof(float);
+  if (dry) {
+    *dry = DecodeLaunchPlan{p, cells, static_cast<int>(grid.y), NBUF, r.waves, kMaxWaveBlocks, shmem};
+    return hipSuccess;
+  }
   static const int trace = env_int("PKV_TRACE_SCHEDULE");   // print the first choice of each variant
   static std::atomic<bool> traced{false};
   if (trace > 0 && !traced.exchange(true))
@@ -1148,32 +1127,38 @@ static hipError_t launch_variant(DecodeParams p, hipStream_t stream) {
 // SIMD hide each other's set-up: full_step 398 -> 388 us.
 // PKV_DECODE_DEEP=0/1 forces the choice.
 template <int D, bool kFp8>
-static hipError_t launch_bf16q(const DecodeParams& p, hipStream_t stream) {
+static hipError_t launch_bf16q(const DecodeParams& p, hipStream_t stream, DecodeLaunchPlan* dry) {
   constexpr int kShallow = kFp8 ? kDepthFp8 : kDepth;
   constexpr int kDeep = kFp8 ? kDepthFp8Deep : kDepthDeep;
   static const int forced = env_int("PKV_DECODE_DEEP");
   const int deep_waves = residency<D, kDeep, kFp8>().waves;
   const bool listed = p.order.active && !long_uniform(p, deep_waves);   // would take the work list
   const bool deep = forced >= 0 ? forced > 0 : !kFp8 && !listed && p.tasks_hint >= 4LL * deep_waves;
-  return deep ? launch_variant<D, kDeep, kFp8>(p, stream) : launch_variant<D, kShallow, kFp8>(p, stream);
+  return deep ? launch_variant<D, kDeep, kFp8>(p, stream, dry) : launch_variant<D, kShallow, kFp8>(p, stream, dry);
 }
 
-hipError_t launch_decode_partial(const DecodeParams& p0, int kind, hipStream_t stream) {
+static hipError_t launch_or_plan(const DecodeParams& p0, int kind, hipStream_t stream, DecodeLaunchPlan* dry) {
   DecodeParams p = p0;
   switch (kind) {
     case kDecodeBF16:
-      if (p.d == 128) return launch_bf16q<128, false>(p, stream);
-      if (p.d == 64) return launch_bf16q<64, false>(p, stream);
+      if (p.d == 128) return launch_bf16q<128, false>(p, stream, dry);
+      if (p.d == 64) return launch_bf16q<64, false>(p, stream, dry);
       return hipErrorInvalidValue;
     case kDecodeFP8KV:
-      if (p.d == 128) return launch_bf16q<128, true>(p, stream);
-      if (p.d == 64) return launch_bf16q<64, true>(p, stream);
+      if (p.d == 128) return launch_bf16q<128, true>(p, stream, dry);
+      if (p.d == 64) return launch_bf16q<64, true>(p, stream, dry);
       return hipErrorInvalidValue;
     case kDecodeF32: {
       p.ppw = 1;
       p.groups = p.pmax;
       p.order.active = 0;
       dim3 grid(static_cast<unsigned>(static_cast<long long>(p.pmax) * p.S * p.Hkv), (p.G + 15) / 16);
+      if (dry) {
+        if (p.d != 128 && p.d != 64) return hipErrorInvalidValue;
+        *dry = DecodeLaunchPlan{p, static_cast<long long>(p.pmax) * p.S, static_cast<int>(grid.y), 1, 0,
+                                kMaxWaveBlocks, 0};
+        return hipSuccess;
+      }
       if (p.d == 128) hipLaunchKernelGGL(decode_partial_f32<128>, grid, dim3(64), 0, stream, p);
       else if (p.d == 64) hipLaunchKernelGGL(decode_partial_f32<64>, grid, dim3(64), 0, stream, p);
       else return hipErrorInvalidValue;
@@ -1182,6 +1167,14 @@ hipError_t launch_decode_partial(const DecodeParams& p0, int kind, hipStream_t s
     default:
       return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_decode_partial(const DecodeParams& p, int kind, hipStream_t stream) {
+  return launch_or_plan(p, kind, stream, nullptr);
+}
+
+hipError_t plan_decode_partial(const DecodeParams& p, int kind, DecodeLaunchPlan* plan) {
+  return launch_or_plan(p, kind, nullptr, plan);
 }
 
 hipError_t launch_decode_reduce(const DecodeParams& p, int kind, hipStream_t stream) {

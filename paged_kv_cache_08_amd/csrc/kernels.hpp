@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime_api.h>
+#include <hip/amd_detail/host_defines.h>
 
 #include <cstddef>
 #include <cstdint>
@@ -105,6 +106,45 @@ struct DecodeParams {
   DecodeOrder order;     // used by the partial kernel when order.active and ppw == 1
 };
 
+// Grid cell `cell` of a decode partial launch (blockIdx.x / Hkv): its
+// sequence s and partitions [part0, part_lim) before the device length
+// clips them (numbered from the window's first partition with a window).
+// False for a sweep cell that the hint's cells already cover (the wave exits
+// before touching memory).  Shared by the kernel and the host's launch plan.
+__host__ __device__ inline bool decode_cell(const DecodeParams& p, int cell, int& s, int& part0, int& part_lim) {
+  if (p.order.active) {
+    const DecodeOrder& o = p.order;
+    if (cell < o.n_full) {
+      int g = 0;
+      while (g < kOrderMaxGroups - 1 && o.full_start[g + 1] <= cell) ++g;
+      s = o.rank_seq[cell - o.full_start[g]];
+      part0 = g;
+      part_lim = part0 + 1;
+    } else if (cell < o.n_full + o.n_partial) {
+      const int e = o.partial[cell - o.n_full];
+      s = o.rank_seq[e & 511];
+      part0 = e >> 9;
+      part_lim = part0 + o.run_cap;                  // the sequence's last hinted partition
+    } else {
+      const int j = cell - o.n_full - o.n_partial;
+      s = j % p.S;
+      const int c = o.sweep_c0 + j / p.S;
+      part0 = c * o.run_cap;
+      const int from = o.hinted[s] - 1 + o.run_cap;
+      if (from > part0) part0 = from;
+      part_lim = (c + 1) * o.run_cap;
+      if (part0 >= part_lim || part0 >= p.pmax) return false;
+    }
+  } else {
+    s = cell % p.S;
+    const int grp = cell / p.S;
+    part0 = grp * p.ppw;
+    part_lim = grp == p.groups - 1 ? p.pmax : part0 + p.ppw;     // the last run takes the rest
+  }
+  if (part_lim > p.pmax) part_lim = p.pmax;
+  return true;
+}
+
 struct PrefillParams {
   const void* q;                 // [T][Hq][d] bf16, sequence s's rows from query_start[s]
   void* out;                     // [T][Hq][d] bf16
@@ -135,6 +175,19 @@ enum DecodeKind : int {
   kDecodeFP8KV = 2,    // bf16 queries, 8-bit E4M3 cache with per-slot scales
 };
 hipError_t launch_decode_partial(const DecodeParams& p, int kind, hipStream_t stream);
+// A decode partial launch as launch_decode_partial would make it, without
+// launching: the kernel variant, the grid and the parameters with the runs
+// and the work list settled (plan->params; decode_cell() maps its cells).
+struct DecodeLaunchPlan {
+  DecodeParams params;
+  long long cells;       // grid x = cells * Hkv
+  int grid_y;            // query-head groups of 16
+  int depth;             // blocks in flight per wave (the pipeline variant)
+  int resident_waves;    // wave slots of that variant on the device
+  int max_wave_blocks;   // most blocks one wave may stream
+  size_t lds_bytes;      // dynamic LDS per wave for staged partials
+};
+hipError_t plan_decode_partial(const DecodeParams& p, int kind, DecodeLaunchPlan* plan);
 hipError_t launch_decode_reduce(const DecodeParams& p, int kind, hipStream_t stream);
 bool decode_shape_supported(int kind, int head_dim, int block_size);
 // Read-bandwidth calibration: wave w reads tiles order[w*tpw ...] (or

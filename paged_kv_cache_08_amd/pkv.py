@@ -63,6 +63,13 @@ class pkv_decode_args(ctypes.Structure):
                 ("k_new", _vp), ("v_new", _vp)]
 
 
+class pkv_decode_plan_info(ctypes.Structure):
+    _fields_ = [("cells", _i64), ("listed_cells", _i64), ("head_groups", _i32), ("pipeline_depth", _i32), ("resident_waves", _i32),
+                ("partitions_per_wave", _i32), ("work_list", _i32), ("run_cap", _i32),
+                ("max_wave_blocks", _i32), ("fused_append", _i32), ("partitions_bound", _i32),
+                ("lds_bytes", _i32)]
+
+
 class pkv_prefill_args(ctypes.Structure):
     _fields_ = [("q", _vp), ("out", _vp), ("k_cache", _vp), ("v_cache", _vp),
                 ("block_tables", _vp), ("seq_lens", _vp), ("query_start", _vp),
@@ -107,6 +114,7 @@ SIGNATURES = [
     ("pkv_paged_decode_partial", ctypes.c_int, [_P(pkv_decode_args), _vp]),
     ("pkv_paged_decode_reduce", ctypes.c_int, [_P(pkv_decode_args), _vp]),
     ("pkv_decode_fuses_append", ctypes.c_int, [_P(pkv_decode_args)]),
+    ("pkv_decode_plan", ctypes.c_int, [_P(pkv_decode_args), _P(pkv_decode_plan_info), _P(_i32), _i64]),
     ("pkv_paged_prefill", ctypes.c_int, [_P(pkv_prefill_args), _vp]),
     ("pkv_read_tiles", ctypes.c_int, [_vp, _i64, _vp, _i64, _i32, _vp, _vp]),
 ]
@@ -464,6 +472,20 @@ def pkv_decode_fuses_append(args: pkv_decode_args) -> bool:
     if status < 0:
         _check(status)
     return status == 1
+
+
+def pkv_decode_plan(args: pkv_decode_args, with_cells: bool = True):
+    """The partial kernel's launch plan for `args` (nothing runs): the
+    pkv_decode_plan_info and, with `with_cells`, an int32 array [cells][3] of
+    (sequence, first partition, end partition) per grid cell."""
+    info = pkv_decode_plan_info()
+    _check(lib().pkv_decode_plan(ctypes.byref(args), ctypes.byref(info), None, 0))
+    if not with_cells:
+        return info, None
+    cells = np.zeros((info.cells, 3), dtype=np.int32)
+    _check(lib().pkv_decode_plan(ctypes.byref(args), ctypes.byref(info),
+                                 cells.ctypes.data_as(_P(_i32)), info.cells))
+    return info, cells
 
 
 def prefill_args(q, out, k_cache, v_cache, block_tables, seq_lens, query_start, num_kv_heads: int,
