@@ -950,6 +950,60 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams p) {
   }
 }
 
+// The same merge for launches with few partitions (pmax <= kRowReduceMaxParts),
+// one wave per (sequence, query head) row and four rows per workgroup: in a
+// mixed batch most rows have one partition and exit after reading their
+// length, and a quarter of the workgroups dispatch faster than one per row.
+// Lane i < P holds partition i's (m, l); lane c accumulates columns
+// c * D/64 ... of every partition's weighted accumulator in partition order.
+constexpr int kRowReduceMaxParts = 32;
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_reduce_rows_kernel(DecodeParams p) {
+  constexpr int CPL = D / 64;      // columns per lane
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= p.S * p.Hq) return;
+  const int s = row / p.Hq;
+  const int n = p.seq_lens[s];
+  if (n < 1 || n > p.max_seq_len) return;
+  int t0, pf, P;
+  window_partitions(p, n, t0, pf, P);
+  if (P <= 1) return;
+  const float* ml = p.part_ml + static_cast<size_t>(row) * p.pmax * 2;
+  const float* acc = p.part_acc + static_cast<size_t>(row) * p.pmax * D + CPL * lane;
+  const float m_i = lane < P ? ml[2 * lane] : -INFINITY;
+  const float l_i = lane < P ? ml[2 * lane + 1] : 0.f;
+  const float M = wave_max(m_i);
+  const float w_i = lane < P ? exp2_fast(m_i - M) : 0.f;
+  const float L = wave_sum(l_i * w_i);
+  float o[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) o[j] = 0.f;
+  int i = 0;
+  for (; i + 4 <= P; i += 4) {
+    float a[4][CPL];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) a[u][j] = acc[static_cast<size_t>(i + u) * D + j];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float w = __shfl(w_i, i + u);
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) o[j] += w * a[u][j];
+    }
+  }
+  for (; i < P; ++i) {
+    const float w = __shfl(w_i, i);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) o[j] += w * acc[static_cast<size_t>(i) * D + j];
+  }
+  T* out = static_cast<T*>(p.out) + static_cast<size_t>(row) * D + CPL * lane;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) out[j] = static_cast<T>(o[j] / L);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1179,6 +1233,20 @@ hipError_t plan_decode_partial(const DecodeParams& p, int kind, DecodeLaunchPlan
 
 hipError_t launch_decode_reduce(const DecodeParams& p, int kind, hipStream_t stream) {
   if (p.pmax <= 1) return hipSuccess;
+  if (p.pmax <= kRowReduceMaxParts) {
+    const dim3 rgrid(static_cast<unsigned>((static_cast<long long>(p.S) * p.Hq + 3) / 4));
+    const bool bf16_out = kind == kDecodeBF16 || kind == kDecodeFP8KV;
+    if (p.d == 128) {
+      if (bf16_out) hipLaunchKernelGGL((decode_reduce_rows_kernel<__bf16, 128>), rgrid, dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((decode_reduce_rows_kernel<float, 128>), rgrid, dim3(256), 0, stream, p);
+    } else if (p.d == 64) {
+      if (bf16_out) hipLaunchKernelGGL((decode_reduce_rows_kernel<__bf16, 64>), rgrid, dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((decode_reduce_rows_kernel<float, 64>), rgrid, dim3(256), 0, stream, p);
+    } else {
+      return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   dim3 grid(static_cast<unsigned>(p.S * p.Hq));
   if (kind == kDecodeBF16 || kind == kDecodeFP8KV) {   // bf16 outputs
     if (p.d == 128) hipLaunchKernelGGL((decode_reduce_kernel<__bf16, 128>), grid, dim3(256), 0, stream, p);
