@@ -66,6 +66,17 @@ def test_edge_lengths(partition):
     _full_case(wl, partition=partition)
 
 
+@pytest.mark.parametrize("longest", [1024, 1025], ids=["32 partitions (row reduce)", "33 partitions (wide reduce)"])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_reduce_kernel_boundary(longest, dtype, d):
+    """Launches whose partition bound is at most 32 merge one row per wave,
+    larger ones with a 256-lane workgroup per row; both against the oracle
+    at the boundary, with every row's partition count from 1 to the bound."""
+    lengths = [1, 31, 32, 33, 97, 480, 512, 513, 1000, longest]
+    wl = workloads.with_lengths(lengths, Hq=8, Hkv=2, d=d, dtype=dtype, seed=longest + d)
+    _full_case(wl, partition=32)
+
+
 def test_edge_lengths_fp32():
     wl = workloads.with_lengths(EDGE, Hq=4, Hkv=1, d=64, dtype="f32", seed=5)
     _full_case(wl)
