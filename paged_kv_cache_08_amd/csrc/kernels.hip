@@ -181,13 +181,24 @@ __global__ __launch_bounds__(64) void kv_append_fp8_kernel(AppendParams p) {
 // table_upload: block tables and lengths from the pinned staging buffer
 // (host memory the GPU reads directly) to the device arrays, in one launch.
 // ---------------------------------------------------------------------------
+// With `vec` (both table pointers 16-byte aligned) the tables move as
+// 16-byte chunks: a quarter of the reads across the host link.
 __global__ __launch_bounds__(256) void table_upload_kernel(const int32_t* __restrict__ src, int32_t* __restrict__ tab,
-                                                           int64_t n_tab, int32_t* __restrict__ lens, int32_t n_len) {
+                                                           int64_t n_tab, int32_t* __restrict__ lens, int32_t n_len,
+                                                           bool vec) {
+  const int64_t n_vec = vec ? n_tab / 4 : 0;          // 16-byte chunks of the tables
+  const int64_t tail0 = 4 * n_vec;                    // first value moved singly
+  const int64_t total = n_vec + (n_tab - tail0) + n_len;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n_tab + n_len; i += stride) {
-    const int32_t v = src[i];
-    if (i < n_tab) tab[i] = v;
-    else lens[i - n_tab] = v;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total; i += stride) {
+    if (i < n_vec) {
+      reinterpret_cast<u32x4*>(tab)[i] = reinterpret_cast<const u32x4*>(src)[i];
+    } else {
+      const int64_t j = tail0 + (i - n_vec);
+      const int32_t v = src[j];
+      if (j < n_tab) tab[j] = v;
+      else lens[j - n_tab] = v;
+    }
   }
 }
 
@@ -1018,11 +1029,12 @@ hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t stream) {
 
 hipError_t launch_table_upload(const int32_t* host_src, int32_t* dev_tables, int64_t n_tab, int32_t* dev_lens,
                                int32_t n_len, hipStream_t stream) {
-  const int64_t total = n_tab + n_len;
-  if (total <= 0) return hipSuccess;
+  if (n_tab + n_len <= 0) return hipSuccess;
+  const bool vec = (reinterpret_cast<uintptr_t>(host_src) & 15) == 0 && (reinterpret_cast<uintptr_t>(dev_tables) & 15) == 0;
+  const int64_t total = (vec ? n_tab / 4 + n_tab % 4 : n_tab) + n_len;
   const int64_t blocks = std::min<int64_t>((total + 255) / 256, 1024);
   hipLaunchKernelGGL(table_upload_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, host_src,
-                     dev_tables, n_tab, dev_lens, n_len);
+                     dev_tables, n_tab, dev_lens, n_len, vec);
   return hipGetLastError();
 }
 

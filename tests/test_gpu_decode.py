@@ -308,3 +308,34 @@ def test_workspace_reuse_and_garbage():
         assert torch.equal(again.view(torch.int16), ref_bits), trial
     rp = oracle_replay(wl, {0: k}, {0: v})
     compare_out(out[0], oracle_out(rp, wl, q))
+
+
+@pytest.mark.parametrize("offset", [0, 1], ids=["16-byte aligned", "4-byte aligned"])
+def test_sync_tables_writes_exactly_the_rows(offset):
+    """pkv_sync_tables writes each row (table, then -1 padding) and the
+    lengths, whether the table buffer allows 16-byte copies or not, with a
+    row count that leaves a ragged tail, and nothing around them."""
+    need_gpu()
+    from paged_kv_cache_08_amd import pkv as P
+    from paged_kv_cache_08_amd.engine import PagedDecodeEngine
+    wl = workloads.with_lengths([1, 17, 33, 100, 257], Hq=4, Hkv=1, d=64, dtype="f32", seed=3)
+    eng = PagedDecodeEngine(1, wl.Hkv, wl.d, wl.num_blocks, wl.cache_dtype, init_perm=wl.perm)
+    eng.run_script(wl.setup_ops + wl.step_ops, None)
+    ids = list(wl.seq_ids)
+    n, mb = len(ids), 23                                    # 115 entries: not a multiple of 4
+    buf = torch.full((n * mb + offset + 8,), -7, dtype=torch.int32, device="cuda")
+    tab = buf[offset:offset + n * mb].view(n, mb)
+    lens = torch.full((n + 2,), -7, dtype=torch.int32, device="cuda")
+    host = np.zeros(n, dtype=np.int32)
+    P.pkv_sync_tables(eng.pool, ids, tab, lens[1:n + 1], host)
+    torch.cuda.synchronize()
+    want = np.full((n, mb), -1, dtype=np.int32)
+    for r, i in enumerate(ids):
+        t = P.pkv_seq_table(eng.pool, i)
+        want[r, :len(t)] = t
+    got = buf.cpu().numpy()
+    assert (got[:offset] == -7).all() and (got[offset + n * mb:] == -7).all()
+    assert np.array_equal(got[offset:offset + n * mb].reshape(n, mb), want)
+    want_lens = np.array([P.pkv_seq_length(eng.pool, i) for i in ids], dtype=np.int32)
+    assert np.array_equal(lens.cpu().numpy()[1:n + 1], want_lens) and np.array_equal(host, want_lens)
+    assert lens[0].item() == -7 and lens[n + 1].item() == -7
