@@ -354,39 +354,40 @@ def prefill_cpu_baseline(wl, seconds: float, window: int = 0):
                       f"{heads} query heads one at a time, {t:.1f} s", "host": host_info()}
 
 
-def read_ceiling(nbytes: int, reps: int = 5):
+def read_ceiling(nbytes: int, reps: int = 5, tile_bytes: int = 4096):
     """What memory delivers for the decode's access pattern without its
     arithmetic: pkv_read_tiles over a buffer of the launch's KV bytes, as
-    4 KiB tiles in a seeded random order (gather) and in address order
-    (stream), best over 16-512 tiles per wave; GB/s from the median of `reps`
-    HIP-event-timed launches each."""
+    tiles of one (block, KV head) (4 KiB in bf16, 2 KiB in 8-bit codes) in a
+    seeded random order (gather) and in address order (stream), best over
+    16-512 tiles per wave; GB/s from the median of `reps` HIP-event-timed
+    launches each."""
     import numpy as np
     import torch
     from paged_kv_cache_08_amd import pkv as P
-    tiles = max(1, nbytes // 4096)
+    tiles = max(1, nbytes // tile_bytes)
     g = torch.Generator(device="cuda")
     g.manual_seed(12345)
-    buf = torch.empty(tiles * 1024, dtype=torch.int32, device="cuda").random_(generator=g)
+    buf = torch.empty(tiles * (tile_bytes // 4), dtype=torch.int32, device="cuda").random_(generator=g)
     perm = np.random.default_rng(12345).permutation(tiles).astype(np.int32)
     order = torch.from_numpy(perm).cuda()
-    result = {"kernel": "read_tiles", "bytes": tiles * 4096, "tile_bytes": 4096}
+    result = {"kernel": "read_tiles", "bytes": tiles * tile_bytes, "tile_bytes": tile_bytes}
     for mode, o in (("gather", order), ("stream", None)):
         best, best_tpw = 0.0, None
         for tpw in (16, 64, 256, 512):
             sink = torch.empty(-(-tiles // tpw) * 64, dtype=torch.int32, device="cuda")
             for _ in range(2):
-                P.pkv_read_tiles(buf, o, tiles, tpw, sink)
+                P.pkv_read_tiles(buf, o, tiles, tpw, sink, tile_bytes=tile_bytes)
             ms = []
             for _ in range(reps):
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record()
-                P.pkv_read_tiles(buf, o, tiles, tpw, sink)
+                P.pkv_read_tiles(buf, o, tiles, tpw, sink, tile_bytes=tile_bytes)
                 e1.record()
                 ms.append((e0, e1))
             torch.cuda.synchronize()
             t = sorted(a.elapsed_time(b) for a, b in ms)[reps // 2] / 1e3
-            rate = tiles * 4096 / t / 1e9
+            rate = tiles * tile_bytes / t / 1e9
             if rate > best:
                 best, best_tpw = rate, tpw
         result[f"{mode}_gbs"] = round(best, 1)
@@ -648,7 +649,9 @@ def main():
     }
     log(f"timed {args.steps} steps: {value:.1f} GB/s; partial kernel {k3_avg_s * 1e6:.1f} us")
     log("read ceiling")
-    ceiling = read_ceiling(int(kv_per_launch))
+    # tiles as the kernel reads them: one (block, KV head) of K or V, 16 x 128
+    # values (2 KiB in 8-bit codes); other shapes use 4 KiB tiles
+    ceiling = read_ceiling(int(kv_per_launch), tile_bytes=2048 if wl.cache_dtype == "fp8" and wl.d == 128 else 4096)
     ceiling["decode_frac_of_gather"] = round(achieved / ceiling["gather_gbs"], 4)
     result["read_ceiling"] = ceiling
     log(f"read ceiling: gather {ceiling['gather_gbs']} GB/s, stream {ceiling['stream_gbs']} GB/s")

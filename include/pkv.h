@@ -415,18 +415,18 @@ int pkv_paged_prefill(const pkv_prefill_args* args, void* stream);
  * A measurement aid, not part of attention («Servicio…presupuesto de
  * memoria» §2: an IO-aware attention kernel is about the memory traffic it
  * causes, so a decode rate is set against what memory delivers for the same
- * access pattern).  Reads n_tiles tiles of 4096 bytes
- * (one KV head's 16 tokens at d = 128, bf16) from the device buffer `base`
- * (base_bytes long, 16-byte aligned): wave w reads tile order[w * tpw + i]
- * for i < tiles_per_wave (tile w * tpw + i when order is NULL), each as
- * 16-byte non-temporal loads, lane l taking the vectors l, l + 64, l + 128,
- * l + 192 of the tile.  sink (device uint32[ceil(n_tiles / tpw) * 64])
+ * access pattern).  Reads n_tiles tiles of tile_bytes bytes, 4096 (one KV
+ * head's 16 tokens at d = 128, bf16) or 2048 (the same in 8-bit codes; else
+ * PKV_ERR_INVALID), from the device buffer `base` (base_bytes long, 16-byte
+ * aligned): wave w reads tile order[w * tpw + i] for i < tiles_per_wave
+ * (tile w * tpw + i when order is NULL), each as 16-byte non-temporal
+ * loads, lane l taking the vectors l, l + 64, ... of the tile.  sink (device uint32[ceil(n_tiles / tpw) * 64])
  * receives, per wave and lane, the xor of every 32-bit word the lane read.
  * order (device int32[n_tiles]) may hold any ids; ids outside the buffer
- * read nothing.  Without order, n_tiles * 4096 must fit in base_bytes
- * (else PKV_ERR_INVALID).  One kernel on `stream`.                        */
-int pkv_read_tiles(const void* base, int64_t base_bytes, const int32_t* order, int64_t n_tiles,
-                   int32_t tiles_per_wave, uint32_t* sink, void* stream);
+ * read nothing.  Without order, n_tiles * tile_bytes must fit in
+ * base_bytes (else PKV_ERR_INVALID).  One kernel on `stream`.             */
+int pkv_read_tiles(const void* base, int64_t base_bytes, int32_t tile_bytes, const int32_t* order,
+                   int64_t n_tiles, int32_t tiles_per_wave, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -2,8 +2,8 @@
 // launch reads, with the attention arithmetic taken away?
 //
 // The decode partial kernel reads each sequence's KV cache as 4 KiB tiles
-// (16 tokens of one KV head at d = 128, bf16) scattered through the pool in
-// block-table order.  This kernel reads the same kind of tiles from a buffer,
+// (16 tokens of one KV head at d = 128, bf16; 2 KiB with 8-bit codes)
+// scattered through the pool in block-table order.  This kernel reads the same kind of tiles from a buffer,
 // in an order given by the caller (a seeded permutation for the gather, none
 // for a contiguous stream), with non-temporal 16-byte loads and nothing else
 // per byte than an xor, so its rate is the ceiling that access pattern allows
@@ -16,13 +16,15 @@ namespace pkv {
 
 namespace {
 
-constexpr int kTileVecs = kReadTileBytes / 16;      // 16-byte vectors per tile: 4 per lane
 constexpr int kReadDepth = 8;                       // tiles in flight per wave
 
 __device__ __forceinline__ int64_t tile_id(const int32_t* order, int64_t i) {
   return order ? static_cast<int64_t>(order[i]) : i;
 }
 
+// kTileVecs: 16-byte vectors per tile (256 for 4 KiB, 128 for 2 KiB); lane l
+// reads vectors l, l + 64, ... of each tile.
+template <int kTileVecs>
 __global__ __launch_bounds__(64) void read_tiles_kernel(const u32x4* __restrict__ base, int64_t base_tiles,
                                                         const int32_t* __restrict__ order, int64_t n_tiles,
                                                         int tiles_per_wave, uint32_t* __restrict__ sink) {
@@ -47,7 +49,7 @@ __global__ __launch_bounds__(64) void read_tiles_kernel(const u32x4* __restrict_
 #pragma unroll
       for (int c = 0; c < kTileVecs / 64; ++c) v[u][c] = __builtin_nontemporal_load(src + 64 * c);
     }
-    __builtin_amdgcn_sched_barrier(0);        // all 32 loads leave before the first is consumed
+    __builtin_amdgcn_sched_barrier(0);        // all loads leave before the first is consumed
 #pragma unroll
     for (int u = 0; u < kReadDepth; ++u)
 #pragma unroll
@@ -65,11 +67,19 @@ __global__ __launch_bounds__(64) void read_tiles_kernel(const u32x4* __restrict_
 
 }  // namespace
 
-hipError_t launch_read_tiles(const void* base, int64_t base_tiles, const int32_t* order, int64_t n_tiles,
-                             int tiles_per_wave, uint32_t* sink, hipStream_t stream) {
+hipError_t launch_read_tiles(const void* base, int64_t base_tiles, int tile_bytes, const int32_t* order,
+                             int64_t n_tiles, int tiles_per_wave, uint32_t* sink, hipStream_t stream) {
   const int64_t waves = (n_tiles + tiles_per_wave - 1) / tiles_per_wave;
-  hipLaunchKernelGGL(read_tiles_kernel, dim3(static_cast<unsigned>(waves)), dim3(64), 0, stream,
-                     static_cast<const u32x4*>(base), base_tiles, order, n_tiles, tiles_per_wave, sink);
+  const dim3 grid(static_cast<unsigned>(waves));
+  const u32x4* b = static_cast<const u32x4*>(base);
+  if (tile_bytes == 4096)
+    hipLaunchKernelGGL(read_tiles_kernel<256>, grid, dim3(64), 0, stream, b, base_tiles, order, n_tiles,
+                       tiles_per_wave, sink);
+  else if (tile_bytes == 2048)
+    hipLaunchKernelGGL(read_tiles_kernel<128>, grid, dim3(64), 0, stream, b, base_tiles, order, n_tiles,
+                       tiles_per_wave, sink);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -805,16 +805,17 @@ int pkv_paged_prefill(const pkv_prefill_args* a, void* stream) {
   return from_hip(pkv::launch_prefill(p, static_cast<hipStream_t>(stream)), "prefill");
 }
 
-int pkv_read_tiles(const void* base, int64_t base_bytes, const int32_t* order, int64_t n_tiles,
+int pkv_read_tiles(const void* base, int64_t base_bytes, int32_t tile_bytes, const int32_t* order, int64_t n_tiles,
                    int32_t tiles_per_wave, uint32_t* sink, void* stream) {
-  if (!base || !sink || base_bytes < pkv::kReadTileBytes || n_tiles < 1 || tiles_per_wave < 1)
+  if (tile_bytes != 2048 && tile_bytes != 4096) return fail(PKV_ERR_INVALID, "read_tiles: tile_bytes must be 2048 or 4096");
+  if (!base || !sink || base_bytes < tile_bytes || n_tiles < 1 || tiles_per_wave < 1)
     return fail(PKV_ERR_INVALID, "read_tiles: bad argument");
   if (!aligned16(base)) return fail(PKV_ERR_INVALID, "read_tiles: base must be 16-byte aligned");
-  const int64_t base_tiles = base_bytes / pkv::kReadTileBytes;
+  const int64_t base_tiles = base_bytes / tile_bytes;
   if (!order && n_tiles > base_tiles) return fail(PKV_ERR_INVALID, "read_tiles: n_tiles exceeds the buffer");
   if ((n_tiles + tiles_per_wave - 1) / tiles_per_wave > 0x7fffffffLL)
     return fail(PKV_ERR_INVALID, "read_tiles: grid too large");
-  return from_hip(pkv::launch_read_tiles(base, base_tiles, order, n_tiles, tiles_per_wave, sink,
+  return from_hip(pkv::launch_read_tiles(base, base_tiles, tile_bytes, order, n_tiles, tiles_per_wave, sink,
                                          static_cast<hipStream_t>(stream)),
                   "read_tiles");
 }

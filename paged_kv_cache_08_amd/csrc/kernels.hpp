@@ -191,10 +191,9 @@ hipError_t plan_decode_partial(const DecodeParams& p, int kind, DecodeLaunchPlan
 hipError_t launch_decode_reduce(const DecodeParams& p, int kind, hipStream_t stream);
 bool decode_shape_supported(int kind, int head_dim, int block_size);
 // Read-bandwidth calibration: wave w reads tiles order[w*tpw ...] (or
-// w*tpw ... without an order) of kReadTileBytes each and writes the xor of
-// what each lane read to sink[w*64 + lane].
-constexpr int kReadTileBytes = 4096;
-hipError_t launch_read_tiles(const void* base, int64_t base_tiles, const int32_t* order, int64_t n_tiles,
-                             int tiles_per_wave, uint32_t* sink, hipStream_t stream);
+// w*tpw ... without an order) of tile_bytes (2048 or 4096) each and writes
+// the xor of what each lane read to sink[w*64 + lane].
+hipError_t launch_read_tiles(const void* base, int64_t base_tiles, int tile_bytes, const int32_t* order,
+                             int64_t n_tiles, int tiles_per_wave, uint32_t* sink, hipStream_t stream);
 
 }  // namespace pkv

@@ -116,7 +116,7 @@ SIGNATURES = [
     ("pkv_decode_fuses_append", ctypes.c_int, [_P(pkv_decode_args)]),
     ("pkv_decode_plan", ctypes.c_int, [_P(pkv_decode_args), _P(pkv_decode_plan_info), _P(_i32), _i64]),
     ("pkv_paged_prefill", ctypes.c_int, [_P(pkv_prefill_args), _vp]),
-    ("pkv_read_tiles", ctypes.c_int, [_vp, _i64, _vp, _i64, _i32, _vp, _vp]),
+    ("pkv_read_tiles", ctypes.c_int, [_vp, _i64, _i32, _vp, _i64, _i32, _vp, _vp]),
 ]
 
 
@@ -513,14 +513,16 @@ def pkv_paged_prefill(args: pkv_prefill_args, stream=None) -> None:
 
 
 
-def pkv_read_tiles(base, order, n_tiles: int, tiles_per_wave: int, sink, stream=None) -> None:
+def pkv_read_tiles(base, order, n_tiles: int, tiles_per_wave: int, sink, stream=None,
+                   tile_bytes: int = 4096) -> None:
     """Read-bandwidth calibration: base is a device tensor (any dtype), order
     a device int32 tensor of tile ids or None (contiguous tiles), sink a
-    device int32/uint32 tensor of ceil(n_tiles / tiles_per_wave) * 64 entries."""
+    device int32/uint32 tensor of ceil(n_tiles / tiles_per_wave) * 64 entries;
+    tiles of tile_bytes (4096 or 2048)."""
     waves = -(-n_tiles // tiles_per_wave)
     if sink.numel() < waves * 64 or sink.element_size() != 4:
         raise ValueError("sink needs ceil(n_tiles / tiles_per_wave) * 64 32-bit entries")
     if order is not None and order.numel() < n_tiles:
         raise ValueError("order holds fewer than n_tiles ids")
-    _check(lib().pkv_read_tiles(_ptr(base), base.numel() * base.element_size(), _ptr(order), n_tiles,
+    _check(lib().pkv_read_tiles(_ptr(base), base.numel() * base.element_size(), tile_bytes, _ptr(order), n_tiles,
                                 tiles_per_wave, _ptr(sink), _stream(stream)))

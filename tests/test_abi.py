@@ -173,10 +173,16 @@ def test_prefill_argument_validation(bad, status):
     (8, 1 << 20, 0, 16, 1, 16),             # misaligned buffer
     (16, 1 << 20, 0, 257, 1, 16),           # contiguous read past the buffer (256 tiles)
 ])
-def test_read_tiles_argument_validation(args):
+@pytest.mark.parametrize("tile_bytes", [4096, 1024, 3000])
+def test_read_tiles_argument_validation(args, tile_bytes):
     base, nbytes, order, n, tpw, sink = args
-    status = P.lib().pkv_read_tiles(base, nbytes, order, n, tpw, sink, 0)
+    status = P.lib().pkv_read_tiles(base, nbytes, tile_bytes, order, n, tpw, sink, 0)
     assert status == P.PKV_ERR_INVALID
+
+
+def test_read_tiles_2k_tiles_count_against_the_buffer():
+    # 513 tiles of 2 KiB do not fit in 1 MiB; with no device the valid call is not made
+    assert P.lib().pkv_read_tiles(16, 1 << 20, 2048, 0, 513, 1, 16, 0) == P.PKV_ERR_INVALID
 
 
 @pytest.mark.parametrize("kw,fused", [

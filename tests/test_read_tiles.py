@@ -11,27 +11,28 @@ pytestmark = pytest.mark.gpu
 TILE_WORDS = 4096 // 4
 
 
-def expected_sink(words: np.ndarray, order, n_tiles: int, tpw: int) -> np.ndarray:
-    """words: the buffer as uint32 [tiles * 1024]; lane l of a wave reads the
-    16-byte vectors l, l + 64, l + 128, l + 192 of each of its tiles."""
-    tiles = words.reshape(-1, 4, 64, 4)                  # [tile][vector group c][lane][word]
+def expected_sink(words: np.ndarray, order, n_tiles: int, tpw: int, tile_bytes: int = 4096) -> np.ndarray:
+    """words: the buffer as uint32 [tiles * tile_bytes / 4]; lane l of a wave
+    reads the 16-byte vectors l, l + 64, ... of each of its tiles."""
+    groups = tile_bytes // 1024                          # 16-byte vectors per lane
+    tiles = words.reshape(-1, groups, 64, 4)             # [tile][vector group c][lane][word]
     ids = np.arange(n_tiles) if order is None else np.asarray(order, dtype=np.int64)[:n_tiles]
     waves = -(-n_tiles // tpw)
     out = np.zeros((waves, 64), dtype=np.uint32)
     for w in range(waves):
         for t in ids[w * tpw:(w + 1) * tpw]:
             if 0 <= t < tiles.shape[0]:
-                out[w] ^= np.bitwise_xor.reduce(tiles[t].reshape(4, 64, 4).transpose(1, 0, 2).reshape(64, 16), axis=1)
+                out[w] ^= np.bitwise_xor.reduce(tiles[t].transpose(1, 0, 2).reshape(64, 4 * groups), axis=1)
     return out.reshape(-1)
 
 
-def run(words: np.ndarray, order, n_tiles: int, tpw: int) -> np.ndarray:
+def run(words: np.ndarray, order, n_tiles: int, tpw: int, tile_bytes: int = 4096) -> np.ndarray:
     from paged_kv_cache_08_amd import pkv as P
     buf = torch.from_numpy(words.view(np.int32)).cuda()
     dorder = None if order is None else torch.from_numpy(np.asarray(order, dtype=np.int32)).cuda()
     waves = -(-n_tiles // tpw)
     sink = torch.full((waves * 64,), -1, dtype=torch.int32, device="cuda")
-    P.pkv_read_tiles(buf, dorder, n_tiles, tpw, sink)
+    P.pkv_read_tiles(buf, dorder, n_tiles, tpw, sink, tile_bytes=tile_bytes)
     torch.cuda.synchronize()
     return sink.cpu().numpy().view(np.uint32)
 
@@ -43,12 +44,13 @@ def run(words: np.ndarray, order, n_tiles: int, tpw: int) -> np.ndarray:
     (300, 257, 7, True),       # fewer tiles than the permutation, tiny waves
     (5, 5, 256, True),         # one wave, remainder loop only
 ])
-def test_read_tiles_xor(tiles, n, tpw, gather):
+@pytest.mark.parametrize("tile_bytes", [4096, 2048])
+def test_read_tiles_xor(tiles, n, tpw, gather, tile_bytes):
     rng = np.random.default_rng(tiles * 1000 + n + tpw)
-    words = rng.integers(0, 2**32, size=tiles * TILE_WORDS, dtype=np.uint32)
+    words = rng.integers(0, 2**32, size=tiles * tile_bytes // 4, dtype=np.uint32)
     order = rng.permutation(tiles).astype(np.int32) if gather else None
-    got = run(words, order, n, tpw)
-    np.testing.assert_array_equal(got, expected_sink(words, order, n, tpw))
+    got = run(words, order, n, tpw, tile_bytes)
+    np.testing.assert_array_equal(got, expected_sink(words, order, n, tpw, tile_bytes))
 
 
 def test_read_tiles_ids_outside_buffer_read_nothing():
