@@ -15,8 +15,17 @@ attention per second (decimal GB/s) over the timed steps.  The *_fp8
 configurations keep the same batch in an 8-bit E4M3 cache (bf16 tokens and
 queries; KV bytes count the codes and the per-token scales).
 
+Before any timing, the first decode step (same path and inputs as the
+timed ones) is checked against the oracle on a few sequences (every query
+head; allocator state and those sequences' pool bytes exactly, outputs
+within the tolerance); the result is the line's `parity` record, and a
+mismatch ends the run with status 3.  The default run also reports the
+32-layer step (256 sequences, MHA) under `full_step`: ms per step, decode
+tokens/s, KV GB/s and the partial kernel's rate, validated the same way.
+
 Prints one JSON line.  Options: --gpus N (only 1 is supported), --steps K,
---warmup W, --config NAME, --no-cpu-baseline, --cpu-seconds S.
+--warmup W, --config NAME, --no-cpu-baseline (also skips the validation),
+--no-full-step, --cpu-seconds S.
 """
 from __future__ import annotations
 
@@ -63,6 +72,8 @@ def parse():
     ap.add_argument("--flush", action="store_true",
                     help="write a 1 GiB buffer before every decode step, outside its timing, to evict L2 and the "
                          "MALL; value and step time then come from events around each step")
+    ap.add_argument("--no-full-step", action="store_true",
+                    help="leave out the 32-layer step that the default (long-context) run also reports")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 1 GiB device copies (known bytes) for counter scaling")
     return ap.parse_args()
@@ -463,6 +474,121 @@ def run_prefill(args, wl):
     print(json.dumps(result), flush=True)
 
 
+def _bits(t):
+    """Raw bit patterns of a CPU tensor (uint32 for fp32, uint16 for bf16)."""
+    import numpy as np
+    import torch
+    t = t.detach().cpu().contiguous()
+    return (t.view(torch.int32).numpy().view(np.uint32) if t.dtype == torch.float32
+            else t.view(torch.int16).numpy().view(np.uint16))
+
+
+def validate_first_step(bench, layers, seqs, atol: float = 2e-2, row_rtol: float = 1e-2):
+    """The oracle leg, before anything is timed: runs the first decode step
+    (the path and inputs the timed steps use, its new token included) and
+    compares it with the oracle on the batch rows `seqs`, every query head,
+    in `layers`.  The oracle replays the setup through its own allocator
+    and pool (writing only those sequences' tokens) and the step's append,
+    then decodes.  Checked: the allocator state bit for bit, the pool bytes
+    of those sequences (every written slot, new token included) bit for bit,
+    and the outputs within max |err| <= atol and row-normwise <= row_rtol.
+    Returns the parity record; exits with status 3 on a mismatch."""
+    import numpy as np
+    import torch
+    from oracle import attention as OA
+    from oracle.pool import to_f64
+    from oracle.replay import Replay
+
+    wl = bench.wl
+    bench.step(record_events=False)
+    torch.cuda.synchronize()
+    entries = wl.step_ops[0][1]                       # (id, logical sequence, position) per batch row
+    srcs = {entries[i][1] for i in seqs}
+    rp = Replay(wl, layers=max(layers) + 1)
+    vals = {}
+    for l in layers:
+        _, k, v = wl.tensors(l, device=bench.dev)
+        vals[l] = (_bits(k), _bits(v))
+        del k, v
+    rp.run(wl.setup_ops, vals, sources=srcs)
+    del vals
+    slots, cow = rp.alloc.append(list(bench.ids))
+    for a, b in cow:
+        rp.pool.copy_block(a, b)
+    sel = np.asarray(seqs)
+    for l in layers:
+        rp.pool.scatter(l, np.asarray(slots)[sel], _bits(bench.knew[l][0])[sel], _bits(bench.vnew[l][0])[sel])
+    if bench.window:
+        B = wl.block
+        for sid in bench.ids:
+            start = rp.alloc.length(sid) - bench.window
+            if start > 0 and start % B == 0:
+                rp.alloc.release_before(sid, start)
+    problems = []
+    if bench.eng.snapshot() != tuple(rp.alloc.snapshot()):
+        problems.append("allocator state differs")
+    tables, lengths = rp.tables(), rp.lengths()
+    worst_abs, worst_rel = 0.0, 0.0
+    for l in layers:
+        # pool bytes of the checked sequences: every written slot
+        pool = rp.pool
+        pairs = [(pool.K[l], bench.eng.k[l]), (pool.V[l], bench.eng.v[l])]
+        if pool.dtype == "fp8":
+            pairs += [(pool.KS[l], bench.eng.ks[l]), (pool.VS[l], bench.eng.vs[l])]
+        B = wl.block
+        for ref, dev in pairs:
+            ours = (dev.cpu().numpy() if dev.dtype == torch.uint8 else _bits(dev)).reshape(ref.shape)
+
+            def slot(arr, b, o):                  # token slot o of block b, every head and value
+                if arr.ndim == 3:                                            # scales [block][head][slot]
+                    return arr[b][:, o]
+                if pool.dtype == "fp8" and arr.ndim == 7:                    # [block][head][a][u][c][b][w]
+                    return arr[b][:, :, o // 4, :, :, o % 4]
+                if arr.ndim == 4:                                            # V [block][head][d][slot]
+                    return arr[b][..., o]
+                return arr[b][:, :, o]                                       # K [block][head][d/x][slot][x]
+
+            for i in seqs:
+                n = lengths[i]
+                t0 = max(0, n - bench.window) if bench.window else 0
+                whole = [tables[i][j] for j in range(-(-t0 // B), n // B)]  # blocks written in full
+                if whole and not np.array_equal(ours[whole], ref[whole]):
+                    problems.append(f"layer {l}: pool blocks of batch row {i} differ")
+                edge = [t for t in range(t0, n) if t < -(-t0 // B) * B or t >= (n // B) * B]
+                for t in edge:
+                    b, o = tables[i][t // B], t % B
+                    if not np.array_equal(slot(ours, b, o), slot(ref, b, o)):
+                        problems.append(f"layer {l}: pool slot {t} of batch row {i} differs")
+                        break
+            del ours
+        q64 = to_f64(_bits(bench.q[l]), wl.dtype)
+        heads = {(i, h) for i in seqs for h in range(wl.Hq)}
+        ref = OA.decode(rp.pool, l, tables, lengths, q64, wl.Hq, heads=heads, window=bench.window)
+        got = bench.out[l].float().cpu().double().numpy()
+        g = np.concatenate([got[i] for i in seqs])
+        r = np.concatenate([ref[i] for i in seqs])
+        if not np.all(np.isfinite(g)):
+            problems.append(f"layer {l}: non-finite outputs")
+            continue
+        err = np.abs(g - r)
+        worst_abs = max(worst_abs, float(err.max()))
+        worst_rel = max(worst_rel, float((err.max(axis=1) / np.maximum(np.abs(r).max(axis=1), 1e-300)).max()))
+    if worst_abs > atol or worst_rel > row_rtol:
+        problems.append(f"outputs beyond tolerance: max_abs {worst_abs:.3e}, row_rel {worst_rel:.3e}")
+    record = {"checked": "first decode step, before timing, against the oracle",
+              "layers": list(layers), "batch_rows": list(map(int, seqs)), "rows": len(seqs) * wl.Hq * len(layers),
+              "max_abs": worst_abs, "row_rel": worst_rel, "atol": atol, "row_rtol": row_rtol,
+              "allocator": "bit-exact" if "allocator state differs" not in problems else "differs",
+              "pool": "checked sequences' slots bit-exact" if not any("pool" in p for p in problems) else "differs",
+              "pass": not problems}
+    if problems:
+        log("VALIDATION FAILED: " + "; ".join(problems[:5]))
+        print(json.dumps({"metric": METRIC, "value": None, "parity": record, "errors": problems[:20]}), flush=True)
+        sys.exit(3)
+    log(f"validated the first step on {record['rows']} rows: max_abs {worst_abs:.3e}, row_rel {worst_rel:.3e}")
+    return record
+
+
 def cpu_baseline(wl_name: str, seconds: float, window: int = 0):
     """The oracle (unchanged) on a bounded sample of the same workload:
     a few of its sequences, one decode step at a time (allocator append,
@@ -584,34 +710,11 @@ def main():
     if wl.chunk is not None:
         run_prefill(args, wl)
         return
-    total = args.warmup + args.steps
-    log(f"setup {wl.description}")
-    bench = DecodeBench(wl, total, partition=args.partition, window=args.window,
-                        fused_append=not args.separate_append)
-    if args.flush:
-        bench.enable_flush()
-    log("setup done; warmup")
-    for _ in range(args.warmup):
-        bench.step(record_events=False)
-    torch.cuda.synchronize()
-    log("timed steps")
-    bench.kv_bytes.clear()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        bench.step(record_events=True)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-
-    kv_total = sum(bench.kv_bytes)
+    bench, t = run_decode(args, wl)
+    elapsed, value, k3_ms, k3_avg_s, kv_per_launch, achieved = (t[k] for k in (
+        "elapsed", "value", "k3_ms", "k3_avg_s", "kv_per_launch", "achieved"))
     logical = bench.attended_bytes(0)              # the last step's bytes per layer, logical and unique
     unique = bench.unique_bytes()
-    if args.flush:      # the flush writes are not part of the step
-        elapsed = sum(a.elapsed_time(b) for a, b in bench.step_events) / 1e3
-    value = kv_total / elapsed / 1e9
-    k3_ms = [a.elapsed_time(b) for a, b, _ in bench.events]
-    k3_avg_s = sum(k3_ms) / len(k3_ms) / 1e3
-    kv_per_launch = sum(n for _, _, n in bench.events) / len(bench.events)   # bytes of the timed launches
-    achieved = kv_per_launch / k3_avg_s / 1e9
     traffic_bytes = load_traffic(args.config) if not args.window else None
     traffic = None if traffic_bytes is None else round(traffic_bytes / k3_avg_s / 1e9, 2)
     result = {
@@ -639,7 +742,10 @@ def main():
         "kv_bytes_unique_per_layer": unique,
         "value_unique_bytes": round(value * unique / logical, 2),
         "cache_assisted": unique < logical,
-        "decode_tokens_per_s": round(wl.S * args.steps / elapsed, 1),
+        # a model step runs every layer: tokens/s of a one-layer batch is a per-layer rate
+        ("decode_tokens_per_s" if wl.layers > 1 else "decode_tokens_per_s_one_layer"):
+            round(wl.S * args.steps / elapsed, 1),
+        "parity": t["parity"],
         "roofline": {"bound": "hbm", "kernel": "decode_partial", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "traffic_bytes_per_launch": traffic_bytes,
@@ -649,16 +755,84 @@ def main():
     }
     log(f"timed {args.steps} steps: {value:.1f} GB/s; partial kernel {k3_avg_s * 1e6:.1f} us")
     log("read ceiling")
-    # tiles as the kernel reads them: one (block, KV head) of K or V, 16 x 128
-    # values (2 KiB in 8-bit codes); other shapes use 4 KiB tiles
-    ceiling = read_ceiling(int(kv_per_launch), tile_bytes=2048 if wl.cache_dtype == "fp8" and wl.d == 128 else 4096)
+    # tiles as the kernel reads them: one (block, KV head) of K or V, 16 x d values
+    tile = 16 * wl.d * {"f32": 4, "bf16": 2, "fp8": 1}[wl.cache_dtype]
+    ceiling = read_ceiling(int(kv_per_launch), tile_bytes=tile if tile in (1024, 2048, 4096) else 4096)
     ceiling["decode_frac_of_gather"] = round(achieved / ceiling["gather_gbs"], 4)
     result["read_ceiling"] = ceiling
     log(f"read ceiling: gather {ceiling['gather_gbs']} GB/s, stream {ceiling['stream_gbs']} GB/s")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds, args.window)
+    if args.config == "long_context" and not args.window and not args.no_full_step:
+        del bench
+        torch.cuda.empty_cache()
+        result["full_step"] = full_step_extra(args)
     print(json.dumps(result), flush=True)
+
+
+def run_decode(args, wl):
+    """Set up a decode batch, validate its first step against the oracle
+    (unless --no-cpu-baseline), run the warmup steps, then time args.steps
+    steps.  Returns the bench and its timings."""
+    import torch
+    total = args.warmup + args.steps + 1           # + the validated first step
+    log(f"setup {wl.description}")
+    bench = DecodeBench(wl, total, partition=args.partition, window=args.window,
+                        fused_append=not args.separate_append)
+    if args.flush:
+        bench.enable_flush()
+    parity = None
+    if args.no_cpu_baseline:
+        bench.step(record_events=False)
+    else:
+        log("validating the first step against the oracle")
+        longest = int(max(range(wl.S), key=lambda i: wl.lengths[i]))
+        shortest = int(min(range(wl.S), key=lambda i: wl.lengths[i]))
+        seqs = sorted({0, wl.S // 2, wl.S - 1, longest, shortest})
+        layers = sorted({0, wl.layers - 1})
+        parity = validate_first_step(bench, layers, seqs)
+    log("warmup")
+    for _ in range(args.warmup):
+        bench.step(record_events=False)
+    torch.cuda.synchronize()
+    log("timed steps")
+    bench.kv_bytes.clear()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        bench.step(record_events=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    if args.flush:      # the flush writes are not part of the step
+        elapsed = sum(a.elapsed_time(b) for a, b in bench.step_events) / 1e3
+    k3_ms = [a.elapsed_time(b) for a, b, _ in bench.events]
+    k3_avg_s = sum(k3_ms) / len(k3_ms) / 1e3
+    kv_per_launch = sum(n for _, _, n in bench.events) / len(bench.events)   # bytes of the timed launches
+    return bench, {"elapsed": elapsed, "value": sum(bench.kv_bytes) / elapsed / 1e9, "k3_ms": k3_ms,
+                   "k3_avg_s": k3_avg_s, "kv_per_launch": kv_per_launch,
+                   "achieved": kv_per_launch / k3_avg_s / 1e9, "parity": parity}
+
+
+def full_step_extra(args):
+    """The 32-layer decode step (256 sequences, MHA) in the same run as the
+    headline: the metric's decode tokens/s is a model step's rate."""
+    import workloads
+    wl = workloads.full_step()
+    bench, t = run_decode(args, wl)
+    out = {"workload": wl.name, "description": wl.description, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(t["elapsed"] / args.steps * 1e3, 4),
+           "decode_tokens_per_s": round(wl.S * args.steps / t["elapsed"], 1),
+           "kv_gbs": round(t["value"], 2), "pct_hbm_peak": round(100 * t["value"] / HBM_PEAK_GBS, 2),
+           "append": "fused into the decode kernel" if bench.fused_append else "separate kernel",
+           "partial_kernel": {"avg_launch_us": round(t["k3_avg_s"] * 1e6, 2), "launch_us": launch_stats_us(t["k3_ms"]),
+                              "launches_timed": len(t["k3_ms"]), "achieved": round(t["achieved"], 2),
+                              "frac": round(t["achieved"] / HBM_PEAK_GBS, 4),
+                              "algorithmic_bytes_per_launch": int(t["kv_per_launch"])},
+           "parity": t["parity"]}
+    log(f"full step: {out['ms_per_step']} ms/step, {out['decode_tokens_per_s']} tokens/s, "
+        f"{out['kv_gbs']} GB/s; partial kernel {out['partial_kernel']['avg_launch_us']} us")
+    del bench
+    return out
 
 
 if __name__ == "__main__":

@@ -416,8 +416,9 @@ int pkv_paged_prefill(const pkv_prefill_args* args, void* stream);
  * memoria» §2: an IO-aware attention kernel is about the memory traffic it
  * causes, so a decode rate is set against what memory delivers for the same
  * access pattern).  Reads n_tiles tiles of tile_bytes bytes, 4096 (one KV
- * head's 16 tokens at d = 128, bf16) or 2048 (the same in 8-bit codes; else
- * PKV_ERR_INVALID), from the device buffer `base` (base_bytes long, 16-byte
+ * head's 16 tokens at d = 128, bf16), 2048 (the same in 8-bit codes, or at
+ * d = 64 in bf16) or 1024 (8-bit codes at d = 64); else PKV_ERR_INVALID,
+ * from the device buffer `base` (base_bytes long, 16-byte
  * aligned): wave w reads tile order[w * tpw + i] for i < tiles_per_wave
  * (tile w * tpw + i when order is NULL), each as 16-byte non-temporal
  * loads, lane l taking the vectors l, l + 64, ... of the tile.  sink (device uint32[ceil(n_tiles / tpw) * 64])

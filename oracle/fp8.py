@@ -20,8 +20,10 @@ here (the library follows the same ones):
   the nearest E4M3 value, ties to the even code; the value a code stands for
   is ``value(code) · s`` (exact in fp64).
 
-Plain definitions, slow on purpose: the value table is built from the bit
-fields, and rounding picks the nearest table entry.
+Plain definitions: the value table is built from the bit fields; rounding
+is defined by picking the nearest table entry (``encode_nearest``) and done,
+for whole pools, by the equivalent rounding onto the format's grid
+(``encode``), which the tests hold equal to the table search.
 """
 from __future__ import annotations
 
@@ -55,10 +57,11 @@ def decode(codes: np.ndarray) -> np.ndarray:
     return VALUES[np.asarray(codes, dtype=np.int64) & 0xFF]
 
 
-def encode(y: np.ndarray) -> np.ndarray:
-    """Nearest E4M3 code to each value of ``y`` (ties to the even code).
-    |y| beyond the rounding range of 448 (that is, > 464) gives NaN (0x7F /
-    0xFF); the sign of zero is kept."""
+def encode_nearest(y: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 code to each value of ``y`` (ties to the even code),
+    found by searching the value table.  |y| beyond the rounding range of
+    448 (that is, > 464) gives NaN (0x7F / 0xFF); the sign of zero is kept.
+    The plain definition; ``encode`` reaches the same codes faster."""
     y = np.asarray(y, dtype=np.float64)
     a = np.abs(y)
     # index of the first table value >= a; compare with its lower neighbour
@@ -75,6 +78,43 @@ def encode(y: np.ndarray) -> np.ndarray:
     return (mag | sign).astype(np.uint8)
 
 
+def _binade(a: np.ndarray) -> np.ndarray:
+    """floor(log2 a) for finite a > 0 (any value for a = 0), from the fp64
+    exponent field (exact: every fp32 value is normal in fp64)."""
+    return ((a.view(np.uint64) >> np.uint64(52)).astype(np.int64) & 0x7FF) - 1023
+
+
+def _pow2(e: np.ndarray) -> np.ndarray:
+    """2.0 ** e for integer arrays e in the fp64 normal range."""
+    return ((e + 1023).astype(np.uint64) << np.uint64(52)).view(np.float64)
+
+
+def encode(y: np.ndarray) -> np.ndarray:
+    """The same codes as ``encode_nearest``, by rounding onto the format's
+    grid: in the binade [2^e, 2^(e+1)) (e >= -6; below 2^-6 the subnormals
+    keep the spacing of e = -6) representable magnitudes are the multiples of
+    2^(e-3), so |y| rounds to rint(|y| / 2^(e-3)) * 2^(e-3) (round half to
+    even on the multiple; an even multiple is an even code, also where the
+    result reaches the next binade).  A result of 480 or more is past 448:
+    NaN.  Scaling by powers of two is exact in fp64."""
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    a = np.abs(y)
+    nan = ~(a < MAX + 32.0)                             # NaN, or surely past 448
+    a = np.where(nan, 0.0, a)
+    e = np.maximum(_binade(a), -6)
+    m = np.rint(a * _pow2(3 - e))                       # the rounded multiple of 2^(e-3): 0 .. 16
+    # code fields: a multiple below 8 is a subnormal (e = -6) or zero; 16 is
+    # the next binade's 8
+    up = m >= 16
+    e = e + up
+    m = np.where(up, 8, m).astype(np.int64)
+    normal = m >= 8
+    mag = np.where(normal, ((e + 7) << 3) | (m - 8), m)
+    mag = np.where(nan | (mag > 0x7E), 0x7F, mag)       # 480 and above: NaN
+    sign = np.where(np.signbit(y), 0x80, 0x00)
+    return (mag | sign).astype(np.uint8)
+
+
 def quantize_rows(x: np.ndarray):
     """(codes uint8 [..., d], scales float32 [...]) of rows of fp32 values
     (the last axis is the row), each row by the readings above."""
@@ -83,7 +123,13 @@ def quantize_rows(x: np.ndarray):
     scale = (amax / np.float32(MAX)).astype(np.float32)             # IEEE fp32 division
     safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
     y = (x / safe[..., None]).astype(np.float32)                    # IEEE fp32 division
-    codes = np.where(scale[..., None] > 0, encode(y), np.uint8(0)).astype(np.uint8)
+    # encode element by element (in pieces that stay in the host caches)
+    flat = y.reshape(-1)
+    codes = np.empty(flat.shape, dtype=np.uint8)
+    piece = 1 << 16
+    for i in range(0, flat.size, piece):
+        codes[i:i + piece] = encode(flat[i:i + piece])
+    codes = np.where(scale[..., None] > 0, codes.reshape(y.shape), np.uint8(0)).astype(np.uint8)
     return codes, scale
 
 

@@ -1,8 +1,9 @@
 // Read-bandwidth calibration: how fast can this GPU read the bytes a decode
 // launch reads, with the attention arithmetic taken away?
 //
-// The decode partial kernel reads each sequence's KV cache as 4 KiB tiles
-// (16 tokens of one KV head at d = 128, bf16; 2 KiB with 8-bit codes)
+// The decode partial kernel reads each sequence's KV cache as tiles of 16
+// tokens of one KV head (4 KiB at d = 128 in bf16, 2 KiB in 8-bit codes or
+// at d = 64 in bf16, 1 KiB in 8-bit codes at d = 64)
 // scattered through the pool in block-table order.  This kernel reads the same kind of tiles from a buffer,
 // in an order given by the caller (a seeded permutation for the gather, none
 // for a contiguous stream), with non-temporal 16-byte loads and nothing else
@@ -22,7 +23,7 @@ __device__ __forceinline__ int64_t tile_id(const int32_t* order, int64_t i) {
   return order ? static_cast<int64_t>(order[i]) : i;
 }
 
-// kTileVecs: 16-byte vectors per tile (256 for 4 KiB, 128 for 2 KiB); lane l
+// kTileVecs: 16-byte vectors per tile (256, 128 or 64 for 4, 2 or 1 KiB); lane l
 // reads vectors l, l + 64, ... of each tile.
 template <int kTileVecs>
 __global__ __launch_bounds__(64) void read_tiles_kernel(const u32x4* __restrict__ base, int64_t base_tiles,
@@ -77,6 +78,9 @@ hipError_t launch_read_tiles(const void* base, int64_t base_tiles, int tile_byte
                        tiles_per_wave, sink);
   else if (tile_bytes == 2048)
     hipLaunchKernelGGL(read_tiles_kernel<128>, grid, dim3(64), 0, stream, b, base_tiles, order, n_tiles,
+                       tiles_per_wave, sink);
+  else if (tile_bytes == 1024)
+    hipLaunchKernelGGL(read_tiles_kernel<64>, grid, dim3(64), 0, stream, b, base_tiles, order, n_tiles,
                        tiles_per_wave, sink);
   else
     return hipErrorInvalidValue;

@@ -10,6 +10,7 @@
 #include <array>
 #include <climits>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <exception>
 #include <new>
@@ -234,25 +235,31 @@ void build_order(const pkv_decode_args* a, pkv::DecodeParams* p) {
 }
 
 // Largest batch, in (sequence, KV head) rows, whose new tokens the partial
-// kernel writes itself.  Each row's token is a scatter of partial-sector
-// writes; a few hundred of them cost the streaming reads little, and the
-// fused call saves the append launch and the gap after it (long context,
-// 128 rows: 1-2% of the step).  With thousands of rows (a 256-sequence
-// 32-head batch: 8192) the writes mixed into the read stream cost the
-// partial kernel 25-33 us, more than the separate append kernel (20 us)
-// and its gap.
+// kernel writes itself (PKV_FUSED_APPEND_MAX_ROWS overrides it).  The
+// appending waves hold the token in registers from their set-up on, use it in
+// place of the token's slot when their last block arrives, and write it to
+// the pool after their last load, so neither a wait nor a load depends on
+// those writes.
 constexpr int64_t kFusedAppendMaxRows = 1024;
 
-// The partial kernel.  With a fused append and more than 16 query heads per
-// KV head (several waves read a sequence's last block) or more than
-// kFusedAppendMaxRows rows, the append kernel (the pkv_kv_append_last path)
-// runs first and the partial kernel only reads.
-bool fuses_append(const pkv::DecodeParams& p) {
-  return p.k_new && p.G <= 16 && static_cast<int64_t>(p.S) * p.Hkv <= kFusedAppendMaxRows;
+int64_t fused_append_max_rows() {
+  static const int64_t v = [] {
+    const char* e = std::getenv("PKV_FUSED_APPEND_MAX_ROWS");
+    return e ? std::max<int64_t>(0, std::atoll(e)) : kFusedAppendMaxRows;
+  }();
+  return v;
+}
+
+// The partial kernel writes the new tokens (k_new) itself for bf16 and 8-bit
+// caches up to fused_append_max_rows() rows; otherwise the append kernel
+// (the pkv_kv_append_last path) runs first and the partial kernel only reads.
+// The fp32 cache always takes the append kernel.
+bool fuses_append(const pkv::DecodeParams& p, int kind) {
+  return p.k_new && kind != pkv::kDecodeF32 && static_cast<int64_t>(p.S) * p.Hkv <= fused_append_max_rows();
 }
 
 int run_partial(const pkv_decode_args* a, pkv::DecodeParams& p, int kind, hipStream_t st) {
-  if (p.k_new && !fuses_append(p)) {
+  if (p.k_new && !fuses_append(p, kind)) {
     if (static_cast<int64_t>(a->max_blocks) * a->block_size > 0x7fffffffLL)
       return fail(PKV_ERR_INVALID, "decode: max_blocks too large");
     pkv::AppendParams ap{};
@@ -723,7 +730,7 @@ int pkv_decode_fuses_append(const pkv_decode_args* a) {
   int kind = 0;
   const int rc = prepare_decode(a, &p, &kind);
   if (rc) return rc;
-  return fuses_append(p) ? 1 : 0;
+  return fuses_append(p, kind) ? 1 : 0;
 }
 
 int pkv_decode_plan(const pkv_decode_args* a, pkv_decode_plan_info* info, int32_t* cells, int64_t cap) {
@@ -747,7 +754,7 @@ int pkv_decode_plan(const pkv_decode_args* a, pkv_decode_plan_info* info, int32_
   info->work_list = q.order.active;
   info->run_cap = q.order.active ? q.order.run_cap : 0;
   info->max_wave_blocks = plan.max_wave_blocks;
-  info->fused_append = fuses_append(p) ? 1 : 0;
+  info->fused_append = fuses_append(p, kind) ? 1 : 0;
   info->partitions_bound = q.pmax;
   info->lds_bytes = static_cast<int32_t>(plan.lds_bytes);
   const int64_t n = std::min<int64_t>(cap, plan.cells);
@@ -807,7 +814,8 @@ int pkv_paged_prefill(const pkv_prefill_args* a, void* stream) {
 
 int pkv_read_tiles(const void* base, int64_t base_bytes, int32_t tile_bytes, const int32_t* order, int64_t n_tiles,
                    int32_t tiles_per_wave, uint32_t* sink, void* stream) {
-  if (tile_bytes != 2048 && tile_bytes != 4096) return fail(PKV_ERR_INVALID, "read_tiles: tile_bytes must be 2048 or 4096");
+  if (tile_bytes != 1024 && tile_bytes != 2048 && tile_bytes != 4096)
+    return fail(PKV_ERR_INVALID, "read_tiles: tile_bytes must be 1024, 2048 or 4096");
   if (!base || !sink || base_bytes < tile_bytes || n_tiles < 1 || tiles_per_wave < 1)
     return fail(PKV_ERR_INVALID, "read_tiles: bad argument");
   if (!aligned16(base)) return fail(PKV_ERR_INVALID, "read_tiles: base must be 16-byte aligned");

@@ -349,32 +349,169 @@ __device__ __forceinline__ int block_id(int id0, int id1, int id2, int id3, int 
   return __builtin_amdgcn_readlane(v, i & 63);
 }
 
-// Fused append (p.k_new set): the wave whose partitions end at the sequence
-// end writes the step's new token, position n - 1, into block b (its last
-// block) of its KV head, before it loads that block.  Its own load then sees
-// the token (one wave's accesses to an address stay in order; the caller
-// follows the write with a compiler memory barrier so that no load is moved
-// above it), and with at most 16 query heads per KV head no other wave reads
-// that block (the host appends separately otherwise).  The bytes are those
-// the append kernels write.  ELEM: cache bytes per value (1: 8-bit codes
-// with scales).
-template <int D, int ELEM>
-__device__ __forceinline__ void append_new_token(const DecodeParams& p, int s, int kvh, int n, int b) {
-  const int o = (n - 1) % kBlock;
-  const size_t row = static_cast<size_t>(b) * p.Hkv + kvh;             // (block, KV head) tile
-  const size_t src = (static_cast<size_t>(s) * p.Hkv + kvh) * D;       // the token's row of k_new / v_new
-  if constexpr (ELEM == 1) {
-    write_token_fp8(static_cast<uint8_t*>(const_cast<void*>(p.k_cache)),
-                    static_cast<uint8_t*>(const_cast<void*>(p.v_cache)), const_cast<float*>(p.k_scale),
-                    const_cast<float*>(p.v_scale), row, static_cast<const __bf16*>(p.k_new) + src,
-                    static_cast<const __bf16*>(p.v_new) + src, D, o);
-  } else {
-    using U = std::conditional_t<ELEM == 2, uint16_t, uint32_t>;
-    U* kt = static_cast<U*>(const_cast<void*>(p.k_cache)) + row * D * kBlock;
-    U* vt = static_cast<U*>(const_cast<void*>(p.v_cache)) + row * D * kBlock;
-    write_token<U>(kt, vt, static_cast<const U*>(p.k_new) + src, static_cast<const U*>(p.v_new) + src, D, kBlock, o);
+// Fused append (p.k_new set).  Every wave whose partitions end at the
+// sequence end (one per group of 16 query heads) holds the step's new token,
+// position n - 1, in registers: lane l keeps 32-bit word l of its K row and
+// of its V row (bf16 values; D / 2 words each), requested with the queries.
+// Once the wave's last block (the one holding slot o = (n - 1) % 16) has been
+// loaded, the token is substituted for slot o in the wave's copy of it, so the
+// attention sees the token whatever the load returned for that slot.  After
+// the wave's last load, head group 0 also writes the token into the pool,
+// with the same bytes as the append kernels (no wait in the stream depends on
+// these stores, and no load of this kernel depends on them either).
+struct NewToken {
+  uint32_t k, v;        // word `lane` of the token's K and V rows
+};
+
+template <int D>
+__device__ __forceinline__ NewToken load_new_token(const DecodeParams& p, int s, int kvh) {
+  NewToken t{0u, 0u};
+  const size_t row = (static_cast<size_t>(s) * p.Hkv + kvh) * (D / 2);     // in 32-bit words
+  if (threadIdx.x < D / 2) {
+    t.k = static_cast<const uint32_t*>(p.k_new)[row + threadIdx.x];
+    t.v = static_cast<const uint32_t*>(p.v_new)[row + threadIdx.x];
   }
-  asm volatile("" ::: "memory");
+  return t;
+}
+
+// Replaces 16-bit half `half` of w by the low 16 bits of x.
+__device__ __forceinline__ uint32_t put_half(uint32_t w, uint32_t x, int half) {
+  const int sh = 16 * half;
+  return (w & ~(0xFFFFu << sh)) | ((x & 0xFFFFu) << sh);
+}
+// Replaces byte `b` of w by the low 8 bits of x.
+__device__ __forceinline__ uint32_t put_byte(uint32_t w, uint32_t x, int b) {
+  const int sh = 8 * b;
+  return (w & ~(0xFFu << sh)) | ((x & 0xFFu) << sh);
+}
+__device__ __forceinline__ uint32_t lane_word(uint32_t x, int src) {
+  return static_cast<uint32_t>(__shfl(static_cast<int>(x), src));
+}
+
+// bf16 cache: the token's value words go to slot o of the wave's registers of
+// one block (lane layout of decode_partial_bf16: per 32-wide slice c of the
+// head dimension, lane (c16, g4) holds words 16c + 4g4 .. +3 of token c16's K;
+// per value tile t, token 4g4 + w of column 16t + c16 in half w % 2 of word
+// w / 2).
+template <int D>
+__device__ __forceinline__ void patch_token_bf16(u32x4* k, u32x2* v, const NewToken& t, int o) {
+  const int c16 = threadIdx.x & 15, g4 = threadIdx.x >> 4;
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = lane_word(t.k, 16 * c + 4 * g4 + j);
+      if (c16 == o) k[c][j] = w;
+    }
+  const int w_idx = (o & 3) >> 1, half = o & 1;
+#pragma unroll
+  for (int tt = 0; tt < D / 16; ++tt) {
+    const uint32_t w = lane_word(t.v, 8 * tt + (c16 >> 1)) >> (16 * (c16 & 1));
+    if (g4 == (o >> 2)) {
+      if (w_idx == 0) v[tt].x = put_half(v[tt].x, w, half);
+      else v[tt].y = put_half(v[tt].y, w, half);
+    }
+  }
+}
+
+// The token's pool bytes as kv_append_kernel writes them (K [d/8][B][8],
+// V [d][B] in 16-bit values): lane l writes word l of each row.
+template <int D>
+__device__ __forceinline__ void store_token_bf16(const DecodeParams& p, size_t row, const NewToken& t, int o) {
+  const int l = threadIdx.x;
+  if (l >= D / 2) return;
+  uint32_t* kt = static_cast<uint32_t*>(const_cast<void*>(p.k_cache)) + row * (kBlock * D / 2);
+  uint16_t* vt = static_cast<uint16_t*>(const_cast<void*>(p.v_cache)) + row * (kBlock * D);
+  kt[((l >> 2) * kBlock + o) * 4 + (l & 3)] = t.k;
+  vt[(2 * l) * kBlock + o] = static_cast<uint16_t>(t.v & 0xFFFFu);
+  vt[(2 * l + 1) * kBlock + o] = static_cast<uint16_t>(t.v >> 16);
+}
+
+// 8-bit cache: the token quantised as kv_append_fp8_kernel quantises it (per
+// row: scale = amax / 448, codes by the hardware conversion); lane l holds
+// the codes of values 2l and 2l + 1 (low 16 bits of kc / vc) and, for
+// l < D / 4, the four codes of values 4l .. 4l + 3 (k4 / v4).
+struct NewTokenFp8 {
+  uint32_t kc, vc, k4, v4;
+  float ks, vs;
+};
+
+template <int D>
+__device__ __forceinline__ NewTokenFp8 quantize_token(const NewToken& t) {
+  const int l = threadIdx.x;
+  auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
+  auto hi = [](uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); };
+  float ka = 0.f, va = 0.f;
+  if (l < D / 2) {
+    ka = fmaxf(fabsf(lo(t.k)), fabsf(hi(t.k)));
+    va = fmaxf(fabsf(lo(t.v)), fabsf(hi(t.v)));
+  }
+  NewTokenFp8 q;
+  q.ks = wave_max(ka) / 448.f;
+  q.vs = wave_max(va) / 448.f;
+  q.kc = e4m3_code(lo(t.k), q.ks) | (static_cast<uint32_t>(e4m3_code(hi(t.k), q.ks)) << 8);
+  q.vc = e4m3_code(lo(t.v), q.vs) | (static_cast<uint32_t>(e4m3_code(hi(t.v), q.vs)) << 8);
+  q.k4 = (lane_word(q.kc, 2 * l) & 0xFFFFu) | (lane_word(q.kc, 2 * l + 1) << 16);
+  q.v4 = (lane_word(q.vc, 2 * l) & 0xFFFFu) | (lane_word(q.vc, 2 * l + 1) << 16);
+  return q;
+}
+
+// 8-bit cache: codes and scales of the token to slot o of the wave's
+// registers of one block (lane (c16, g4): per 64-value segment c of K, word
+// j = codes of values 16(4c + g4) + 4j .. +3 of token c16; per segment a of V,
+// byte w of word b = column 64a + 4c16 + b of token 4g4 + w; the scales of
+// tokens 4g4 .. 4g4 + 3).
+template <int D>
+__device__ __forceinline__ void patch_token_fp8(u32x4* k, u32x4* v, f32x4& ks, f32x4& vs, const NewTokenFp8& q,
+                                                int o) {
+  const int c16 = threadIdx.x & 15, g4 = threadIdx.x >> 4;
+#pragma unroll
+  for (int c = 0; c < D / 64; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = lane_word(q.k4, 4 * (4 * c + g4) + j);
+      if (c16 == o) k[c][j] = w;
+    }
+  const int w = o & 3;
+#pragma unroll
+  for (int a = 0; a < D / 64; ++a) {
+    const uint32_t codes = lane_word(q.v4, 16 * a + c16);     // columns 64a + 4c16 + b, b = 0..3
+    if (g4 == (o >> 2)) {
+      v[a].x = put_byte(v[a].x, codes, w);
+      v[a].y = put_byte(v[a].y, codes >> 8, w);
+      v[a].z = put_byte(v[a].z, codes >> 16, w);
+      v[a].w = put_byte(v[a].w, codes >> 24, w);
+    }
+  }
+  if (g4 == (o >> 2)) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j == w) {
+        ks[j] = q.ks;
+        vs[j] = q.vs;
+      }
+  }
+}
+
+// The 8-bit token's pool bytes as kv_append_fp8_kernel writes them.
+template <int D>
+__device__ __forceinline__ void store_token_fp8(const DecodeParams& p, size_t row, const NewTokenFp8& q, int o) {
+  const int l = threadIdx.x;
+  if (l < D / 2) {
+    uint8_t* kd = static_cast<uint8_t*>(const_cast<void*>(p.k_cache)) + row * kBlock * D;
+    uint8_t* vd = static_cast<uint8_t*>(const_cast<void*>(p.v_cache)) + row * kBlock * D;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = 2 * l + h;
+      kd[(e >> 4) * (kBlock * 16) + o * 16 + (e & 15)] = static_cast<uint8_t>(q.kc >> (8 * h));
+      vd[(e >> 6) * 1024 + (o >> 2) * 256 + ((e & 63) >> 2) * 16 + (e & 3) * 4 + (o & 3)] =
+          static_cast<uint8_t>(q.vc >> (8 * h));
+    }
+  }
+  if (l == 0) {
+    const_cast<float*>(p.k_scale)[row * kBlock + o] = q.ks;
+    const_cast<float*>(p.v_scale)[row * kBlock + o] = q.vs;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -465,11 +602,13 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
   };
   int s_, kvh, h0, nh, P, part0, part_end, t_lo, t_end, blk_first, nblk, boundary0, id0, id1, id2, id3, id4;
   int n_;
-  bool new_token;              // this wave appends the step's new token (fused append)
+  bool new_token;              // this wave's last block receives the step's new token (fused append)
+  NewToken tok{0u, 0u};
   {
     WaveTask w;
     if (!setup_task<__bf16, D>(p, w, issue_q)) return;
     new_token = p.k_new != nullptr && w.part_end == w.P;
+    if (new_token) tok = load_new_token<D>(p, w.s, w.kvh);   // in flight with the queries
     n_ = w.n;
     s_ = w.s; kvh = w.kvh; h0 = w.h0; nh = w.nh; P = w.P; part0 = w.part0; part_end = w.part_end;
     t_lo = w.t_lo; t_end = w.t_end; blk_first = w.blk_first; nblk = w.nblk; boundary0 = w.boundary0;
@@ -662,17 +801,18 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
   using MayTail = std::integral_constant<bool, true>;
   BlockRegs<D, kFp8> buf[NBUF];
   int i = 0;
-  // The fused append's stores must precede the load of the last block.  A
-  // wait for block data also waits for every older store (stores and loads
-  // share vmcnt), so they go as late as possible: an appending wave leaves
-  // its last block to the drain loop and stores just before that loop; with
-  // at most NBUF blocks the last one is among the first loads, and the
-  // stores go before them.
-  auto append = [&]() {
-    append_new_token<D, kFp8 ? 1 : 2>(p, s_, kvh, n_, block_id(id0, id1, id2, id3, id4, nblk - 1));
+  // Fused append: the token's slot in the last block, and (8-bit cache) its
+  // codes, made once the drain loop reaches that block.
+  const int tok_slot = (n_ - 1) % kBlock;
+  NewTokenFp8 tok8{};
+  auto patch_last = [&](BlockRegs<D, kFp8>& r) {
+    if constexpr (kFp8) {
+      tok8 = quantize_token<D>(tok);
+      patch_token_fp8<D>(r.k, r.v, r.ks, r.vs, tok8, tok_slot);
+    } else {
+      patch_token_bf16<D>(r.k, r.v, tok, tok_slot);
+    }
   };
-  if (new_token && nblk <= NBUF) append();
-  const int nblk_steady = new_token ? nblk - 1 : nblk;   // the steady loop loads blocks below this
   if (nblk >= 2 * NBUF) {
     // Issue order matters: the loop expects buf[0] to be the oldest load in
     // flight on entry (as it is on the back edge), otherwise the wait at the
@@ -682,7 +822,7 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
       load_block(buf[u], u);
       __builtin_amdgcn_sched_barrier(0);
     }
-    for (; i + 2 * NBUF <= nblk_steady; i += NBUF) {
+    for (; i + 2 * NBUF <= nblk; i += NBUF) {
       if (prio_swap) {
         if ((static_cast<unsigned>(__builtin_amdgcn_s_memrealtime() >> 12) ^ slot_bit) & 1)
           __builtin_amdgcn_s_setprio(1);
@@ -700,17 +840,23 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
     for (int u = 0; u < NBUF; ++u)
       if (u < nblk) load_block(buf[u], u);
   }
-  // Here the blocks below i + NBUF are loaded, and the last one is not
-  // (nblk > NBUF; the steady loop stops before it).
-  if (new_token && nblk > NBUF) append();
+  // The last block is always consumed here (the steady loop stops at least
+  // NBUF blocks before the end).
   for (; i < nblk; i += NBUF) {
 #pragma unroll
     for (int u = 0; u < NBUF; ++u) {
       if (i + u < nblk) {
+        if (new_token && i + u == nblk - 1) patch_last(buf[u]);
         compute_block(buf[u], i + u, MayTail{});
         if (i + u + NBUF < nblk) load_block(buf[u], i + u + NBUF);
       }
     }
+  }
+  // Every load has been consumed: the new token's pool write can go now.
+  if (new_token && blockIdx.y == 0) {
+    const size_t row = static_cast<size_t>(block_id(id0, id1, id2, id3, id4, nblk - 1)) * p.Hkv + kvh;
+    if constexpr (kFp8) store_token_fp8<D>(p, row, tok8, tok_slot);
+    else store_token_bf16<D>(p, row, tok, tok_slot);
   }
 
   // The stream has ended: write the staged partitions, then the last one.
@@ -792,8 +938,6 @@ __global__ __launch_bounds__(64) void decode_partial_f32(DecodeParams p) {
   {
     WaveTask w;
     if (!setup_task<float, D>(p, w, [](const WaveTask&) {})) return;
-    if (p.k_new && w.part_end == w.P)        // before any block load (this kernel is not on the hot path)
-      append_new_token<D, 4>(p, w.s, w.kvh, w.n, block_id(w.id0, w.id1, w.id2, w.id3, w.id4, w.nblk - 1));
     s_ = w.s; kvh = w.kvh; h0 = w.h0; nh = w.nh; P = w.P; part0 = w.part0;
     t_lo = w.t_lo; t_end = w.t_end; blk_first = w.blk_first; nblk = w.nblk;
     id0 = w.id0; id1 = w.id1; id2 = w.id2; id3 = w.id3; id4 = w.id4;

@@ -518,7 +518,7 @@ def pkv_read_tiles(base, order, n_tiles: int, tiles_per_wave: int, sink, stream=
     """Read-bandwidth calibration: base is a device tensor (any dtype), order
     a device int32 tensor of tile ids or None (contiguous tiles), sink a
     device int32/uint32 tensor of ceil(n_tiles / tiles_per_wave) * 64 entries;
-    tiles of tile_bytes (4096 or 2048)."""
+    tiles of tile_bytes (4096, 2048 or 1024)."""
     waves = -(-n_tiles // tiles_per_wave)
     if sink.numel() < waves * 64 or sink.element_size() != 4:
         raise ValueError("sink needs ceil(n_tiles / tiles_per_wave) * 64 32-bit entries")

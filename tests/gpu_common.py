@@ -97,3 +97,59 @@ def oracle_out(rp, wl, q, layer=0, rows=None, scale=None, window=0):
     heads = None if rows is None else set(rows)
     return OA.decode(rp.pool, layer, rp.tables(), rp.lengths(), q64, wl.Hq, scale=scale, heads=heads,
                      window=window)
+
+
+def step_inputs(wl, k_log):
+    """The checked step's new token of each batch row ([S][Hkv][d] views of
+    the logical tensors) and the ids, for a workload whose step appends one
+    token per sequence in batch order."""
+    (kind, entries), = wl.step_ops
+    assert kind == "append"
+    ids = [e[0] for e in entries]
+    assert ids == list(wl.seq_ids)
+    rows = torch.tensor([wl.offsets[src] + pos for (_, src, pos) in entries], device=k_log.device)
+    return ids, rows
+
+
+def decode_step(wl, k_log, v_log, q, fused, layers=(0,), engine_layers=None, partition=0, window=0):
+    """Run the workload's setup, then its decode step the way a serving loop
+    does: host slot reservation, table upload, and per layer the new token's
+    K/V plus attention — handed to the decode call (fused: the library
+    appends, in its partial kernel where it fuses) or written first by
+    kv_append_last.  k_log / v_log / q: {layer: device tensor}; engine layer
+    i holds layers[i].  Returns (engine, {layer: out})."""
+    from paged_kv_cache_08_amd import pkv as P
+    from paged_kv_cache_08_amd.engine import PagedDecodeEngine
+    eng = PagedDecodeEngine(engine_layers or len(layers), wl.Hkv, wl.d, wl.num_blocks, wl.cache_dtype,
+                            init_perm=wl.perm, partition=partition)
+    eng.run_script(wl.setup_ops, wl, {i: k_log[l] for i, l in enumerate(layers)},
+                   {i: v_log[l] for i, l in enumerate(layers)}, layers=range(len(layers)))
+    ids, rows = step_inputs(wl, k_log[layers[0]])
+    new = {i: (k_log[l].index_select(0, rows).contiguous(), v_log[l].index_select(0, rows).contiguous())
+           for i, l in enumerate(layers)}
+    if fused:
+        _, cow = P.pkv_append_slots(eng.pool, ids)
+        if cow:
+            P.pkv_copy_blocks(eng.pool, cow)
+        eng.sync(ids)
+    else:
+        eng.step_append(ids, new)
+    out = {}
+    for i, l in enumerate(layers):
+        kn, vn = new[i] if fused else (None, None)
+        out[l] = eng.decode(i, q[l], max_seq_len=wl.max_len, window=window, k_new=kn, v_new=vn)
+    torch.cuda.synchronize()
+    return eng, out
+
+
+def check_same_bits(a, b, what):
+    assert np.array_equal(gpu_bits(a), gpu_bits(b)), f"{what} differs"
+
+
+def check_pool_layer(eng, i, rp, layer):
+    """Engine layer i against the oracle pool's layer `layer`, bit for bit."""
+    for name, o, g in (("K", rp.pool.K[layer], eng.k[i]), ("V", rp.pool.V[layer], eng.v[i])):
+        assert np.array_equal(gpu_bits(g).reshape(o.shape), o), f"{name} pool differs (layer {layer})"
+    if rp.pool.dtype == "fp8":
+        for name, o, g in (("K", rp.pool.KS[layer], eng.ks[i]), ("V", rp.pool.VS[layer], eng.vs[i])):
+            assert np.array_equal(gpu_bits(g).reshape(o.shape), o), f"{name} scales differ (layer {layer})"

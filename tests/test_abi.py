@@ -167,11 +167,11 @@ def test_prefill_argument_validation(bad, status):
 @pytest.mark.parametrize("args", [
     (0, 1 << 20, 0, 16, 1, 16),             # null buffer
     (16, 1 << 20, 0, 16, 1, 0),             # null sink
-    (16, 4095, 0, 1, 1, 16),                # buffer smaller than one tile
+    (16, 1000, 0, 1, 1, 16),                # buffer smaller than one tile
     (16, 1 << 20, 0, 0, 1, 16),             # no tiles
     (16, 1 << 20, 0, 16, 0, 16),            # tiles_per_wave < 1
     (8, 1 << 20, 0, 16, 1, 16),             # misaligned buffer
-    (16, 1 << 20, 0, 257, 1, 16),           # contiguous read past the buffer (256 tiles)
+    (16, 1 << 20, 0, 1025, 1, 16),          # contiguous read past the buffer (at most 1024 tiles)
 ])
 @pytest.mark.parametrize("tile_bytes", [4096, 1024, 3000])
 def test_read_tiles_argument_validation(args, tile_bytes):
@@ -188,9 +188,11 @@ def test_read_tiles_2k_tiles_count_against_the_buffer():
 @pytest.mark.parametrize("kw,fused", [
     (dict(), 0),                                          # nothing to append
     (dict(k_new=16, v_new=16), 1),
-    (dict(k_new=16, v_new=16, num_q_heads=64), 0),        # 32 query heads per KV head: append kernel first
+    (dict(k_new=16, v_new=16, num_q_heads=64), 1),        # 32 query heads per KV head: every head group
+                                                          #   substitutes the token, group 0 stores it
     (dict(k_new=16, v_new=16, num_seqs=513), 0),          # 1026 (sequence, KV head) rows: append kernel first
     (dict(k_new=16, v_new=16, num_seqs=512), 1),          # 1024 rows
+    (dict(k_new=16, v_new=16, dtype=P.PKV_F32, kv_dtype=P.PKV_F32), 0),   # fp32 cache: append kernel first
 ])
 def test_decode_fuses_append(kw, fused):
     assert P.lib().pkv_decode_fuses_append(P.ctypes.byref(_args(**kw))) == fused

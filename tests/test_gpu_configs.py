@@ -1,8 +1,9 @@
-"""GPU parity on the five decode workloads at their full sizes.
-
-Small ones are compared on every output; the 32K-token batch and the
-32-layer step on sampled (sequence, head) rows that the oracle computes one
-by one.  Allocator state and the pool bytes are compared exactly.
+"""GPU parity on the five decode workloads at their full sizes, every
+output row against the oracle; allocator state and pool bytes exactly.
+The 32K-token batch (bf16 and 8-bit caches) and the 32-layer step are
+decoded the way the benchmark decodes them, with the step's new token
+handed to the decode call, and checked bit for bit against the same step
+done with a separate kv_append_last.
 """
 import dataclasses
 
@@ -11,8 +12,8 @@ import pytest
 import torch
 
 import workloads
-from gpu_common import (check_allocator, check_pool, compare_out, need_gpu, note, oracle_out,
-                        oracle_replay, run_gpu)
+from gpu_common import (check_allocator, check_pool, check_pool_layer, check_same_bits, compare_out, decode_step,
+                        need_gpu, note, oracle_out, oracle_replay, run_gpu, step_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -69,22 +70,53 @@ def test_shared_prefix_config_and_private_twin():
     assert torch.equal(out_s[0].view(torch.int16), out_p[0].view(torch.int16))
 
 
-def test_long_context_config_sampled():
+def _plan(eng, wl, q, layer=0, **kw):
+    from paged_kv_cache_08_amd import pkv as P
+    info, _ = P.pkv_decode_plan(eng.decode_args(layer, q, torch.empty_like(q), wl.max_len, **kw), with_cells=False)
+    return info
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_long_context_config(cache):
+    """The 32K-token batch decoded as the benchmark decodes it: the step's
+    new token handed to the decode call (written by the partial kernel),
+    runs of several partitions per wave (the deep pipeline for the bf16
+    cache).  Pool and output bits equal those of the same step done by
+    kv_append_last + decode; allocator, pool and every (sequence, head)
+    row against the oracle."""
     need_gpu()
     wl = workloads.long_context()
+    if cache == "fp8":
+        wl = workloads.fp8_cache(wl)
     note(wl.description)
     q, k, v = wl.tensors(device="cuda")
-    eng, log, out = run_gpu(wl, {0: k}, {0: v}, q)
+    fus, out_f = decode_step(wl, {0: k}, {0: v}, {0: q}, fused=True)
+    ids, rows = step_inputs(wl, k)
+    info = _plan(fus, wl, q, k_new=k.index_select(0, rows), v_new=v.index_select(0, rows))
+    note(f"  plan: depth {info.pipeline_depth}, {info.partitions_per_wave} partitions per wave, "
+         f"fused append {info.fused_append}, {info.cells} cells")
+    assert info.fused_append == 1 and info.partitions_per_wave > 1 and not info.work_list
+    assert info.pipeline_depth == (5 if cache == "bf16" else 4)
+    sep, out_s = decode_step(wl, {0: k}, {0: v}, {0: q}, fused=False)
+    for a, b, what in ((fus.k[0], sep.k[0], "K pool"), (fus.v[0], sep.v[0], "V pool"), (out_f[0], out_s[0], "output")):
+        check_same_bits(a, b, what)
+    if cache == "fp8":
+        check_same_bits(fus.ks[0], sep.ks[0], "K scales")
+        check_same_bits(fus.vs[0], sep.vs[0], "V scales")
+    del sep
     rp = oracle_replay(wl, {0: k}, {0: v})
-    check_allocator(eng, rp, log)
-    check_pool(eng, rp)
-    rows = [(s, h) for s in (0, 6, 15) for h in (0, 7, 8, 33, 63)]
-    e = compare_out(out[0], oracle_out(rp, wl, q, rows=rows), rows=rows)
-    note(f"  sampled rows max_abs={e[0]:.3e} row_rel={e[1]:.3e}")
-    assert torch.isfinite(out[0].float()).all()
+    assert fus.snapshot() == tuple(rp.alloc.snapshot())
+    check_pool(fus, rp)
+    e = compare_out(out_f[0], oracle_out(rp, wl, q))
+    note(f"  all {wl.S * wl.Hq} rows max_abs={e[0]:.3e} row_rel={e[1]:.3e}")
 
 
-def test_full_step_config_sampled():
+def test_full_step_config():
+    """The 32-layer step at full size: layers 0 and 31 (their own K/V and
+    queries), the new token handed to the decode call as the benchmark does
+    (the library picks the fused or the separate append for this batch),
+    bits equal to the kv_append_last step; allocator, pools and every
+    (sequence, head) row of both layers against the oracle."""
     need_gpu()
     wl = workloads.full_step()
     note(wl.description)
@@ -93,13 +125,16 @@ def test_full_step_config_sampled():
     k = {l: ts[l][1] for l in layers}
     v = {l: ts[l][2] for l in layers}
     q = {l: ts[l][0] for l in layers}
-    eng, log, out = run_gpu(wl, k, v, q, layers=layers, engine_layers=wl.layers)
+    fus, out_f = decode_step(wl, k, v, q, fused=True, layers=layers)
+    sep, out_s = decode_step(wl, k, v, q, fused=False, layers=layers)
+    for i, l in enumerate(layers):
+        check_same_bits(fus.k[i], sep.k[i], f"K pool of layer {l}")
+        check_same_bits(fus.v[i], sep.v[i], f"V pool of layer {l}")
+        check_same_bits(out_f[l], out_s[l], f"output of layer {l}")
+    del sep
     rp = oracle_replay(wl, k, v, layers=layers)
-    check_allocator(eng, rp, log)
-    longest = int(np.argmax(wl.lengths))
-    rows = [(s, h) for s in (0, 17, 100, 255, longest) for h in (0, 13, 31)]
-    for l in layers:
-        check_pool(eng, rp, l)
-        e = compare_out(out[l], oracle_out(rp, wl, q[l], layer=l, rows=rows), rows=rows)
-        note(f"  layer {l} sampled rows max_abs={e[0]:.3e} row_rel={e[1]:.3e}")
-        assert torch.isfinite(out[l].float()).all()
+    assert fus.snapshot() == tuple(rp.alloc.snapshot())
+    for i, l in enumerate(layers):
+        check_pool_layer(fus, i, rp, l)
+        e = compare_out(out_f[l], oracle_out(rp, wl, q[l], layer=l))
+        note(f"  layer {l}: all {wl.S * wl.Hq} rows max_abs={e[0]:.3e} row_rel={e[1]:.3e}")

@@ -127,11 +127,26 @@ def test_prefill_bad_block_gives_nan_rows():
 
 
 @pytest.mark.parametrize("name", ["prefill_prompts", "prefill_chunked"])
-def test_prefill_configs_sampled(name):
-    """The measured prefill batches at full size, on sampled rows."""
+def test_prefill_configs(name):
+    """The measured prefill batches at full size: every query head of every
+    sequence at the query positions around the kernel's boundaries — both
+    ends of each chunk, 16-token cache blocks, 64-token K/V tiles, the
+    workgroup's 384 (position, head) rows (96 positions at four heads per
+    KV head) — plus random positions; pool and allocator exactly."""
     wl = workloads.CONFIGS[name]()
-    T = int(wl.chunk_lens.sum())
+    G = wl.Hq // wl.Hkv
+    per_wg = 384 // G
     rng = np.random.default_rng(0)
-    rows = [(int(r), int(h)) for r, h in zip(rng.integers(0, T, 24), rng.integers(0, wl.Hq, 24))]
-    rows += [(0, 0), (T - 1, wl.Hq - 1), (4095, 3)]
-    run_prefill_case(wl, rows=rows, check_state=False)
+    rows = []
+    r0 = 0
+    for m in map(int, wl.chunk_lens):
+        pos = {0, 1, m - 2, m - 1}
+        for step in (16, 64, per_wg):
+            for b in range(step, m, step * 7):           # a spread of boundaries, both sides
+                pos |= {b - 1, b, b + 1}
+            pos |= {m - step - 1, m - step}
+        pos |= set(map(int, rng.integers(0, m, 8)))
+        rows += [(r0 + i, h) for i in sorted(p for p in pos if 0 <= p < m) for h in range(wl.Hq)]
+        r0 += m
+    note(f"  {len(rows)} (row, head) pairs")
+    run_prefill_case(wl, rows=rows, check_state=True)

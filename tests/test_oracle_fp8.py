@@ -75,6 +75,28 @@ def test_encode_matches_library_rounding():
     assert np.array_equal(fp8.encode(ys.astype(np.float64)), ref)
 
 
+def test_grid_rounding_equals_table_search():
+    """``encode`` (rounding onto the format's grid) gives the codes of the
+    plain nearest-value search ``encode_nearest`` on every fp32 value of
+    whole binades around the subnormal, normal and overflow ranges, on
+    midpoints and their neighbours, and on random values of both signs."""
+    rng = np.random.default_rng(7)
+    f32 = np.float32
+    pos = fp8.VALUES[:0x7F]
+    mids = (pos[:-1] + pos[1:]) / 2
+    binades = []
+    for lo in (2.0 ** -12, 2.0 ** -9, 2.0 ** -7, 2.0 ** -6, 0.75, 1.0, 256.0):   # every fp32 in [lo, 2 lo)
+        a = np.float32(lo).view(np.uint32)
+        binades.append(np.arange(a, a + (1 << 23), 64, dtype=np.uint32).view(np.float32))
+    ys = np.concatenate(binades + [
+        rng.uniform(-600, 600, 200000).astype(f32), (rng.standard_normal(200000) * 2.0 ** -7).astype(f32),
+        mids.astype(f32), np.nextafter(mids.astype(f32), f32(np.inf)), np.nextafter(mids.astype(f32), f32(-np.inf)),
+        pos.astype(f32), np.array([0.0, 464.0, 464.00003, 479.99997, 480.0, 1e30, np.nan, np.inf], dtype=f32),
+    ]).astype(np.float64)
+    ys = np.concatenate([ys, -ys])
+    assert np.array_equal(fp8.encode(ys), fp8.encode_nearest(ys))
+
+
 def test_quantize_row_scale_and_error_bound():
     rng = np.random.default_rng(1)
     for trial in range(200):

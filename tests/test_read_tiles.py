@@ -44,7 +44,7 @@ def run(words: np.ndarray, order, n_tiles: int, tpw: int, tile_bytes: int = 4096
     (300, 257, 7, True),       # fewer tiles than the permutation, tiny waves
     (5, 5, 256, True),         # one wave, remainder loop only
 ])
-@pytest.mark.parametrize("tile_bytes", [4096, 2048])
+@pytest.mark.parametrize("tile_bytes", [4096, 2048, 1024])
 def test_read_tiles_xor(tiles, n, tpw, gather, tile_bytes):
     rng = np.random.default_rng(tiles * 1000 + n + tpw)
     words = rng.integers(0, 2**32, size=tiles * tile_bytes // 4, dtype=np.uint32)
