@@ -327,6 +327,20 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
 /* Partial kernel followed, when max_seq_len exceeds one partition, by the
  * reduce kernel; both on `stream`.                                        */
 int pkv_paged_attention_decode(const pkv_decode_args* args, void* stream);
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops that must not allocate, harnesses that forbid it):
+ * pkv_paged_attention_decode with the library's own workspace instead of
+ * args->workspace (ignored, as is workspace_bytes).  That workspace is a
+ * device array of 64 MiB (67,108,864 bytes) inside the library, one per
+ * device, held until the process ends; its address is looked up on the
+ * first call on each device, and no call allocates anything.  A call whose
+ * pkv_decode_workspace_bytes() exceeds 64 MiB fails with PKV_ERR_INVALID
+ * before any device work.  Every call on one device uses the same array:
+ * calls that overlap on a device (other streams, other threads) race on it,
+ * so the caller serialises them.  The workspace needs no clearing (every
+ * partial result is written before the reduce reads it).  Other arguments,
+ * errors and results are those of pkv_paged_attention_decode.             */
+int pkv_paged_attention_decode_static(const pkv_decode_args* args, void* stream);
 /* The partial kernel alone (single-partition sequences are finished here). */
 int pkv_paged_decode_partial(const pkv_decode_args* args, void* stream);
 /* The reduce kernel alone (no-op when one partition suffices). */

@@ -10,6 +10,7 @@
 #include <array>
 #include <climits>
 #include <cmath>
+#include <cstdint>
 #include <cstdlib>
 #include <cstring>
 #include <exception>
@@ -723,6 +724,32 @@ int pkv_paged_attention_decode(const pkv_decode_args* a, void* stream) {
   rc = run_partial(a, p, kind, st);
   if (rc) return rc;
   return from_hip(pkv::launch_decode_reduce(p, kind, st), "decode_reduce");
+}
+
+int pkv_paged_attention_decode_static(const pkv_decode_args* a, void* stream) {
+  if (!a) return fail(PKV_ERR_INVALID, "decode_static: null args");
+  // Check the arguments as the decode call does, with a stand-in workspace
+  // of any size, to learn the workspace this call needs.
+  pkv_decode_args b = *a;
+  b.workspace = reinterpret_cast<void*>(static_cast<uintptr_t>(256));
+  b.workspace_bytes = SIZE_MAX;
+  pkv::DecodeParams p{};
+  int kind = 0;
+  const int rc = prepare_decode(&b, &p, &kind);
+  if (rc) return rc;
+  const size_t need = p.pmax > 1 ? workspace_bytes(static_cast<int64_t>(p.S) * p.Hq * p.pmax, p.d) : 0;
+  if (need > pkv::kStaticWorkspaceBytes)
+    return fail(PKV_ERR_INVALID, "decode_static: the call needs " + std::to_string(need) +
+                                     " bytes of workspace, more than the library's " +
+                                     std::to_string(pkv::kStaticWorkspaceBytes));
+  b.workspace = nullptr;
+  b.workspace_bytes = 0;
+  if (need > 0) {
+    const int hrc = from_hip(pkv::static_workspace(&b.workspace), "decode_static: workspace address");
+    if (hrc) return hrc;
+    b.workspace_bytes = pkv::kStaticWorkspaceBytes;
+  }
+  return pkv_paged_attention_decode(&b, stream);
 }
 
 int pkv_decode_fuses_append(const pkv_decode_args* a) {

@@ -35,6 +35,7 @@
 #include <cstdio>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 #include <type_traits>
 
 #include "device_util.hpp"
@@ -1385,6 +1386,30 @@ hipError_t launch_decode_partial(const DecodeParams& p, int kind, hipStream_t st
 
 hipError_t plan_decode_partial(const DecodeParams& p, int kind, DecodeLaunchPlan* plan) {
   return launch_or_plan(p, kind, nullptr, plan);
+}
+
+// The static decode workspace.  In host code `scratch` names a host-side
+// stand-in, not device memory: only the address hipGetSymbolAddress returns
+// (per device, with that device current) is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[kStaticWorkspaceBytes];
+
+hipError_t static_workspace(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode_reduce(const DecodeParams& p, int kind, hipStream_t stream) {

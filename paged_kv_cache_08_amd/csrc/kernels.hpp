@@ -189,6 +189,12 @@ struct DecodeLaunchPlan {
 };
 hipError_t plan_decode_partial(const DecodeParams& p, int kind, DecodeLaunchPlan* plan);
 hipError_t launch_decode_reduce(const DecodeParams& p, int kind, hipStream_t stream);
+// The library's own decode workspace for callers that cannot allocate: a
+// device array of kStaticWorkspaceBytes in the library's code object, one
+// per device.  static_workspace() gives its address on the current device
+// (looked up on the first call on each device).
+constexpr size_t kStaticWorkspaceBytes = size_t(64) << 20;
+hipError_t static_workspace(void** ptr);
 bool decode_shape_supported(int kind, int head_dim, int block_size);
 // Read-bandwidth calibration: wave w reads tiles order[w*tpw ...] (or
 // w*tpw ... without an order) of tile_bytes (2048 or 4096) each and writes

@@ -111,6 +111,7 @@ SIGNATURES = [
                                          _P(_i32), _P(_i64), _P(_i64), _P(_i64), _P(_i64)]),
     ("pkv_decode_workspace_bytes", ctypes.c_size_t, [_i32, _i32, _i32, _i32, _i32]),
     ("pkv_paged_attention_decode", ctypes.c_int, [_P(pkv_decode_args), _vp]),
+    ("pkv_paged_attention_decode_static", ctypes.c_int, [_P(pkv_decode_args), _vp]),
     ("pkv_paged_decode_partial", ctypes.c_int, [_P(pkv_decode_args), _vp]),
     ("pkv_paged_decode_reduce", ctypes.c_int, [_P(pkv_decode_args), _vp]),
     ("pkv_decode_fuses_append", ctypes.c_int, [_P(pkv_decode_args)]),
@@ -455,6 +456,12 @@ def set_new_token(a: pkv_decode_args, k_new, v_new) -> None:
 
 def pkv_paged_attention_decode(args: pkv_decode_args, stream=None) -> None:
     _check(lib().pkv_paged_attention_decode(ctypes.byref(args), _stream(stream)))
+
+
+def pkv_paged_attention_decode_static(args: pkv_decode_args, stream=None) -> None:
+    """pkv_paged_attention_decode with the library's own 64 MiB device
+    workspace (args.workspace is ignored); allocates nothing."""
+    _check(lib().pkv_paged_attention_decode_static(ctypes.byref(args), _stream(stream)))
 
 
 def pkv_paged_decode_partial(args: pkv_decode_args, stream=None) -> None:

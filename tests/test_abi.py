@@ -200,3 +200,12 @@ def test_decode_fuses_append(kw, fused):
 
 def test_decode_fuses_append_rejects_bad_args():
     assert P.lib().pkv_decode_fuses_append(P.ctypes.byref(_args(k_new=16))) == P.PKV_ERR_INVALID
+
+
+def test_static_decode_rejects_batches_beyond_its_workspace():
+    # 64 x 64 heads x 128 partitions of d = 128: about 272 MB of workspace, more than the 64 MiB
+    a = _args(num_seqs=64, num_q_heads=64, num_kv_heads=8, max_seq_len=65536, max_blocks=4096)
+    assert P.lib().pkv_paged_attention_decode_static(P.ctypes.byref(a), None) == P.PKV_ERR_INVALID
+    assert "workspace" in P.pkv_last_error()
+    # invalid arguments are reported as by the caller-workspace call
+    assert P.lib().pkv_paged_attention_decode_static(P.ctypes.byref(_args(num_q_heads=7)), None) == P.PKV_ERR_INVALID
