@@ -31,6 +31,16 @@ __device__ __forceinline__ float sum_over_rows(float x) {
   auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
+// IEEE 754-2019 maximum (NaN-propagating; v_maximum3_f32 on gfx950), for
+// operands that are never NaN: unlike fmaxf (IEEE 754-2008 maxNum) it needs
+// no canonicalisation of operands the compiler cannot prove canonical.
+__device__ __forceinline__ float fmax_ieee(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float max_over_rows_ieee(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmax_ieee(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmax_ieee(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));

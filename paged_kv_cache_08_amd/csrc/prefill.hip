@@ -10,7 +10,7 @@
 // las cabezas KV").  Prefill work has many queries per KV token, so unlike
 // decode it is bound by the matrix cores, not by HBM.
 //
-// One workgroup = 8 waves = 256 query rows of one (sequence, KV head).  A row
+// One workgroup = 12 waves = 384 query rows of one (sequence, KV head).  A row
 // is one (query position, query head of the group) pair, position-major, so
 // the group's heads share every K/V tile.  Each wave owns 32 rows (two
 // 16-row blocks).  K/V are streamed in tiles of 64 tokens (four 16-token
@@ -86,14 +86,13 @@ struct PrefillShape {
 template <int D>
 __device__ __forceinline__ void write_nan_rows(const PrefillParams& p, int q0, int m, int row_lo, int row_hi,
                                                int kvh) {
-  __bf16* out = static_cast<__bf16*>(p.out);
+  uint16_t* out = static_cast<uint16_t*>(p.out);        // bf16 bit patterns: 0x7FC0 is a quiet NaN
   constexpr int per_row = D / 8;
   for (int r = row_lo + static_cast<int>(threadIdx.x) / per_row; r < row_hi; r += kWaves * 64 / per_row) {
     const int qi = r / p.G, g = r - (r / p.G) * p.G;
     if (qi >= m) continue;
-    __bf16* o = out + (static_cast<size_t>(q0 + qi) * p.Hq + kvh * p.G + g) * D + (threadIdx.x % per_row) * 8;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = static_cast<__bf16>(NAN);
+    uint16_t* o = out + (static_cast<size_t>(q0 + qi) * p.Hq + kvh * p.G + g) * D + (threadIdx.x % per_row) * 8;
+    *reinterpret_cast<u32x4*>(o) = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
   }
 }
 
@@ -210,25 +209,33 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16(PrefillParams p) {
       return false;
     }
     const __bf16* src = (is_v ? vc_base : kc_base) + static_cast<size_t>(b) * blk_stride;
+    const int t_end = n - tok0;                                // written slots of this block (>= 1)
 #pragma unroll
     for (int u = 0; u < D / 32; ++u) {
       const int ci = 64 * u + lane;                            // LDS chunk of this lane
-      // K keeps the cache order; V chunk ci holds (half ci / D, column ci % D),
-      // which is cache chunk 2 * column + half
-      const int gi = is_v ? 2 * (ci % D) + ci / D : ci;
+      // K keeps the cache order (chunk ci holds token ci % 16), except that a
+      // slot past the end is read from slot 0 of the same head-dimension
+      // chunk (a written token) instead of whatever the free slot holds.  V
+      // chunk ci holds (half ci / D, column ci % D), which is cache chunk
+      // 2 * column + half.
+      const int gi = is_v ? 2 * (ci % D) + ci / D : ((ci & 15) < t_end ? ci : (ci & ~15));
       __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(gi) * 8, dst + 64 * u * 8, 16, 0, 0);
     }
     return true;
   };
   // After this wave's loads of tile kt landed: zero V tokens at or past n
-  // (free or poisoned slots) in the block that holds token n - 1.
+  // (free slots, which may hold anything, NaN included) in the block that
+  // holds token n - 1.  (Their K chunks were read from slot 0 instead, see
+  // issue().)  So every value the matrix cores read is a cached token or
+  // zero: scores of keys past the end are finite (and masked), and their
+  // zero probabilities meet zero values.
   auto fix_tail = [&](int kt, int buf) {
     if (!loader || !is_v) return;
     const int tok0 = (kt * (kTile / kTok) + tb) * kTok;
     if (tok0 >= n || tok0 + kTok <= n) return;
-    __bf16* dst = lds + buf * Sh::tile + 4 * Sh::blk_stride + tb * Sh::blk_stride;
+    uint16_t* dst = reinterpret_cast<uint16_t*>(lds + buf * Sh::tile + 4 * Sh::blk_stride + tb * Sh::blk_stride);
     for (int e = lane; e < D; e += 64)
-      for (int t = n - tok0; t < kTok; ++t) dst[((t >> 3) * D + e) * 8 + (t & 7)] = static_cast<__bf16>(0.f);
+      for (int t = n - tok0; t < kTok; ++t) dst[((t >> 3) * D + e) * 8 + (t & 7)] = 0;
   };
 
   f32x4 acc[kRB][VT];
@@ -336,12 +343,16 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16(PrefillParams p) {
               if (j > hi) x[j] = -INFINITY;
           }
         }
-        float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-        mx = max_over_rows(mx);
+        // IEEE maximum (v_maximum3_f32): the scores are never NaN here (every
+        // key the cores read is a cached token or zero), and unlike fmaxf it
+        // needs no canonicalisation of the matrix cores' results first.
+        float mx = fmax_ieee(fmax_ieee(fmax_ieee(x[0], x[1]), fmax_ieee(x[2], x[3])),
+                             fmax_ieee(fmax_ieee(x[4], x[5]), fmax_ieee(x[6], x[7])));
+        mx = max_over_rows_ieee(mx);
         if (__any(mx > thr[rb])) {
           // Rows of one block have different masks: a row whose maximum did
           // not grow keeps alpha = 1 (also with no key yet, m = -inf).
-          const float m_new = fmaxf(m_run[rb], mx);
+          const float m_new = fmax_ieee(m_run[rb], mx);
           const float alpha = m_new > m_run[rb] ? exp2_fast((m_run[rb] - m_new) * p.scale_log2) : 1.f;
           acc_l[rb] *= alpha;
 #pragma unroll
