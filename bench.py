@@ -542,10 +542,10 @@ def validate_first_step(bench, layers, seqs, atol: float = 2e-2, row_rtol: float
             def slot(arr, b, o):                  # token slot o of block b, every head and value
                 if arr.ndim == 3:                                            # scales [block][head][slot]
                     return arr[b][:, o]
-                if pool.dtype == "fp8" and arr.ndim == 7:                    # [block][head][a][u][c][b][w]
+                if arr.ndim == 7:                                            # 8-bit V [block][head][a][u][c][b][w]
                     return arr[b][:, :, o // 4, :, :, o % 4]
-                if arr.ndim == 4:                                            # V [block][head][d][slot]
-                    return arr[b][..., o]
+                if arr.ndim == 6:                                            # V [block][head][u][c][b][w]
+                    return arr[b][:, o // 4, :, :, o % 4]
                 return arr[b][:, :, o]                                       # K [block][head][d/x][slot][x]
 
             for i in seqs:

@@ -37,10 +37,13 @@
  * waits for the device except where stated.  A pkv_pool is not thread-safe:
  * the caller serialises calls on one pool.
  *
- * Pool byte layout of one layer (B = block_size tokens, x = 16 / element
- * size, i.e. 4 for fp32 and 8 for bf16; d must be a multiple of x):
+ * Pool byte layout of one layer (B = block_size tokens, a multiple of 4;
+ * x = 16 / element size, i.e. 4 for fp32 and 8 for bf16; d must be a
+ * multiple of x):
  *   K: [num_blocks][num_kv_heads][d / x][B][x]
- *   V: [num_blocks][num_kv_heads][d][B]
+ *   V: [num_blocks][num_kv_heads][B / 4][d / 4][4][4]: value column j of
+ *      token offset o sits at [o / 4][j / 4][j % 4][o % 4] (each run of four
+ *      values holds one column of four consecutive tokens)
  * Slot number s names block s / B, token offset s % B.  One block id
  * addresses the same token range in every layer's pool.
  *
@@ -97,7 +100,8 @@ typedef struct pkv_pool_desc {
   int32_t num_layers;      /* >= 1                                          */
   int32_t num_kv_heads;    /* Hkv >= 1                                      */
   int32_t head_dim;        /* d, multiple of 16 bytes / element size        */
-  int32_t block_size;      /* B tokens per block (16 for the kernels)       */
+  int32_t block_size;      /* B tokens per block (16 for the attention      */
+                           /*   kernels; a multiple of 4 with caches)       */
   int32_t num_blocks;      /* pool capacity in blocks, >= 1                 */
   int32_t dtype;           /* PKV_F32, PKV_BF16 or PKV_FP8_E4M3             */
   void* const* k_cache;    /* [num_layers] device pointers, or NULL for an  */

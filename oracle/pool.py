@@ -13,8 +13,10 @@ for bf16):
 
 * K of layer l: ``K[l][block][head][d // x][B][x]`` — element ``j`` of
   token slot ``o`` sits at ``[block][head][j // x][o][j % x]``;
-* V of layer l: ``V[l][block][head][d][B]`` — element ``j`` of slot ``o``
-  sits at ``[block][head][j][o]``.
+* V of layer l: ``V[l][block][head][B // 4][d // 4][4][4]`` — element ``j``
+  of slot ``o`` sits at ``[block][head][o // 4][j // 4][j % 4][o % 4]``: every
+  run of four values holds one column of four consecutive tokens, and one
+  token's row fills a quarter of the block tile.
 
 Values are stored as raw bit patterns (uint32 for fp32, uint16 for bf16) so
 that the pool can be compared bit for bit.  Slots nothing has written hold a
@@ -63,6 +65,8 @@ class Pool:
         self.x = 16 // self.itemsize
         if d % self.x:
             raise ValueError("head dim must be a multiple of 16 bytes")
+        if block % 4 or d % 4:
+            raise ValueError("the value layout needs block and head dim multiples of 4")
         if dtype == "fp8" and (d % 64 or block != 16):
             raise ValueError("the 8-bit layout needs d % 64 == 0 and B == 16")
         self.layers = layers
@@ -84,7 +88,7 @@ class Pool:
                 self.KS[l] = np.full((self.N, self.Hkv, self.B), POISON["f32"], dtype=np.uint32)
                 self.VS[l] = np.full((self.N, self.Hkv, self.B), POISON["f32"], dtype=np.uint32)
             else:
-                self.V[l] = np.full((self.N, self.Hkv, self.d, self.B),
+                self.V[l] = np.full((self.N, self.Hkv, self.B // 4, self.d // 4, 4, 4),
                                     POISON[self.dtype], dtype=BITS[self.dtype])
 
     def scatter(self, layer: int, slots, k_bits: np.ndarray, v_bits: np.ndarray) -> None:
@@ -105,7 +109,7 @@ class Pool:
         for i, slot in enumerate(slots):
             b, o = divmod(int(slot), self.B)
             K[b, :, :, o, :] = k_bits[i].reshape(self.Hkv, self.d // self.x, self.x)
-            V[b, :, :, o] = v_bits[i]
+            V[b, :, o // 4, :, :, o % 4] = v_bits[i].reshape(self.Hkv, self.d // 4, 4)
 
     def copy_block(self, src: int, dst: int) -> None:
         """Copy-on-write: block ``dst`` becomes a copy of ``src`` in every layer."""
@@ -142,14 +146,6 @@ class Pool:
             kf = fp8.decode(kb[:n]) * ks[:n, None]
             vf = fp8.decode(vb[:n]) * vs[:n, None]
             return kf, vf
-        vb = self.V[layer][blocks, head]                 # [nblk][d][B]
-        vb = vb.transpose(0, 2, 1).reshape(nblk * self.B, self.d)
+        vb = self.V[layer][blocks, head]                 # [nblk][B/4][d/4][4][4]
+        vb = vb.transpose(0, 1, 4, 2, 3).reshape(nblk * self.B, self.d)
         return to_f64(kb[:n], self.dtype), to_f64(vb[:n], self.dtype)
-
-    def valid_mask(self, tables, lengths) -> np.ndarray:
-        """Boolean [N][B]: slots that hold a token of some listed sequence."""
-        m = np.zeros((self.N, self.B), dtype=bool)
-        for table, n in zip(tables, lengths):
-            for t in range(int(n)):
-                m[table[t // self.B], t % self.B] = True
-        return m

@@ -328,6 +328,8 @@ int pkv_pool_create(const pkv_pool_desc* d, pkv_pool** out) {
       return fail(PKV_ERR_INVALID, "pool_create: num_blocks * block_size must fit in int32 slots");
     if ((d->k_cache == nullptr) != (d->v_cache == nullptr))
       return fail(PKV_ERR_INVALID, "pool_create: give both k_cache and v_cache, or neither");
+    if (d->k_cache && (d->block_size % 4 != 0 || d->head_dim % 4 != 0))
+      return fail(PKV_ERR_INVALID, "pool_create: device pools need block_size and head_dim multiples of 4");
     if (d->init_perm) {
       std::vector<char> seen(d->num_blocks, 0);
       for (int32_t i = 0; i < d->num_blocks; ++i) {

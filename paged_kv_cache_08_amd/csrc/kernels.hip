@@ -17,12 +17,14 @@
 //
 // Pool layout of one layer (B = 16 tokens per block for the decode kernels,
 // x = 16 bytes / element size):
-//   K [block][kv_head][d/x][B][x]    V [block][kv_head][d][B]
+//   K [block][kv_head][d/x][B][x]    V [block][kv_head][B/4][d/4][4][4]
 // The K layout makes one 16-byte load per lane, 64 lanes wide, read 1 KiB of
 // contiguous memory that is already in the MFMA A-operand order (lane l:
 // token l%16, 16-byte chunk l/16 of the head dimension slice).  The V layout
-// stores tokens fastest, so a lane's run of consecutive tokens for one value
-// column is contiguous, which is the PV product's operand order.
+// keeps runs of four consecutive tokens of one value column together (value
+// column j of token o at [o/4][j/4][j%4][o%4]), the PV product's operand
+// order, and one token's values within a quarter of the tile: an append
+// touches a quarter of the tile's 32-byte sectors.
 //
 // Scores are kept in base-2 units (score * scale * log2 e) so the softmax
 // uses the hardware exp2.
@@ -101,17 +103,22 @@ __device__ __forceinline__ int append_slot(const AppendParams& p, int i) {
   return slot;
 }
 
+// Offset of value column e of token slot o in a (block, KV head) V tile
+// [B/4][d/4][4][4].
+__device__ __forceinline__ size_t v_index(int e, int o, int d) {
+  return (static_cast<size_t>(o >> 2) * d + e) * 4 + (o & 3);
+}
+
 // One wave writes token o of a (block, KV head) tile: kt / vt point at the
-// tile's K and V (layouts [d/x][B][x] and [d][B]), ks / vs at the token's d
-// values.  Shared by the append kernels and the decode kernels' fused
-// append, so both write the same bytes.
+// tile's K and V (layouts [d/x][B][x] and [B/4][d/4][4][4]), ks / vs at the
+// token's d values.
 template <typename T>
 __device__ __forceinline__ void write_token(T* kt, T* vt, const T* ks, const T* vs, int d, int B, int o) {
   constexpr int x = 16 / sizeof(T);
   for (int ch = threadIdx.x; ch < d / x; ch += 64)
     *reinterpret_cast<u32x4*>(kt + (static_cast<size_t>(ch) * B + o) * x) =
         *reinterpret_cast<const u32x4*>(ks + ch * x);
-  for (int e = threadIdx.x; e < d; e += 64) vt[static_cast<size_t>(e) * B + o] = vs[e];
+  for (int e = threadIdx.x; e < d; e += 64) vt[v_index(e, o, d)] = vs[e];
 }
 
 template <typename T>
@@ -416,7 +423,7 @@ __device__ __forceinline__ void patch_token_bf16(u32x4* k, u32x2* v, const NewTo
 }
 
 // The token's pool bytes as kv_append_kernel writes them (K [d/8][B][8],
-// V [d][B] in 16-bit values): lane l writes word l of each row.
+// V [B/4][d/4][4][4] in 16-bit values): lane l writes word l of each row.
 template <int D>
 __device__ __forceinline__ void store_token_bf16(const DecodeParams& p, size_t row, const NewToken& t, int o) {
   const int l = threadIdx.x;
@@ -424,8 +431,8 @@ __device__ __forceinline__ void store_token_bf16(const DecodeParams& p, size_t r
   uint32_t* kt = static_cast<uint32_t*>(const_cast<void*>(p.k_cache)) + row * (kBlock * D / 2);
   uint16_t* vt = static_cast<uint16_t*>(const_cast<void*>(p.v_cache)) + row * (kBlock * D);
   kt[((l >> 2) * kBlock + o) * 4 + (l & 3)] = t.k;
-  vt[(2 * l) * kBlock + o] = static_cast<uint16_t>(t.v & 0xFFFFu);
-  vt[(2 * l + 1) * kBlock + o] = static_cast<uint16_t>(t.v >> 16);
+  vt[v_index(2 * l, o, D)] = static_cast<uint16_t>(t.v & 0xFFFFu);
+  vt[v_index(2 * l + 1, o, D)] = static_cast<uint16_t>(t.v >> 16);
 }
 
 // 8-bit cache: the token quantised as kv_append_fp8_kernel quantises it (per
@@ -533,8 +540,9 @@ __device__ __forceinline__ void store_token_fp8(const DecodeParams& p, size_t ro
 // block i has been consumed.
 //
 // bf16 cache: the K chunk is read as it lies; V^T row c of tile t is value
-// column 16t+c, read as one 8-byte run of the token-fastest V tile; lane l
-// accumulates value columns 16t+4g..16t+4g+3 of head c.
+// column 16t+c, whose tokens 4g..4g+3 are one 8-byte run of the V tile (the
+// 16 lanes of a group read 128 contiguous bytes, the four groups a quarter
+// tile apart); lane l accumulates value columns 16t+4g..16t+4g+3 of head c.
 //
 // 8-bit cache: each lane reads 16 bytes per 1 KiB of K (one token's 16
 // codes; MFMA 2i+h takes head-dimension values 16(4i+g)+8h.. of the chunk,
@@ -629,7 +637,7 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
   const char* vc_b = static_cast<const char*>(p.v_cache) + kvh * tile_bytes;
   // Block bases are wave-uniform; per-lane byte offsets are 32-bit.
   const uint32_t k_off = static_cast<uint32_t>(lane) * 16u;
-  const uint32_t v_off = kFp8 ? static_cast<uint32_t>(lane) * 16u : static_cast<uint32_t>(c16 * 4 + g4) * 8u;
+  const uint32_t v_off = kFp8 ? static_cast<uint32_t>(lane) * 16u : static_cast<uint32_t>(D * g4 + c16) * 8u;
 
   auto load_block = [&](BlockRegs<D, kFp8>& r, int i) {
     const size_t b = static_cast<size_t>(block_id(id0, id1, id2, id3, id4, i));
@@ -648,7 +656,7 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
 #pragma unroll
       for (int c = 0; c < KC; ++c) r.k[c] = stream_load(kp + 64 * c);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) r.v[t] = stream_load(vp + 64 * t);
+      for (int t = 0; t < NT; ++t) r.v[t] = stream_load(vp + 16 * t);
     }
   };
 
@@ -971,12 +979,12 @@ __global__ __launch_bounds__(64) void decode_partial_f32(DecodeParams p) {
   for (int i = 0; i < nblk; ++i) {    // one partition per wave (ppw = 1)
     const int b = block_id(id0, id1, id2, id3, id4, i);
     const f32x4* kp = reinterpret_cast<const f32x4*>(kc + b * blk_stride) + lane;
-    const f32x4* vp = reinterpret_cast<const f32x4*>(vc + b * blk_stride) + c16 * 4 + g4;
+    const f32x4* vp = reinterpret_cast<const f32x4*>(vc + b * blk_stride) + D * g4 + c16;   // [B/4][D/4][4][4]
     f32x4 kr[KC], vr[NT];
 #pragma unroll
     for (int c = 0; c < KC; ++c) kr[c] = stream_load(kp + 64 * c);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) vr[t] = stream_load(vp + 64 * t);
+    for (int t = 0; t < NT; ++t) vr[t] = stream_load(vp + 16 * t);
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < KC; ++c)

@@ -14,10 +14,7 @@
 // is one (query position, query head of the group) pair, position-major, so
 // the group's heads share every K/V tile.  Each wave owns 32 rows (two
 // 16-row blocks).  K/V are streamed in tiles of 64 tokens (four 16-token
-// blocks gathered through the block table) into LDS:
-//   K  [64 tokens][D + 8]   (token rows, 16 bytes of padding against bank
-//                            conflicts),
-//   Vt [D][64 + 4]          (value-column rows, tokens fastest, padded).
+// blocks gathered through the block table) into LDS (see PrefillShape).
 // Per 32-token half tile (cache blocks b0, b1) and wave, with lane
 // l = 16*g + c (g = l/16, c = l%16), lane group g owns the eight tokens
 // tau(g, j) = 16*(g/2) + 8*(g%2) + j, j = 0..7 (block g/2, half g%2):
@@ -67,14 +64,16 @@ constexpr int kRB = PKV_PREFILL_RB;         // 16-row blocks per wave
 constexpr int kRowsWG = kWaves * kRB * 16;
 
 // LDS holds kBufs tiles (a ring: tile kt + kBufs - 1 is loaded while tile
-// kt is consumed).  A tile is four K block tiles in the
-// cache's own order ([D/8][16 tokens][8]: a lane's A operand is one 16-byte
-// chunk) and four V block tiles stored half-major ([2 token halves][D
-// columns][8 tokens]: a lane's A operand is one 16-byte chunk, 16 lanes read
-// 16 consecutive chunks).  Block tiles sit 64 bytes apart beyond their 4 KiB
-// (D = 128), so the 16 lanes of a K read — eight tokens from each block of a
-// pair — fall on distinct banks.  Both are filled by direct global-to-LDS
-// loads (lane i writes bytes 16i..16i+15 of each 1 KiB run).
+// kt is consumed).  A tile is four K block tiles in the cache's own order
+// ([D/8][16 tokens][8]: a lane's A operand is one 16-byte chunk) and four V
+// block tiles stored half-major ([2 token halves][D columns][8 tokens]: a
+// lane's A operand is one 16-byte chunk, 16 lanes read 16 consecutive
+// chunks).  Block tiles sit 64 bytes apart beyond their 4 KiB (D = 128), so
+// the 16 lanes of a K read (eight tokens from each block of a pair) fall on
+// distinct banks.  Both arrive by direct global-to-LDS loads (lane i writes
+// bytes 16i..16i+15 of each 1 KiB run) in the cache's order; the wave that
+// loaded a V block tile then reorders it in place (the cache keeps four
+// tokens of a column together, [4 token groups][D/4][4 columns][4 tokens]).
 template <int D>
 struct PrefillShape {
   static constexpr int blk = kTok * D;                   // bf16 elements of one block tile
@@ -213,29 +212,49 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16(PrefillParams p) {
 #pragma unroll
     for (int u = 0; u < D / 32; ++u) {
       const int ci = 64 * u + lane;                            // LDS chunk of this lane
-      // K keeps the cache order (chunk ci holds token ci % 16), except that a
-      // slot past the end is read from slot 0 of the same head-dimension
-      // chunk (a written token) instead of whatever the free slot holds.  V
-      // chunk ci holds (half ci / D, column ci % D), which is cache chunk
-      // 2 * column + half.
-      const int gi = is_v ? 2 * (ci % D) + ci / D : ((ci & 15) < t_end ? ci : (ci & ~15));
+      // Both land in the cache order, except that a K slot past the end (K
+      // chunk ci holds token ci % 16) is read from slot 0 of the same
+      // head-dimension chunk (a written token) instead of whatever the free
+      // slot holds.
+      const int gi = is_v ? ci : ((ci & 15) < t_end ? ci : (ci & ~15));
       __builtin_amdgcn_global_load_lds(src + static_cast<size_t>(gi) * 8, dst + 64 * u * 8, 16, 0, 0);
     }
     return true;
   };
-  // After this wave's loads of tile kt landed: zero V tokens at or past n
-  // (free slots, which may hold anything, NaN included) in the block that
-  // holds token n - 1.  (Their K chunks were read from slot 0 instead, see
-  // issue().)  So every value the matrix cores read is a cached token or
-  // zero: scores of keys past the end are finite (and masked), and their
-  // zero probabilities meet zero values.
-  auto fix_tail = [&](int kt, int buf) {
+  // After this wave's loads of tile kt landed, a V loader puts its block
+  // tile into the half-major order.  In the cache order, 16-byte chunk
+  // (D/2) u + p holds columns 2p and 2p + 1 of tokens 4u .. 4u + 3; the
+  // half-major chunk D h + c holds tokens 8h .. 8h + 7 of column c.  So the
+  // chunks of token groups 2h and 2h + 1 of one column pair give the two
+  // half-major chunks of those columns.  Every chunk is read before any is
+  // written (the writes use the reads), so the reorder works in place.
+  // Tokens at or past n (free slots, which may hold anything, NaN included)
+  // become zeros; with the K redirect in issue(), every value the matrix
+  // cores read is a cached token or zero.
+  auto reorder_v = [&](int kt, int buf) {
     if (!loader || !is_v) return;
     const int tok0 = (kt * (kTile / kTok) + tb) * kTok;
-    if (tok0 >= n || tok0 + kTok <= n) return;
-    uint16_t* dst = reinterpret_cast<uint16_t*>(lds + buf * Sh::tile + 4 * Sh::blk_stride + tb * Sh::blk_stride);
-    for (int e = lane; e < D; e += 64)
-      for (int t = n - tok0; t < kTok; ++t) dst[((t >> 3) * D + e) * 8 + (t & 7)] = 0;
+    if (tok0 >= n || tok0 + kTok <= key_lo) return;       // zero-filled
+    u32x4* blk = reinterpret_cast<u32x4*>(lds + buf * Sh::tile + 4 * Sh::blk_stride + tb * Sh::blk_stride);
+    const int t_end = n - tok0;
+    constexpr int kItems = D / 64;                          // (half, column pair) items per lane
+    u32x4 a[kItems], b[kItems];
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+      const int i = lane + 64 * k, h = i / (D / 2), pc = i % (D / 2);
+      a[k] = blk[h * D + pc];                               // token group 2h
+      b[k] = blk[h * D + D / 2 + pc];                       // token group 2h + 1
+    }
+#pragma unroll
+    for (int k = 0; k < kItems; ++k) {
+      const int i = lane + 64 * k, h = i / (D / 2), pc = i % (D / 2);
+      uint32_t keep[4];                                     // 16-bit lanes of token 8h + 2j (+1) kept
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        keep[j] = (8 * h + 2 * j < t_end ? 0xFFFFu : 0u) | (8 * h + 2 * j + 1 < t_end ? 0xFFFF0000u : 0u);
+      blk[h * D + 2 * pc] = u32x4{a[k].x & keep[0], a[k].y & keep[1], b[k].x & keep[2], b[k].y & keep[3]};
+      blk[h * D + 2 * pc + 1] = u32x4{a[k].z & keep[0], a[k].w & keep[1], b[k].z & keep[2], b[k].w & keep[3]};
+    }
   };
 
   f32x4 acc[kRB][VT];
@@ -285,7 +304,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16(PrefillParams p) {
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    fix_tail(kt, buf);
+    reorder_v(kt, buf);
     // Tile kt is in LDS (every wave waited for its own loads of it above,
     // and for its LDS writes here); tile kt-1 is consumed by every wave.  A
     // plain barrier: __syncthreads() would also wait for the loads of the

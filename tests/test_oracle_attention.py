@@ -212,7 +212,7 @@ def test_fork_isolation():
 
 def test_pool_layout_bytes():
     """The documented layout: K element j of slot o at [blk][h][j//x][o][j%x],
-    V element j at [blk][h][j][o] (x = 8 for bf16)."""
+    V element j at [blk][h][o//4][j//4][j%4][o%4] (x = 8 for bf16)."""
     d, B = 16, 4
     pool = Pool(3, 2, d, "bf16", B)
     k = torch.arange(2 * d, dtype=torch.float32).reshape(1, 2, d).to(torch.bfloat16)
@@ -223,9 +223,13 @@ def test_pool_layout_bytes():
     for h in range(2):
         for j in range(d):
             assert K[2, h, j // 8, 3, j % 8] == kb[0, h, j]
-            assert V[2, h, j, 3] == vb[0, h, j]
+            assert V[2, h, 0, j // 4, j % 4, 3] == vb[0, h, j]
     flatK = K.reshape(-1)
     # byte offset of element (blk 2, h 1, j 11, slot 3) in the flat K array
     off = (((2 * 2 + 1) * (d // 8) + 11 // 8) * B + 3) * 8 + 11 % 8
     assert flatK[off] == kb[0, 1, 11]
+    # and in the flat V array: four columns of four tokens per 16 values
+    flatV = V.reshape(-1)
+    off = ((((2 * 2 + 1) * (B // 4) + 3 // 4) * (d // 4) + 11 // 4) * 4 + 11 % 4) * 4 + 3 % 4
+    assert flatV[off] == vb[0, 1, 11]
     assert np.all(K[0] == 0x7FC0) and np.all(V[1] == 0x7FC0)

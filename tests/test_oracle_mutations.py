@@ -67,7 +67,7 @@ def test_transposed_value_gather(monkeypatch):
         nblk = -(-n // self.B)
         blocks = np.asarray(table[:nblk])
         kb = self.K[layer][blocks, head].transpose(0, 2, 1, 3).reshape(nblk * self.B, self.d)
-        vb = self.V[layer][blocks, head].reshape(nblk * self.B, self.d)   # missing transpose
+        vb = self.V[layer][blocks, head].reshape(nblk * self.B, self.d)   # token and column order not swapped
         return pool.to_f64(kb[:n], self.dtype), pool.to_f64(vb[:n], self.dtype)
     monkeypatch.setattr(pool.Pool, "gather", gather)
     _fails(T_att.test_brute_force, workloads.tiny())
@@ -81,7 +81,7 @@ def test_off_by_one_block_index(monkeypatch):
             if b >= self.N:
                 b = 0
             self.K[layer][b, :, :, o, :] = k_bits[i].reshape(self.Hkv, self.d // self.x, self.x)
-            self.V[layer][b, :, :, o] = v_bits[i]
+            self.V[layer][b, :, o // 4, :, :, o % 4] = v_bits[i].reshape(self.Hkv, self.d // 4, 4)
     monkeypatch.setattr(pool.Pool, "scatter", scatter)
     _fails(T_att.test_brute_force, workloads.random_small(11, S=3, Hq=6, Hkv=2, d=16, dtype="bf16", max_len=40))
 
