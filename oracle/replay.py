@@ -57,11 +57,3 @@ class Replay:
 
     def lengths(self):
         return [self.alloc.length(sid) for sid in self.wl.seq_ids]
-
-    def padded_tables(self, max_blocks=None, pad=-1):
-        t = self.tables()
-        mb = max_blocks or max(len(x) for x in t)
-        arr = np.full((len(t), mb), pad, dtype=np.int32)
-        for i, row in enumerate(t):
-            arr[i, :len(row)] = row
-        return arr
