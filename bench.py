@@ -72,6 +72,8 @@ def parse():
     ap.add_argument("--flush", action="store_true",
                     help="write a 1 GiB buffer before every decode step, outside its timing, to evict L2 and the "
                          "MALL; value and step time then come from events around each step")
+    ap.add_argument("--table-stream", choices=["side", "main"], default="side",
+                    help="stream of each step's table upload: a side stream with events, or the main stream")
     ap.add_argument("--no-full-step", action="store_true",
                     help="leave out the 32-layer step that the default (long-context) run also reports")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -111,7 +113,7 @@ class DecodeBench:
     buffer has finished, and the main stream waits for the upload."""
 
     def __init__(self, wl, steps_total: int, partition: int = 0, device="cuda", window: int = 0,
-                 fused_append: bool = True):
+                 fused_append: bool = True, table_stream: str = "side"):
         import numpy as np
         import torch
         from paged_kv_cache_08_amd import pkv as P
@@ -148,7 +150,7 @@ class DecodeBench:
         self.lens = [torch.empty((len(self.ids),), dtype=torch.int32, device=self.dev) for _ in range(2)]
         self.eng.host_lens = np.zeros(len(self.ids), dtype=np.int32)
         self.main = torch.cuda.current_stream()
-        self.side = torch.cuda.Stream()          # default priority
+        self.side = torch.cuda.Stream() if table_stream == "side" else self.main   # default priority
         self.ready = [torch.cuda.Event() for _ in range(2)]
         self.done = [torch.cuda.Event() for _ in range(2)]
         for e in self.done:
@@ -191,7 +193,8 @@ class DecodeBench:
         j = self.step_idx
         b = j % 2
         side = self.side
-        side.wait_event(self.done[b])        # the step that last used these tables has finished
+        if side is not self.main:
+            side.wait_event(self.done[b])    # the step that last used these tables has finished
         if self.flush is not None:
             self.flush.fill_(j & 0xFF)
         slots, cow = P.pkv_append_slots(self.eng.pool, self.ids)
@@ -204,8 +207,9 @@ class DecodeBench:
                 if start > 0 and start % B == 0:
                     P.pkv_seq_release_before(self.eng.pool, sid, start)
         P.pkv_sync_tables(self.eng.pool, self.ids, self.tables[b], self.lens[b], self.eng.host_lens, side)
-        self.ready[b].record(side)
-        self.main.wait_event(self.ready[b])
+        if side is not self.main:
+            self.ready[b].record(side)
+            self.main.wait_event(self.ready[b])
         if self.flush is not None and record_events:
             s0 = torch.cuda.Event(enable_timing=True)
             s0.record(self.main)
@@ -235,7 +239,8 @@ class DecodeBench:
                 e1.record()
                 self.events.append((e0, e1, self.attended_bytes(l)))
             P.pkv_paged_decode_reduce(a)
-        self.done[b].record(self.main)
+        if side is not self.main:
+            self.done[b].record(self.main)
         if self.flush is not None and record_events:
             s1 = torch.cuda.Event(enable_timing=True)
             s1.record(self.main)
@@ -779,7 +784,7 @@ def run_decode(args, wl):
     total = args.warmup + args.steps + 1           # + the validated first step
     log(f"setup {wl.description}")
     bench = DecodeBench(wl, total, partition=args.partition, window=args.window,
-                        fused_append=not args.separate_append)
+                        fused_append=not args.separate_append, table_stream=args.table_stream)
     if args.flush:
         bench.enable_flush()
     parity = None
