@@ -311,18 +311,21 @@ typedef struct pkv_decode_args {
                               /*   none (both or neither)                   */
 } pkv_decode_args;
 
-/* Fused append (k_new, v_new set): before attending, the partial kernel
- * writes row s of k_new / v_new as token seq_lens[s] - 1 of sequence s,
- * exactly as pkv_kv_append_last with the same tables would (same bytes;
- * an 8-bit cache quantises them the same way), so the attention sees it.
- * The write is made by the wave that reads the sequence's last block, before
- * it reads that block; with more than 16 query heads per KV head, or more
- * than 1024 (sequence, KV head) rows (where a separate append is faster),
- * the call runs the append kernel first instead.  Rows the decode cannot read (a
- * length outside [1, max_seq_len], or a block id outside the pool among the
- * last wave's blocks) may or may not receive the token; their outputs are
- * NaN.  The block that receives the token must not be shared (copy it
- * first, as for any append).  pkv_paged_decode_reduce ignores these fields. */
+/* Fused append (k_new, v_new set): row s of k_new / v_new is token
+ * seq_lens[s] - 1 of sequence s.  The partial kernel writes it into the pool
+ * exactly as pkv_kv_append_last with the same tables would (same bytes; an
+ * 8-bit cache quantises it the same way), and the attention sees it: every
+ * wave that reads the sequence's last block substitutes the token for its
+ * slot in the registers holding that block, and the wave of the first 16
+ * query heads writes it to the pool after its last load (no load depends on
+ * that write).  With more than 1024 (sequence, KV head) rows, or an fp32
+ * cache, the call runs the append kernel first instead (the writes inside
+ * the partial kernel's read stream then cost more than that kernel).  Rows
+ * the decode cannot read (a length outside [1, max_seq_len], or a block id
+ * outside the pool among the last wave's blocks) may or may not receive the
+ * token; their outputs are NaN.  The block that receives the token must not
+ * be shared (copy it first, as for any append).  pkv_paged_decode_reduce
+ * ignores these fields.                                                    */
 
 /* Workspace bytes the decode call needs (0 when one partition suffices);
  * enough for any window, which needs at most as much.                     */
@@ -350,9 +353,9 @@ int pkv_paged_decode_partial(const pkv_decode_args* args, void* stream);
 /* The reduce kernel alone (no-op when one partition suffices). */
 int pkv_paged_decode_reduce(const pkv_decode_args* args, void* stream);
 /* 1 if a decode call with these arguments writes the new tokens in the
- * partial kernel (k_new set, at most 16 query heads per KV head and at most
- * 1024 (sequence, KV head) rows), 0 if it would run the append kernel first
- * or has no k_new; a negative status for invalid arguments (as the decode
+ * partial kernel (k_new set, a bf16 or 8-bit cache and at most 1024
+ * (sequence, KV head) rows), 0 if it would run the append kernel first or
+ * has no k_new; a negative status for invalid arguments (as the decode
  * call).  Reads nothing on the device.                                    */
 int pkv_decode_fuses_append(const pkv_decode_args* args);
 
