@@ -349,7 +349,7 @@ __device__ __forceinline__ bool setup_task(const DecodeParams& p, WaveTask& w, I
   return true;
 }
 
-// Physical id of a wave's i-th block (i wave-uniform) from the four id
+// Physical id of a wave's i-th block (i wave-uniform) from the five id
 // registers.
 __device__ __forceinline__ int block_id(int id0, int id1, int id2, int id3, int id4, int i) {
   const int c = i >> 6;
@@ -1251,14 +1251,8 @@ static bool long_uniform(const DecodeParams& p, int waves) {
   return p.tasks_hint > 0 && p.uniform_hint && p.tasks_hint >= 3LL * waves;
 }
 
-// Partitions per wave.  Each wave streams a run of consecutive partitions;
-// for long uniform batches runs are made as long as possible while the grid
-// still fills every resident wave slot once (one round: equal-length runs then
-// finish together instead of leaving a partly filled last round).  A run's
-// staged partials must fit the wave's LDS share and its blocks the four id
-// registers.  PKV_WAVE_PARTITIONS overrides the choice.
-// Largest run (in partitions) that fits the id registers and the wave's LDS
-// share for staged partials.
+// Largest run (in partitions) that fits the five id registers and the wave's
+// LDS share for staged partials.
 static int max_run(const DecodeParams& p, const Residency& r) {
   const int rows = std::min(16, p.G);
   const int lds_row = (p.d + 2) * static_cast<int>(sizeof(float));
@@ -1266,6 +1260,11 @@ static int max_run(const DecodeParams& p, const Residency& r) {
   return std::max(1, std::min(by_ids, 1 + r.lds_per_wave / (rows * lds_row)));
 }
 
+// Partitions per wave.  Each wave streams a run of consecutive partitions;
+// for long uniform batches runs are made as long as possible while the grid
+// still fills every resident wave slot once (one round: equal-length runs then
+// finish together instead of leaving a partly filled last round), within
+// max_run.  PKV_WAVE_PARTITIONS overrides the choice.
 static int pick_partitions_per_wave(const DecodeParams& p, const Residency& r) {
   static const int forced = env_int("PKV_WAVE_PARTITIONS");
   // leave room for a short remainder to join the last run
