@@ -47,6 +47,10 @@ namespace pkv {
 namespace {
 
 constexpr int kBlock = 16;   // tokens per block on the decode path
+// Partitions are merged in groups of kMergeGroup consecutive ones (numbered
+// from 0, the window's first with a window), then the groups: one fixed
+// order of operations whatever wave or kernel does each merge.
+constexpr int kMergeGroup = 4;
 // Blocks in flight per wave.  Two streaming waves on one SIMD do not share
 // it evenly: the arbiter favours the older wave (about 3.5 : 1 in measured
 // per-wave end times), so with equal work the younger wave streams alone for
@@ -584,8 +588,11 @@ __device__ __forceinline__ int acc_column(int t, int j, int g4) {
   return kFp8 ? 64 * (t >> 2) + 16 * g4 + 4 * j + (t & 3) : 16 * t + 4 * g4 + j;
 }
 
+// (The 8-bit shallow variant is held to two waves per SIMD: its merge of
+// staged partitions would otherwise take it past 256 registers.)
 template <int D, int NBUF, bool kFp8>
-__global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kFp8 && NBUF == kDepthFp8 ? 2 : 1)))
+void decode_partial_bf16(DecodeParams p) {
   constexpr int KC = D / 32;                   // QK MFMAs per block
   constexpr int NT = D / 16;                   // PV MFMAs (value tiles) per block
   constexpr int ELEM = kFp8 ? 1 : 2;           // cache bytes per value
@@ -868,30 +875,17 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
     else store_token_bf16<D>(p, row, tok, tok_slot);
   }
 
-  // The stream has ended: write the staged partitions, then the last one.
+  // The stream has ended.  A single partition is the output.  Otherwise the
+  // partitions go to the workspace in merge groups of kMergeGroup (see the
+  // reduce kernels): a group the wave holds whole is merged here and written
+  // once, at its first partition's slot, its sum negated to mark it; the
+  // partitions of a group the wave holds in part are written one by one.
+  // (LDS accesses of one wave complete in order: no barrier is needed.)
   const float l_tot = sum_over_rows(l_run);
-  if (staged_parts > 0) {
-    // (LDS accesses of one wave complete in order: no barrier is needed.)
-    // Lane l moves 16-byte chunks l, l + 64, ... of the nh accumulator rows.
-    const size_t row0 = (static_cast<size_t>(s_) * p.Hq + h0) * p.pmax + part0;
-    for (int sp = 0; sp < staged_parts; ++sp) {
-      for (int c = lane; c < nh * (D / 4); c += 64) {
-        const int h = c / (D / 4), e = (c % (D / 4)) * 4;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(staged + (sp * nh + h) * D + e);
-        *reinterpret_cast<f32x4*>(p.part_acc + (row0 + static_cast<size_t>(h) * p.pmax + sp) * D + e) = v;
-      }
-      if (lane < nh) {
-        const size_t row = row0 + static_cast<size_t>(lane) * p.pmax + sp;
-        p.part_ml[2 * row] = staged_ml[2 * (sp * nh + lane)];
-        p.part_ml[2 * row + 1] = staged_ml[2 * (sp * nh + lane) + 1];
-      }
-    }
-  }
-  if (c16 >= nh) return;
-  const size_t head_row = static_cast<size_t>(s_) * p.Hq + h0 + c16;
   if (P == 1) {
+    if (c16 >= nh) return;
     const float inv = 1.f / l_tot;
-    __bf16* out = static_cast<__bf16*>(p.out) + head_row * D;
+    __bf16* out = static_cast<__bf16*>(p.out) + (static_cast<size_t>(s_) * p.Hq + h0 + c16) * D;
     if constexpr (kFp8) {
 #pragma unroll
       for (int a = 0; a < D / 64; ++a)
@@ -911,8 +905,13 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
         *reinterpret_cast<bf16x4*>(out + acc_column<false>(t, 0, g4)) = o;
       }
     }
-  } else {
-    const size_t row = head_row * p.pmax + part_end - 1;
+    return;
+  }
+  const size_t row0 = (static_cast<size_t>(s_) * p.Hq + h0) * p.pmax;    // + h * pmax + partition
+  const int last = part_end - 1;                                          // in registers; the rest staged
+  auto write_last = [&]() {
+    if (c16 >= nh) return;
+    const size_t row = row0 + static_cast<size_t>(c16) * p.pmax + last;
     float* pa = p.part_acc + row * D;
     if constexpr (kFp8) {
 #pragma unroll
@@ -928,6 +927,85 @@ __global__ __launch_bounds__(64) void decode_partial_bf16(DecodeParams p) {
     if (g4 == 0) {
       p.part_ml[2 * row] = m_run;
       p.part_ml[2 * row + 1] = l_tot;
+    }
+  };
+  // Staged partitions [a, b) one by one; lane l moves 16-byte chunks l,
+  // l + 64, ... of the nh accumulator rows.
+  auto write_staged = [&](int a, int b) {
+    for (int part = a; part < b; ++part) {
+      const int sp = part - part0;
+      for (int c = lane; c < nh * (D / 4); c += 64) {
+        const int h = c / (D / 4), e = (c % (D / 4)) * 4;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(staged + (sp * nh + h) * D + e);
+        *reinterpret_cast<f32x4*>(p.part_acc + (row0 + static_cast<size_t>(h) * p.pmax + part) * D + e) = v;
+      }
+      if (lane < nh) {
+        const size_t row = row0 + static_cast<size_t>(lane) * p.pmax + part;
+        p.part_ml[2 * row] = staged_ml[2 * (sp * nh + lane)];
+        p.part_ml[2 * row + 1] = staged_ml[2 * (sp * nh + lane) + 1];
+      }
+    }
+  };
+  if (part_end - part0 == 1) {        // one partition (the work list's waves): nothing to merge
+    write_last();
+    return;
+  }
+  // Accumulator chunk q of the lane's head, as staged (four value columns).
+  auto acc_chunk = [&](int q) -> f32x4 {
+    if constexpr (kFp8) {
+      const int a = q >> 2, j = q & 3;
+      return f32x4{acc[4 * a][j], acc[4 * a + 1][j], acc[4 * a + 2][j], acc[4 * a + 3][j]};
+    } else {
+      return acc[q];
+    }
+  };
+  auto chunk_column = [&](int q) { return kFp8 ? acc_column<true>(4 * (q >> 2), q & 3, g4) : acc_column<false>(q, 0, g4); };
+  for (int g = part0 / kMergeGroup; g <= last / kMergeGroup; ++g) {
+    const int g0 = g * kMergeGroup;
+    if (g0 >= part0 && g0 + kMergeGroup <= part_end) {
+      // The whole group: M = max m_i, w_i = 2^(m_i - M), L = sum l_i w_i and
+      // A = sum acc_i w_i, each a chain of fused multiply-adds in partition order.
+      if (c16 < nh) {
+        float m_i[kMergeGroup], l_i[kMergeGroup];
+        float M = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kMergeGroup; ++u) {
+          const int sp = g0 + u - part0;
+          m_i[u] = g0 + u == last ? m_run : staged_ml[2 * (sp * nh + c16)];
+          l_i[u] = g0 + u == last ? l_tot : staged_ml[2 * (sp * nh + c16) + 1];
+          M = fmaxf(M, m_i[u]);
+        }
+        float w[kMergeGroup];
+        float L = 0.f;
+#pragma unroll
+        for (int u = 0; u < kMergeGroup; ++u) {
+          w[u] = exp2_fast(m_i[u] - M);
+          L = __builtin_fmaf(l_i[u], w[u], L);
+        }
+        const size_t row = row0 + static_cast<size_t>(c16) * p.pmax + g0;
+#pragma unroll
+        for (int q = 0; q < NT; ++q) {
+          f32x4 A = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int u = 0; u < kMergeGroup; ++u) {
+            const f32x4 v = g0 + u == last ? acc_chunk(q)
+                                           : *reinterpret_cast<const f32x4*>(
+                                                 staged + ((g0 + u - part0) * nh + c16) * D + chunk_column(q));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) A[e] = __builtin_fmaf(v[e], w[u], A[e]);
+          }
+          *reinterpret_cast<f32x4*>(p.part_acc + row * D + chunk_column(q)) = A;
+        }
+        if (g4 == 0) {
+          p.part_ml[2 * row] = M;
+          p.part_ml[2 * row + 1] = -L;          // negative: a merged group
+        }
+      }
+    } else {
+      const int a = g0 > part0 ? g0 : part0;
+      const int b = g0 + kMergeGroup < part_end ? g0 + kMergeGroup : part_end;
+      write_staged(a, b < last ? b : last);
+      if (b == part_end) write_last();
     }
   }
 }
@@ -1039,12 +1117,17 @@ __global__ __launch_bounds__(64) void decode_partial_f32(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// decode_reduce: one 256-lane workgroup per (sequence, query head) with more
-// than one partition.  M = max_p m_p, L = sum_p l_p 2^(m_p - M),
-// out = sum_p acc_p 2^(m_p - M) / L, rounded to the output type.  Lane t
-// owns value columns 4(t % CG) .. +3 for partitions p = t / CG + k * PH, so
-// all its loads are independent and in flight together; the PH partial sums
-// of a column are added through LDS.
+// decode_reduce: merges the P > 1 partitions of each (sequence, query head)
+// row, always in one order of operations (so the result does not depend on
+// which kernel, or which partial-kernel wave, merges what):
+//   partitions in groups of kMergeGroup, g = [K g, K g + K) within [0, P):
+//     M_g = max m_i,  w_i = 2^(m_i - M_g),
+//     L_g = l_0 w_0 + l_1 w_1 + ...,  A_g = acc_0 w_0 + acc_1 w_1 + ...
+//   then the groups:  M = max M_g,  W_g = 2^(M_g - M),
+//     L = L_0 W_0 + L_1 W_1 + ...,  out = (A_0 W_0 + A_1 W_1 + ...) / L,
+// every sum a chain of fused multiply-adds from 0 in index order.  A group
+// the partial kernel merged itself sits at its first partition's slot with
+// its sum negated (a partition's own sum is at least 1).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float block_max_256(float x, float* scratch) {
   x = wave_max(x);
@@ -1054,20 +1137,27 @@ __device__ __forceinline__ float block_max_256(float x, float* scratch) {
   __syncthreads();
   return x;
 }
-__device__ __forceinline__ float block_sum_256(float x, float* scratch) {
-  x = wave_sum(x);
-  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = x;
-  __syncthreads();
-  x = (scratch[0] + scratch[1]) + (scratch[2] + scratch[3]);
-  __syncthreads();
-  return x;
+
+__device__ __forceinline__ bool merged_group(const float* ml, int g0) { return ml[2 * g0 + 1] < 0.f; }
+
+// M_g of group g (partitions [g0, min(g0 + K, P))).
+__device__ __forceinline__ float group_max(const float* ml, int g0, int P) {
+  if (merged_group(ml, g0)) return ml[2 * g0];
+  float M = -INFINITY;
+  for (int i = g0; i < g0 + kMergeGroup && i < P; ++i) M = fmaxf(M, ml[2 * i]);
+  return M;
 }
 
+// One workgroup per row, for launches with more than kRowReduceMaxParts
+// partitions: PH groups at a time are merged in parallel (thread (cg, ph):
+// four value columns of group c0 + ph) into LDS, then the first CG threads
+// fold them into the output columns in group order.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams p) {
   constexpr int CG = D / 4;        // float4 column groups
-  constexpr int PH = 256 / CG;     // partition phases
-  __shared__ float red[PH][D];
+  constexpr int PH = 256 / CG;     // merge groups per round
+  __shared__ f32x4 red[PH][CG];
+  __shared__ float red_m[PH], red_l[PH];
   __shared__ float scratch[4];
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
@@ -1079,38 +1169,58 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams p) {
   if (P <= 1) return;
   const float* ml = p.part_ml + static_cast<size_t>(row) * p.pmax * 2;
   const float* acc = p.part_acc + static_cast<size_t>(row) * p.pmax * D;
+  const int NG = (P + kMergeGroup - 1) / kMergeGroup;
   float M = -INFINITY;
-  for (int i = tid; i < P; i += 256) M = fmaxf(M, ml[2 * i]);
+  for (int g = tid; g < NG; g += 256) M = fmaxf(M, group_max(ml, g * kMergeGroup, P));
   M = block_max_256(M, scratch);
-  float L = 0.f;
-  for (int i = tid; i < P; i += 256) L += ml[2 * i + 1] * exp2_fast(ml[2 * i] - M);
-  L = block_sum_256(L, scratch);
   const int cg = tid % CG;
   const int ph = tid / CG;
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  int i = ph;
-  for (; i + 3 * PH < P; i += 4 * PH) {
-    f32x4 a[4];
-    float wgt[4];
+  float L = 0.f;
+  f32x4 O = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < NG; c0 += PH) {
+    const int g = c0 + ph;
+    if (g < NG) {
+      const int g0 = g * kMergeGroup;
+      float Mg, Lg;
+      f32x4 Ag;
+      if (merged_group(ml, g0)) {
+        Mg = ml[2 * g0];
+        Lg = -ml[2 * g0 + 1];
+        Ag = *reinterpret_cast<const f32x4*>(acc + static_cast<size_t>(g0) * D + 4 * cg);
+      } else {
+        Mg = group_max(ml, g0, P);
+        Lg = 0.f;
+        Ag = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = g0; i < g0 + kMergeGroup && i < P; ++i) {
+          const float w = exp2_fast(ml[2 * i] - Mg);
+          Lg = __builtin_fmaf(ml[2 * i + 1], w, Lg);
+          const f32x4 a = *reinterpret_cast<const f32x4*>(acc + static_cast<size_t>(i) * D + 4 * cg);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      a[u] = *reinterpret_cast<const f32x4*>(acc + static_cast<size_t>(i + u * PH) * D + 4 * cg);
-      wgt[u] = exp2_fast(ml[2 * (i + u * PH)] - M);
+          for (int e = 0; e < 4; ++e) Ag[e] = __builtin_fmaf(a[e], w, Ag[e]);
+        }
+      }
+      red[ph][cg] = Ag;
+      if (cg == 0) {
+        red_m[ph] = Mg;
+        red_l[ph] = Lg;
+      }
     }
+    __syncthreads();
+    if (tid < CG) {
+      for (int u = 0; u < PH && c0 + u < NG; ++u) {
+        const float W = exp2_fast(red_m[u] - M);
+        L = __builtin_fmaf(red_l[u], W, L);
+        const f32x4 a = red[u][tid];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) o += wgt[u] * a[u];
+        for (int e = 0; e < 4; ++e) O[e] = __builtin_fmaf(a[e], W, O[e]);
+      }
+    }
+    __syncthreads();
   }
-  for (; i < P; i += PH)
-    o += exp2_fast(ml[2 * i] - M) * *reinterpret_cast<const f32x4*>(acc + static_cast<size_t>(i) * D + 4 * cg);
+  if (tid < CG) {
+    T* out = static_cast<T*>(p.out) + static_cast<size_t>(row) * D + 4 * tid;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) red[ph][4 * cg + j] = o[j];
-  __syncthreads();
-  if (tid < D) {
-    float sum = 0.f;
-#pragma unroll
-    for (int k = 0; k < PH; ++k) sum += red[k][tid];
-    T* out = static_cast<T*>(p.out) + static_cast<size_t>(row) * D;
-    out[tid] = static_cast<T>(sum / L);
+    for (int e = 0; e < 4; ++e) out[e] = static_cast<T>(O[e] / L);
   }
 }
 
@@ -1118,8 +1228,8 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams p) {
 // one wave per (sequence, query head) row and four rows per workgroup: in a
 // mixed batch most rows have one partition and exit after reading their
 // length, and a quarter of the workgroups dispatch faster than one per row.
-// Lane i < P holds partition i's (m, l); lane c accumulates columns
-// c * D/64 ... of every partition's weighted accumulator in partition order.
+// Lane i < P reads partition i's (m, l); lane c merges value columns
+// c * D/64 ... group by group.
 constexpr int kRowReduceMaxParts = 32;
 
 template <typename T, int D>
@@ -1136,32 +1246,54 @@ __global__ __launch_bounds__(256) void decode_reduce_rows_kernel(DecodeParams p)
   if (P <= 1) return;
   const float* ml = p.part_ml + static_cast<size_t>(row) * p.pmax * 2;
   const float* acc = p.part_acc + static_cast<size_t>(row) * p.pmax * D + CPL * lane;
+  // Lane i: partition i's m and l, and whether its group was merged (then
+  // only the group's first slot was written).
+  const int gi = lane - lane % kMergeGroup;
   const float m_i = lane < P ? ml[2 * lane] : -INFINITY;
   const float l_i = lane < P ? ml[2 * lane + 1] : 0.f;
-  const float M = wave_max(m_i);
-  const float w_i = lane < P ? exp2_fast(m_i - M) : 0.f;
-  const float L = wave_sum(l_i * w_i);
+  const float l_g = lane < P ? ml[2 * gi + 1] : 0.f;
+  const bool live = lane < P && (l_g >= 0.f || lane == gi);
+  const float M = wave_max(live ? m_i : -INFINITY);
+  float L = 0.f;
   float o[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; ++j) o[j] = 0.f;
-  int i = 0;
-  for (; i + 4 <= P; i += 4) {
-    float a[4][CPL];
+  for (int g0 = 0; g0 < P; g0 += kMergeGroup) {
+    const int cnt = P - g0 < kMergeGroup ? P - g0 : kMergeGroup;
+    float Mg, Lg = 0.f;
+    float ag[CPL];
+    if (__shfl(l_i, g0) < 0.f) {                   // merged by the partial kernel
+      Mg = __shfl(m_i, g0);
+      Lg = -__shfl(l_i, g0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+      for (int j = 0; j < CPL; ++j) ag[j] = acc[static_cast<size_t>(g0) * D + j];
+    } else {
+      float mu[kMergeGroup], lu[kMergeGroup], a[kMergeGroup][CPL];
+      Mg = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) a[u][j] = acc[static_cast<size_t>(i + u) * D + j];
+      for (int u = 0; u < kMergeGroup; ++u) {
+        mu[u] = __shfl(m_i, g0 + u);
+        lu[u] = __shfl(l_i, g0 + u);
+        if (u < cnt) Mg = fmaxf(Mg, mu[u]);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float w = __shfl(w_i, i + u);
+        for (int j = 0; j < CPL; ++j) a[u][j] = u < cnt ? acc[static_cast<size_t>(g0 + u) * D + j] : 0.f;
+      }
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) o[j] += w * a[u][j];
+      for (int j = 0; j < CPL; ++j) ag[j] = 0.f;
+#pragma unroll
+      for (int u = 0; u < kMergeGroup; ++u) {
+        if (u < cnt) {
+          const float w = exp2_fast(mu[u] - Mg);
+          Lg = __builtin_fmaf(lu[u], w, Lg);
+#pragma unroll
+          for (int j = 0; j < CPL; ++j) ag[j] = __builtin_fmaf(a[u][j], w, ag[j]);
+        }
+      }
     }
-  }
-  for (; i < P; ++i) {
-    const float w = __shfl(w_i, i);
+    const float W = exp2_fast(Mg - M);
+    L = __builtin_fmaf(Lg, W, L);
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) o[j] += w * acc[static_cast<size_t>(i) * D + j];
+    for (int j = 0; j < CPL; ++j) o[j] = __builtin_fmaf(ag[j], W, o[j]);
   }
   T* out = static_cast<T*>(p.out) + static_cast<size_t>(row) * D + CPL * lane;
 #pragma unroll
