@@ -125,6 +125,51 @@ __device__ __forceinline__ void write_token(T* kt, T* vt, const T* ks, const T* 
   for (int e = threadIdx.x; e < d; e += 64) vt[v_index(e, o, d)] = vs[e];
 }
 
+// Wide form, for 64 / (d / x) heads per wave: one wave takes token i of a
+// group of consecutive KV heads.  For K, lane l moves 16-byte chunk
+// l % (d / x) of head l / (d / x) of the group; for V, value k * 64 + l of
+// the group's rows in step k, so each V store covers 64 consecutive columns
+// of one head, as in kv_append_kernel.  The k_new / v_new reads are issued
+// before the slot lookup, which they do not depend on.  The same bytes as
+// write_token.
+template <typename T>
+__global__ __launch_bounds__(64) void kv_append_wide_kernel(AppendParams p) {
+  constexpr int x = 16 / sizeof(T);
+  const int i = blockIdx.x;
+  const int d = p.head_dim;
+  const int Hkv = p.num_kv_heads;
+  const int cpr = d / x;                               // chunks per row, divides 64
+  const int h0 = blockIdx.y * (64 / cpr);
+  const int l = threadIdx.x;
+  const int hk = h0 + l / cpr;
+  const int c = l % cpr;
+  const size_t row0 = static_cast<size_t>(i) * Hkv;
+  const T* ksrc = static_cast<const T*>(p.k_new);
+  const T* vsrc = static_cast<const T*>(p.v_new);
+  const u32x4 kw = *reinterpret_cast<const u32x4*>(ksrc + (row0 + (hk < Hkv ? hk : 0)) * d + c * x);
+  T vals[x];
+#pragma unroll
+  for (int k = 0; k < x; ++k) {
+    const int v = k * 64 + l;
+    const int hv = h0 + v / d;
+    vals[k] = vsrc[(row0 + (hv < Hkv ? hv : 0)) * d + v % d];
+  }
+  const int B = p.block_size;
+  const int slot = append_slot(p, i);
+  if (slot < 0) return;
+  const int b = slot / B;
+  const int o = slot - b * B;
+  const size_t blk = static_cast<size_t>(b) * Hkv;
+  if (hk < Hkv)
+    *reinterpret_cast<u32x4*>(static_cast<T*>(p.k_cache) + (blk + hk) * d * B + (static_cast<size_t>(c) * B + o) * x) = kw;
+#pragma unroll
+  for (int k = 0; k < x; ++k) {
+    const int v = k * 64 + l;
+    const int hv = h0 + v / d;
+    if (hv < Hkv) static_cast<T*>(p.v_cache)[(blk + hv) * d * B + v_index(v % d, o, d)] = vals[k];
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(64) void kv_append_kernel(AppendParams p) {
   const int i = blockIdx.x;
@@ -187,6 +232,67 @@ __global__ __launch_bounds__(64) void kv_append_fp8_kernel(AppendParams p) {
   const __bf16* vs = static_cast<const __bf16*>(p.v_new) + (static_cast<size_t>(i) * p.num_kv_heads + h) * d;
   write_token_fp8(static_cast<uint8_t*>(p.k_cache), static_cast<uint8_t*>(p.v_cache), p.k_scale, p.v_scale,
                   static_cast<size_t>(b) * p.num_kv_heads + h, ks, vs, d, o);
+}
+
+// Wide 8-bit form for D = 64 or 128: one wave takes token i of a group of
+// 512 / D consecutive KV heads, eight values per lane (value k * 64 + l of
+// the group's rows in step k, so loads and code stores cover 64 consecutive
+// columns of one head).  The k_new / v_new reads are issued before the slot
+// lookup.  Same scales and codes as write_token_fp8: the per-row amax is a
+// max, whichever lanes take part.
+template <int D>
+__global__ __launch_bounds__(64) void kv_append_fp8_wide_kernel(AppendParams p) {
+  constexpr int G = 512 / D;          // heads per wave
+  constexpr int kph = D / 64;         // values per lane and head
+  const int i = blockIdx.x;
+  const int Hkv = p.num_kv_heads;
+  const int h0 = blockIdx.y * G;
+  const int l = threadIdx.x;
+  const size_t row0 = static_cast<size_t>(i) * Hkv;
+  const __bf16* ks = static_cast<const __bf16*>(p.k_new);
+  const __bf16* vs = static_cast<const __bf16*>(p.v_new);
+  float kv[8], vv[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int hv = h0 + k / kph;
+    const size_t idx = (row0 + (hv < Hkv ? hv : 0)) * D + (k % kph) * 64 + l;
+    kv[k] = static_cast<float>(ks[idx]);
+    vv[k] = static_cast<float>(vs[idx]);
+  }
+  const int slot = append_slot(p, i);
+  if (slot < 0) return;
+  const int b = slot / kBlock;
+  const int o = slot - b * kBlock;
+  float ksc = 0.f, vsc = 0.f;         // lane hl < G keeps head hl's scales
+#pragma unroll
+  for (int hl = 0; hl < G; ++hl) {
+    float ka = 0.f, va = 0.f;
+#pragma unroll
+    for (int j = 0; j < kph; ++j) {
+      ka = fmaxf(ka, fabsf(kv[hl * kph + j]));
+      va = fmaxf(va, fabsf(vv[hl * kph + j]));
+    }
+    const float kscale = wave_max(ka) / 448.f;
+    const float vscale = wave_max(va) / 448.f;
+    if (l == hl) { ksc = kscale; vsc = vscale; }
+    const int hv = h0 + hl;
+    if (hv >= Hkv) continue;
+    const size_t row = static_cast<size_t>(b) * Hkv + hv;
+    uint8_t* kd = static_cast<uint8_t*>(p.k_cache) + row * kBlock * D;
+    uint8_t* vd = static_cast<uint8_t*>(p.v_cache) + row * kBlock * D;
+#pragma unroll
+    for (int j = 0; j < kph; ++j) {
+      const int e = j * 64 + l;
+      kd[(e >> 4) * (kBlock * 16) + o * 16 + (e & 15)] = e4m3_code(kv[hl * kph + j], kscale);
+      vd[(e >> 6) * 1024 + (o >> 2) * 256 + ((e & 63) >> 2) * 16 + (e & 3) * 4 + (o & 3)] =
+          e4m3_code(vv[hl * kph + j], vscale);
+    }
+  }
+  if (l < G && h0 + l < Hkv) {
+    const size_t row = static_cast<size_t>(b) * Hkv + h0 + l;
+    p.k_scale[row * kBlock + o] = ksc;
+    p.v_scale[row * kBlock + o] = vsc;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1326,7 +1432,22 @@ hipError_t launch_table_upload(const int32_t* host_src, int32_t* dev_tables, int
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream) {
   if (p.n <= 0) return hipSuccess;
   dim3 grid(p.n, p.num_kv_heads);
-  if (p.elem_bytes == 1)
+  const int cpr = p.elem_bytes > 1 ? p.head_dim * p.elem_bytes / 16 : 0;   // 16-byte chunks per row
+  if (cpr > 0 && cpr <= 64 && 64 % cpr == 0) {         // several heads per wave
+    const int hpw = 64 / cpr;
+    dim3 g(p.n, (p.num_kv_heads + hpw - 1) / hpw);
+    if (p.elem_bytes == 4)
+      hipLaunchKernelGGL(kv_append_wide_kernel<uint32_t>, g, dim3(64), 0, stream, p);
+    else
+      hipLaunchKernelGGL(kv_append_wide_kernel<uint16_t>, g, dim3(64), 0, stream, p);
+  } else if (p.elem_bytes == 1 && (p.head_dim == 64 || p.head_dim == 128)) {
+    const int hpw = 512 / p.head_dim;
+    dim3 g(p.n, (p.num_kv_heads + hpw - 1) / hpw);
+    if (p.head_dim == 64)
+      hipLaunchKernelGGL(kv_append_fp8_wide_kernel<64>, g, dim3(64), 0, stream, p);
+    else
+      hipLaunchKernelGGL(kv_append_fp8_wide_kernel<128>, g, dim3(64), 0, stream, p);
+  } else if (p.elem_bytes == 1)
     hipLaunchKernelGGL(kv_append_fp8_kernel, grid, dim3(64), 0, stream, p);
   else if (p.elem_bytes == 4)
     hipLaunchKernelGGL(kv_append_kernel<uint32_t>, grid, dim3(64), 0, stream, p);

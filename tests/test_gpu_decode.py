@@ -284,6 +284,43 @@ def test_step_append_matches_oracle(make):
 
 
 
+@pytest.mark.parametrize("dtype,d,Hkv", [
+    ("bf16", 128, 6),    # 4 heads per wave: the second wave has heads 4 and 5 only
+    ("bf16", 64, 3),     # 8 heads per wave, 3 present
+    ("bf16", 256, 3),    # 2 heads per wave
+    ("f32", 16, 5),      # 16 heads per wave
+    ("f32", 128, 3),     # 2 heads per wave
+    ("bf16", 96, 3),     # 12 chunks per row do not divide a wave: one wave per row
+    ("fp8", 128, 6),     # 8-bit pool: 4 heads per wave, eight values per lane
+    ("fp8", 64, 9),      # 8 heads per wave: the second wave has head 8 only
+    ("fp8", 192, 2),     # one wave per row
+])
+def test_append_shapes_match_oracle(dtype, d, Hkv):
+    """Both append forms (slot mapping for the set-up, last position for the
+    step) write the oracle's pool bit for bit at head dims and head counts
+    that fill a wave's head group raggedly or not at all."""
+    need_gpu()
+    from paged_kv_cache_08_amd.engine import PagedDecodeEngine
+    wl = workloads.random_small(91, S=5, Hq=Hkv, Hkv=Hkv, d=d, dtype="bf16" if dtype == "fp8" else dtype,
+                                max_len=70)
+    if dtype == "fp8":
+        wl = workloads.fp8_cache(wl)
+    note(f"append shapes: {wl.description}, {wl.cache_dtype} cache")
+    q, k, v = wl.tensors(device="cuda")
+    eng = PagedDecodeEngine(1, wl.Hkv, wl.d, wl.num_blocks, wl.cache_dtype, init_perm=wl.perm)
+    log = eng.run_script(wl.setup_ops, wl, {0: k}, {0: v})
+    (kind, entries), = wl.step_ops
+    offs = wl.offsets
+    rows = torch.tensor([offs[src] + pos for (_, src, pos) in entries], device="cuda")
+    ids = [e[0] for e in entries]
+    slots, cow = eng.step_append(ids, {0: (k.index_select(0, rows), v.index_select(0, rows))})
+    log.append(("append", ids, slots, cow))
+    torch.cuda.synchronize()
+    rp = oracle_replay(wl, {0: k}, {0: v})
+    check_allocator(eng, rp, log)
+    check_pool(eng, rp)
+
+
 def test_workspace_reuse_and_garbage():
     """The split-K workspace may hold anything: repeated calls on one
     workspace, and a workspace full of random bytes, give the same bits, with
