@@ -207,9 +207,12 @@ int pkv_seq_table(const pkv_pool* pool, int64_t seq_id, int32_t* table_out, int3
 /* Upload the block tables and lengths of `n` sequences to caller-owned
  * device arrays: dev_block_tables int32[n][max_blocks] (row i = ids[i],
  * unused entries -1) and dev_seq_lens int32[n].  Asynchronous on `stream`
- * by one small kernel that reads two pinned staging buffers owned by the
- * pool (used alternately: a call waits only for the upload issued two calls
- * earlier).  If
+ * by one small kernel that reads a pinned staging buffer owned by the pool.
+ * The pool keeps a ring of eight such buffers and marks the end of every
+ * fourth upload with an event, so a call waits (on the host) only at the
+ * start of a group of four, for the group that used the same buffers eight
+ * uploads earlier; calls may use different streams.  pkv_pool_destroy waits
+ * for the device when uploads are in flight.  If
  * host_seq_lens_out is not NULL it also receives the lengths (host int32[n]),
  * e.g. to pass as pkv_decode_args.host_seq_lens.  PKV_ERR_INVALID if a
  * sequence holds more than max_blocks blocks.                              */

@@ -26,13 +26,25 @@ struct pkv_pool {
   int32_t num_layers, num_kv_heads, head_dim, dtype;
   std::vector<void*> k_cache, v_cache;    // empty for an allocator-only pool
   std::vector<void*> k_scale, v_scale;    // 8-bit pools: per-slot scales
-  // Two pinned staging buffers for table uploads, used alternately; a buffer
-  // is refilled only after the upload that last read it has finished.
-  void* staging[2] = {nullptr, nullptr};
-  size_t staging_bytes[2] = {0, 0};
-  hipEvent_t upload_done[2] = {nullptr, nullptr};
-  bool upload_pending[2] = {false, false};
-  int next_staging = 0;
+  // Pinned staging buffers for table uploads, a ring: upload u fills buffer
+  // u % kStagingRing.  Uploads form groups of kUploadsPerEvent, and events
+  // mark a group's end (one per run of uploads on one stream), so a stream
+  // holds one event marker per group rather than one per upload: a marker
+  // between an upload and the next kernel leaves the GPU idle for about
+  // 4.5 us.  A buffer is refilled only after the events of the group that
+  // last used it have completed.
+  static constexpr int kStagingRing = 8;
+  static constexpr int kUploadsPerEvent = 4;
+  struct UploadGroup {
+    hipEvent_t ev[kUploadsPerEvent] = {};
+    int n_ev = 0;                 // events recorded for the group
+    bool pending = false;
+  };
+  void* staging[kStagingRing] = {};
+  size_t staging_bytes[kStagingRing] = {};
+  UploadGroup groups[kStagingRing / kUploadsPerEvent];
+  uint64_t uploads = 0;           // uploads launched so far
+  hipStream_t last_stream = nullptr;
 
   pkv_pool(int32_t nb, int32_t bs, const int32_t* perm) : alloc(nb, bs, perm) {}
 };
@@ -370,14 +382,18 @@ int pkv_pool_create(const pkv_pool_desc* d, pkv_pool** out) {
 int pkv_pool_destroy(pkv_pool* pool) {
   if (!pool) return PKV_OK;
   int st = PKV_OK;
-  for (int i = 0; i < 2; ++i) {
-    if (pool->upload_done[i]) {
-      if (pool->upload_pending[i] && st == PKV_OK)
-        st = from_hip(hipEventSynchronize(pool->upload_done[i]), "pool_destroy");
-      (void)hipEventDestroy(pool->upload_done[i]);
-    }
-    if (pool->staging[i]) (void)hipHostFree(pool->staging[i]);
+  // The last uploads of an unfinished group have no event yet (and their
+  // stream may be gone): wait for the device instead.
+  if (pool->uploads % pkv_pool::kUploadsPerEvent != 0)
+    st = from_hip(hipDeviceSynchronize(), "pool_destroy");
+  for (auto& g : pool->groups) {
+    for (int e = 0; e < g.n_ev; ++e)
+      if (g.pending && st == PKV_OK) st = from_hip(hipEventSynchronize(g.ev[e]), "pool_destroy");
+    for (hipEvent_t ev : g.ev)
+      if (ev) (void)hipEventDestroy(ev);
   }
+  for (void* buf : pool->staging)
+    if (buf) (void)hipHostFree(buf);
   delete pool;
   return st;
 }
@@ -500,16 +516,18 @@ int pkv_sync_tables(pkv_pool* pool, const int64_t* ids, int32_t n, int32_t* dev_
     const size_t table_bytes = static_cast<size_t>(n) * max_blocks * sizeof(int32_t);
     const size_t need = table_bytes + static_cast<size_t>(n) * sizeof(int32_t);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const int k = pool->next_staging;
+    const uint64_t u = pool->uploads;
+    const int k = static_cast<int>(u % pkv_pool::kStagingRing);
+    const int pos = static_cast<int>(u % pkv_pool::kUploadsPerEvent);
+    auto& grp = pool->groups[(u / pkv_pool::kUploadsPerEvent) % (pkv_pool::kStagingRing / pkv_pool::kUploadsPerEvent)];
     int rc;
-    if (!pool->upload_done[k]) {
-      rc = from_hip(hipEventCreateWithFlags(&pool->upload_done[k], hipEventDisableTiming), "sync_tables");
-      if (rc) return rc;
-    }
-    if (pool->upload_pending[k]) {
-      rc = from_hip(hipEventSynchronize(pool->upload_done[k]), "sync_tables: wait for an earlier upload");
-      if (rc) return rc;
-      pool->upload_pending[k] = false;
+    if (pos == 0 && grp.pending) {     // the group that last used these buffers
+      for (int e = 0; e < grp.n_ev; ++e) {
+        rc = from_hip(hipEventSynchronize(grp.ev[e]), "sync_tables: wait for an earlier upload");
+        if (rc) return rc;
+      }
+      grp.pending = false;
+      grp.n_ev = 0;
     }
     if (pool->staging_bytes[k] < need) {
       if (pool->staging[k]) (void)hipHostFree(pool->staging[k]);
@@ -533,10 +551,31 @@ int pkv_sync_tables(pkv_pool* pool, const int64_t* ids, int32_t n, int32_t* dev_
     rc = from_hip(pkv::launch_table_upload(tab, dev_tables, static_cast<int64_t>(n) * max_blocks, dev_lens, n, st),
                   "sync_tables: upload");
     if (rc) return rc;
-    rc = from_hip(hipEventRecord(pool->upload_done[k], st), "sync_tables: record");
-    if (rc) return rc;
-    pool->upload_pending[k] = true;
-    pool->next_staging = 1 - k;
+    const hipStream_t prev = pool->last_stream;
+    pool->uploads = u + 1;
+    pool->last_stream = st;
+    // The events only tell the host when uploads have finished reading their
+    // staging buffers; no device write has to reach the host.  So they record
+    // without the system-scope fence (a cache write-back and invalidation).
+    auto mark = [&](hipStream_t s) -> int {
+      hipEvent_t& ev = grp.ev[grp.n_ev];
+      int r = PKV_OK;
+      if (!ev) r = from_hip(hipEventCreateWithFlags(&ev, hipEventDisableTiming | hipEventDisableSystemFence),
+                            "sync_tables: event");
+      if (!r) r = from_hip(hipEventRecord(ev, s), "sync_tables: record");
+      if (r) {                          // no event: make sure the buffers are free before returning
+        (void)hipDeviceSynchronize();
+        return r;
+      }
+      ++grp.n_ev;
+      grp.pending = true;
+      return PKV_OK;
+    };
+    if (pos > 0 && st != prev) {        // the group's uploads on the previous stream end here
+      rc = mark(prev);
+      if (rc) return rc;
+    }
+    if (pos == pkv_pool::kUploadsPerEvent - 1) return mark(st);
     return PKV_OK;
   });
 }

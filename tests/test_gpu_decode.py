@@ -376,3 +376,42 @@ def test_sync_tables_writes_exactly_the_rows(offset):
     want_lens = np.array([P.pkv_seq_length(eng.pool, i) for i in ids], dtype=np.int32)
     assert np.array_equal(lens.cpu().numpy()[1:n + 1], want_lens) and np.array_equal(host, want_lens)
     assert lens[0].item() == -7 and lens[n + 1].item() == -7
+
+
+def test_sync_tables_ring_keeps_every_upload():
+    """Successive uploads, on two streams that alternate within the pool's
+    groups of four and behind a long matrix product, each land their own
+    step's tables and lengths: no staging buffer is refilled while an upload
+    that reads it is still queued."""
+    need_gpu()
+    from paged_kv_cache_08_amd import pkv as P
+    from paged_kv_cache_08_amd.engine import PagedDecodeEngine
+    wl = workloads.with_lengths([15, 16, 31, 47, 64, 100], Hq=4, Hkv=1, d=64, dtype="f32", seed=5, slack=2.0)
+    eng = PagedDecodeEngine(1, wl.Hkv, wl.d, wl.num_blocks, wl.cache_dtype, init_perm=wl.perm)
+    eng.run_script(wl.setup_ops + wl.step_ops, None)
+    ids = list(wl.seq_ids)
+    n, mb, uploads = len(ids), 16, 27
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    tabs = [torch.full((n, mb), -7, dtype=torch.int32, device="cuda") for _ in range(uploads)]
+    lens = [torch.full((n,), -7, dtype=torch.int32, device="cuda") for _ in range(uploads)]
+    busy = [torch.randn((6144, 6144), device="cuda") for _ in range(2)]
+    torch.cuda.synchronize()
+    for st, a in zip((main, side), busy):    # keep both streams busy for a while
+        with torch.cuda.stream(st):
+            for _ in range(4):
+                a.copy_(a @ a / 80.0)
+    want_tab, want_len = [], []
+    for u in range(uploads):
+        P.pkv_append_slots(eng.pool, ids)
+        t = np.full((n, mb), -1, dtype=np.int32)
+        for r, i in enumerate(ids):
+            row = P.pkv_seq_table(eng.pool, i)
+            t[r, :len(row)] = row
+        want_tab.append(t)
+        want_len.append(np.array([P.pkv_seq_length(eng.pool, i) for i in ids], dtype=np.int32))
+        st = side if u % 3 == 1 else main
+        P.pkv_sync_tables(eng.pool, ids, tabs[u], lens[u], stream=st)
+    torch.cuda.synchronize()
+    for u in range(uploads):
+        assert np.array_equal(tabs[u].cpu().numpy(), want_tab[u]), f"upload {u}: tables"
+        assert np.array_equal(lens[u].cpu().numpy(), want_len[u]), f"upload {u}: lengths"
