@@ -31,6 +31,7 @@ Prints one JSON line.  Options: --gpus N (only 1 is supported), --steps K
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -80,6 +81,9 @@ def parse():
                          "auto: the side stream for a multi-layer step, the main stream for one layer")
     ap.add_argument("--no-full-step", action="store_true",
                     help="leave out the 32-layer step that the default (long-context) run also reports")
+    ap.add_argument("--torch-events", action="store_true",
+                    help="time and order the streams with torch's events (recorded with the system-scope fence) "
+                         "instead of fence-free HIP events")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 1 GiB device copies (known bytes) for counter scaling")
     return ap.parse_args()
@@ -87,6 +91,88 @@ def parse():
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class _Hip:
+    """The HIP runtime that torch has loaded (found among the process's
+    mappings, so the same library instance and device state)."""
+    lib = None
+
+    @classmethod
+    def get(cls):
+        if cls.lib is None:
+            import ctypes
+            path = None
+            with open("/proc/self/maps") as f:
+                for line in f:
+                    if "libamdhip64" in line:
+                        path = line.split()[-1]
+                        break
+            if path is None:
+                raise RuntimeError("the HIP runtime is not loaded")
+            h = ctypes.CDLL(path)
+            vp, u = ctypes.c_void_p, ctypes.c_uint
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), u]
+            h.hipEventRecord.argtypes = [vp, vp]
+            h.hipStreamWaitEvent.argtypes = [vp, vp, u]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+            for f in (h.hipEventCreateWithFlags, h.hipEventRecord, h.hipStreamWaitEvent, h.hipEventElapsedTime):
+                f.restype = ctypes.c_int
+            cls.lib = h
+        return cls.lib
+
+
+class Event:
+    """A stream event with the part of torch.cuda.Event's interface the
+    bench uses.  By default a HIP event recorded without the system-scope
+    fence (hipEventDisableSystemFence): a fenced event writes back and
+    invalidates the caches at its marker, which leaves the GPU idle for a
+    few microseconds, and the bench's events order and time work on one
+    device only.  `use_torch` (--torch-events) takes torch's events."""
+    use_torch = False
+    _DISABLE_TIMING = 0x2
+    _NO_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, enable_timing: bool = False):
+        import torch
+        if Event.use_torch:
+            self.t = torch.cuda.Event(enable_timing=enable_timing)
+            return
+        import ctypes
+        self.t = None
+        self.ev = ctypes.c_void_p()
+        flags = self._NO_SYSTEM_FENCE | (0 if enable_timing else self._DISABLE_TIMING)
+        self._check(_Hip.get().hipEventCreateWithFlags(ctypes.byref(self.ev), flags), "hipEventCreateWithFlags")
+
+    @staticmethod
+    def _check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    @staticmethod
+    def _handle(stream):
+        import torch
+        return (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
+
+    def record(self, stream=None):
+        if self.t is not None:
+            return self.t.record(stream) if stream is not None else self.t.record()
+        self._check(_Hip.get().hipEventRecord(self.ev, self._handle(stream)), "hipEventRecord")
+
+    def wait_on(self, stream):
+        """Make `stream` wait for this event."""
+        if self.t is not None:
+            return stream.wait_event(self.t)
+        self._check(_Hip.get().hipStreamWaitEvent(self._handle(stream), self.ev, 0), "hipStreamWaitEvent")
+
+    def elapsed_time(self, end: "Event") -> float:
+        """Milliseconds from this event to `end` (both completed)."""
+        if self.t is not None:
+            return self.t.elapsed_time(end.t)
+        import ctypes
+        ms = ctypes.c_float()
+        self._check(_Hip.get().hipEventElapsedTime(ctypes.byref(ms), self.ev, end.ev), "hipEventElapsedTime")
+        return ms.value
 
 
 def copy_calibration(reps: int = 5, nbytes: int = 1 << 30) -> None:
@@ -161,8 +247,8 @@ class DecodeBench:
             table_stream = "side" if wl.layers > 1 else "main"
         self.table_stream = table_stream
         self.side = torch.cuda.Stream() if table_stream == "side" else self.main   # default priority
-        self.ready = [torch.cuda.Event() for _ in range(2)]
-        self.done = [torch.cuda.Event() for _ in range(2)]
+        self.ready = [Event() for _ in range(2)]
+        self.done = [Event() for _ in range(2)]
         for e in self.done:
             e.record(self.main)
         # per-step inputs: new K/V per layer and the step's queries
@@ -204,7 +290,7 @@ class DecodeBench:
         b = j % 2
         side = self.side
         if side is not self.main:
-            side.wait_event(self.done[b])    # the step that last used these tables has finished
+            self.done[b].wait_on(side)       # the step that last used these tables has finished
         if self.flush is not None:
             self.flush.fill_(j & 0xFF)
         slots, cow = P.pkv_append_slots(self.eng.pool, self.ids)
@@ -219,9 +305,9 @@ class DecodeBench:
         P.pkv_sync_tables(self.eng.pool, self.ids, self.tables[b], self.lens[b], self.eng.host_lens, side)
         if side is not self.main:
             self.ready[b].record(side)
-            self.main.wait_event(self.ready[b])
+            self.ready[b].wait_on(self.main)
         if self.flush is not None and record_events:
-            s0 = torch.cuda.Event(enable_timing=True)
+            s0 = Event(enable_timing=True)
             s0.record(self.main)
         if cow:
             P.pkv_copy_blocks(self.eng.pool, cow)
@@ -241,8 +327,8 @@ class DecodeBench:
                                         #  outside the timed partial launch)
                 P.pkv_kv_append_last(self.eng.pool, l, self.knew[l][j], self.vnew[l][j], self.tables[b], self.lens[b])
             if l == timed:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
+                e0 = Event(enable_timing=True)
+                e1 = Event(enable_timing=True)
                 e0.record()
             P.pkv_paged_decode_partial(a)
             if l == timed:
@@ -252,7 +338,7 @@ class DecodeBench:
         if side is not self.main:
             self.done[b].record(self.main)
         if self.flush is not None and record_events:
-            s1 = torch.cuda.Event(enable_timing=True)
+            s1 = Event(enable_timing=True)
             s1.record(self.main)
             self.step_events.append((s0, s1))
         self.kv_bytes.append(self.attended_bytes(0) * self.layers)
@@ -330,8 +416,8 @@ class PrefillBench:
         for l in range(self.wl.layers):
             P.pkv_kv_append(self.eng.pool, l, self.k[l], self.v[l], self.chunk_slots)
             if record_events:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
+                e0 = Event(enable_timing=True)
+                e1 = Event(enable_timing=True)
                 e0.record()
             P.pkv_paged_prefill(self.args[l])
             if record_events:
@@ -405,8 +491,8 @@ def read_ceiling(nbytes: int, reps: int = 5, tile_bytes: int = 4096):
                 P.pkv_read_tiles(buf, o, tiles, tpw, sink, tile_bytes=tile_bytes)
             ms = []
             for _ in range(reps):
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
+                e0 = Event(enable_timing=True)
+                e1 = Event(enable_timing=True)
                 e0.record()
                 P.pkv_read_tiles(buf, o, tiles, tpw, sink, tile_bytes=tile_bytes)
                 e1.record()
@@ -472,11 +558,16 @@ def run_prefill(args, wl):
         bench.step(record_events=False)
     torch.cuda.synchronize()
     log("timed steps")
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        bench.step(record_events=True)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    gc.collect()
+    gc.disable()
+    try:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            bench.step(record_events=True)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    finally:
+        gc.enable()
     flops_step = wl.prefill_flops(args.window) * wl.layers
     k_ms = [a.elapsed_time(b) for a, b in bench.events]
     k_avg = sum(k_ms) / len(k_ms) / 1e3
@@ -725,6 +816,7 @@ def main():
     import torch
     import workloads
 
+    Event.use_torch = args.torch_events
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
@@ -768,6 +860,7 @@ def main():
                    "partition": args.partition or 512, "window": args.window, "cache_flush": args.flush,
                    "append": "fused into the decode kernel" if bench.fused_append else "separate kernel",
                    "table_upload": f"{bench.table_stream} stream",
+                   "events": "torch" if Event.use_torch else "HIP, no system fence",
                    "start_lengths_mean": float(wl.lengths.mean())},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         # Blocks shared between sequences (a common prefix) are read by each of them; their unique bytes
@@ -831,11 +924,16 @@ def run_decode(args, wl):
     torch.cuda.synchronize()
     log("timed steps")
     bench.kv_bytes.clear()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        bench.step(record_events=True)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    gc.collect()
+    gc.disable()                  # no collector pause inside the timed steps
+    try:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            bench.step(record_events=True)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    finally:
+        gc.enable()
     if args.flush:      # the flush writes are not part of the step
         elapsed = sum(a.elapsed_time(b) for a, b in bench.step_events) / 1e3
     k3_ms = [a.elapsed_time(b) for a, b, _ in bench.events]

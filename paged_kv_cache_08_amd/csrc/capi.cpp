@@ -529,14 +529,17 @@ int pkv_sync_tables(pkv_pool* pool, const int64_t* ids, int32_t n, int32_t* dev_
       grp.pending = false;
       grp.n_ev = 0;
     }
-    if (pool->staging_bytes[k] < need) {
-      if (pool->staging[k]) (void)hipHostFree(pool->staging[k]);
-      pool->staging[k] = nullptr;
-      pool->staging_bytes[k] = 0;
-      const size_t cap = std::max(need, static_cast<size_t>(1) << 20);
-      rc = from_hip(hipHostMalloc(&pool->staging[k], cap, hipHostMallocDefault), "sync_tables: pinned staging");
+    // Pinning host memory takes milliseconds: the first call sizes the whole
+    // ring (no buffer is in use yet); later a buffer grows when its turn comes.
+    const size_t cap = std::max(need, static_cast<size_t>(1) << 20);
+    for (int b = (u == 0 ? 0 : k); b < (u == 0 ? pkv_pool::kStagingRing : k + 1); ++b) {
+      if (pool->staging_bytes[b] >= need) continue;
+      if (pool->staging[b]) (void)hipHostFree(pool->staging[b]);
+      pool->staging[b] = nullptr;
+      pool->staging_bytes[b] = 0;
+      rc = from_hip(hipHostMalloc(&pool->staging[b], cap, hipHostMallocDefault), "sync_tables: pinned staging");
       if (rc) return rc;
-      pool->staging_bytes[k] = cap;
+      pool->staging_bytes[b] = cap;
     }
     int32_t* tab = static_cast<int32_t*>(pool->staging[k]);
     int32_t* lens = tab + static_cast<size_t>(n) * max_blocks;
