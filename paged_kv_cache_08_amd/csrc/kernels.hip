@@ -1276,20 +1276,40 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeParams p) {
   const float* ml = p.part_ml + static_cast<size_t>(row) * p.pmax * 2;
   const float* acc = p.part_acc + static_cast<size_t>(row) * p.pmax * D;
   const int NG = (P + kMergeGroup - 1) / kMergeGroup;
+  const int cg = tid % CG;
+  const int ph = tid / CG;
+  // The thread's groups in the first two rounds: their (m, l) and first
+  // accumulator chunk (all of a merged group) are requested together with
+  // the maxima, so one round trip precedes the merge instead of three.
+  constexpr int R = 2;                               // (the selects below assume 2)
+  float pm[R], pl[R];
+  f32x4 pa[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int g = r * PH + ph;
+    const int g0 = (g < NG ? g : 0) * kMergeGroup;
+    pm[r] = ml[2 * g0];
+    pl[r] = ml[2 * g0 + 1];
+    pa[r] = *reinterpret_cast<const f32x4*>(acc + static_cast<size_t>(g0) * D + 4 * cg);
+  }
   float M = -INFINITY;
   for (int g = tid; g < NG; g += 256) M = fmaxf(M, group_max(ml, g * kMergeGroup, P));
   M = block_max_256(M, scratch);
-  const int cg = tid % CG;
-  const int ph = tid / CG;
   float L = 0.f;
   f32x4 O = {0.f, 0.f, 0.f, 0.f};
   for (int c0 = 0; c0 < NG; c0 += PH) {
     const int g = c0 + ph;
     if (g < NG) {
       const int g0 = g * kMergeGroup;
+      const int r = c0 / PH;
       float Mg, Lg;
       f32x4 Ag;
-      if (merged_group(ml, g0)) {
+      const float plr = r == 0 ? pl[0] : pl[1];
+      if (r < R && plr < 0.f) {                          // merged group, prefetched
+        Mg = r == 0 ? pm[0] : pm[1];
+        Lg = -plr;
+        Ag = r == 0 ? pa[0] : pa[1];
+      } else if (merged_group(ml, g0)) {
         Mg = ml[2 * g0];
         Lg = -ml[2 * g0 + 1];
         Ag = *reinterpret_cast<const f32x4*>(acc + static_cast<size_t>(g0) * D + 4 * cg);
