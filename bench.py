@@ -554,6 +554,10 @@ def run_prefill(args, wl):
     import torch
     log(f"setup {wl.description}")
     bench = PrefillBench(wl, window=args.window)
+    parity = None
+    if not args.no_cpu_baseline:
+        log("validating the first step against the oracle")
+        parity = validate_prefill_first_step(bench, sorted({0, wl.S - 1}))
     for _ in range(args.warmup):
         bench.step(record_events=False)
     torch.cuda.synchronize()
@@ -588,6 +592,8 @@ def run_prefill(args, wl):
                      "avg_launch_us": round(k_avg * 1e6, 2), "launch_us": launch_stats_us(k_ms),
                      "algorithmic_flops_per_launch": wl.prefill_flops(args.window)},
     }
+    if parity is not None:
+        result["parity"] = parity
     log(f"timed {args.steps} steps: {value:.1f} TFLOP/s; prefill kernel {k_avg * 1e6:.1f} us")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -602,6 +608,47 @@ def _bits(t):
     t = t.detach().cpu().contiguous()
     return (t.view(torch.int32).numpy().view(np.uint32) if t.dtype == torch.float32
             else t.view(torch.int16).numpy().view(np.uint16))
+
+
+def pool_problems(eng, rp, layer, seqs, B, window=0):
+    """Compares the library's pool with the oracle's for the batch rows
+    `seqs` of one layer: every block those sequences wrote in full, bit for
+    bit, and each slot of their partly written edge blocks (every head and
+    value; the 8-bit pools' scales too).  Returns the differences found."""
+    import numpy as np
+    import torch
+    problems = []
+    tables, lengths = rp.tables(), rp.lengths()
+    pool = rp.pool
+    pairs = [(pool.K[layer], eng.k[layer]), (pool.V[layer], eng.v[layer])]
+    if pool.dtype == "fp8":
+        pairs += [(pool.KS[layer], eng.ks[layer]), (pool.VS[layer], eng.vs[layer])]
+    for ref, dev in pairs:
+        ours = (dev.cpu().numpy() if dev.dtype == torch.uint8 else _bits(dev)).reshape(ref.shape)
+
+        def slot(arr, b, o):                  # token slot o of block b, every head and value
+            if arr.ndim == 3:                                            # scales [block][head][slot]
+                return arr[b][:, o]
+            if arr.ndim == 7:                                            # 8-bit V [block][head][a][u][c][b][w]
+                return arr[b][:, :, o // 4, :, :, o % 4]
+            if arr.ndim == 6:                                            # V [block][head][u][c][b][w]
+                return arr[b][:, o // 4, :, :, o % 4]
+            return arr[b][:, :, o]                                       # K [block][head][d/x][slot][x]
+
+        for i in seqs:
+            n = lengths[i]
+            t0 = max(0, n - window) if window else 0
+            whole = [tables[i][j] for j in range(-(-t0 // B), n // B)]  # blocks written in full
+            if whole and not np.array_equal(ours[whole], ref[whole]):
+                problems.append(f"layer {layer}: pool blocks of batch row {i} differ")
+            edge = [t for t in range(t0, n) if t < -(-t0 // B) * B or t >= (n // B) * B]
+            for t in edge:
+                b, o = tables[i][t // B], t % B
+                if not np.array_equal(slot(ours, b, o), slot(ref, b, o)):
+                    problems.append(f"layer {layer}: pool slot {t} of batch row {i} differs")
+                    break
+        del ours
+    return problems
 
 
 def validate_first_step(bench, layers, seqs, atol: float = 2e-2, row_rtol: float = 1e-2):
@@ -651,37 +698,7 @@ def validate_first_step(bench, layers, seqs, atol: float = 2e-2, row_rtol: float
     tables, lengths = rp.tables(), rp.lengths()
     worst_abs, worst_rel = 0.0, 0.0
     for l in layers:
-        # pool bytes of the checked sequences: every written slot
-        pool = rp.pool
-        pairs = [(pool.K[l], bench.eng.k[l]), (pool.V[l], bench.eng.v[l])]
-        if pool.dtype == "fp8":
-            pairs += [(pool.KS[l], bench.eng.ks[l]), (pool.VS[l], bench.eng.vs[l])]
-        B = wl.block
-        for ref, dev in pairs:
-            ours = (dev.cpu().numpy() if dev.dtype == torch.uint8 else _bits(dev)).reshape(ref.shape)
-
-            def slot(arr, b, o):                  # token slot o of block b, every head and value
-                if arr.ndim == 3:                                            # scales [block][head][slot]
-                    return arr[b][:, o]
-                if arr.ndim == 7:                                            # 8-bit V [block][head][a][u][c][b][w]
-                    return arr[b][:, :, o // 4, :, :, o % 4]
-                if arr.ndim == 6:                                            # V [block][head][u][c][b][w]
-                    return arr[b][:, o // 4, :, :, o % 4]
-                return arr[b][:, :, o]                                       # K [block][head][d/x][slot][x]
-
-            for i in seqs:
-                n = lengths[i]
-                t0 = max(0, n - bench.window) if bench.window else 0
-                whole = [tables[i][j] for j in range(-(-t0 // B), n // B)]  # blocks written in full
-                if whole and not np.array_equal(ours[whole], ref[whole]):
-                    problems.append(f"layer {l}: pool blocks of batch row {i} differ")
-                edge = [t for t in range(t0, n) if t < -(-t0 // B) * B or t >= (n // B) * B]
-                for t in edge:
-                    b, o = tables[i][t // B], t % B
-                    if not np.array_equal(slot(ours, b, o), slot(ref, b, o)):
-                        problems.append(f"layer {l}: pool slot {t} of batch row {i} differs")
-                        break
-            del ours
+        problems += pool_problems(bench.eng, rp, l, seqs, wl.block, bench.window)
         q64 = to_f64(_bits(bench.q[l]), wl.dtype)
         heads = {(i, h) for i in seqs for h in range(wl.Hq)}
         ref = OA.decode(rp.pool, l, tables, lengths, q64, wl.Hq, heads=heads, window=bench.window)
@@ -707,6 +724,74 @@ def validate_first_step(bench, layers, seqs, atol: float = 2e-2, row_rtol: float
         print(json.dumps({"metric": METRIC, "value": None, "parity": record, "errors": problems[:20]}), flush=True)
         sys.exit(3)
     log(f"validated the first step on {record['rows']} rows: max_abs {worst_abs:.3e}, row_rel {worst_rel:.3e}")
+    return record
+
+
+def validate_prefill_first_step(bench, seqs, atol: float = 2e-2, row_rtol: float = 1e-2):
+    """The oracle leg of a prefill run, before anything is timed: runs the
+    first step (the chunk's append and the prefill kernel, as timed) and
+    compares layer 0 with the oracle's prefill on the batch rows `seqs`:
+    every query head at the chunk's first and last two positions, its middle,
+    and the positions around the first 16-token block, 64-token tile and
+    384-row workgroup boundaries.  The oracle replays the setup through its
+    own allocator and pool, writing only those sequences' tokens.  Checked:
+    the allocator state and those sequences' pool slots bit for bit, and the
+    outputs within max |err| <= atol and row-normwise <= row_rtol.  Returns
+    the parity record; exits with status 3 on a mismatch."""
+    import numpy as np
+    import torch
+    from oracle import attention as OA
+    from oracle.pool import to_f64
+    from oracle.replay import Replay
+
+    wl = bench.wl
+    bench.step(record_events=False)
+    torch.cuda.synchronize()
+    sids = {wl.seq_ids[i] for i in seqs}
+    srcs = {op[3] for op in wl.setup_ops + wl.step_ops if op[0] == "extend" and op[1] in sids}
+    _, k, v = wl.tensors(0, device=bench.dev)
+    rp = Replay(wl, layers=1).run(wl.setup_ops + wl.step_ops, {0: (_bits(k), _bits(v))}, sources=srcs)
+    del k, v
+    problems = []
+    if bench.eng.snapshot() != tuple(rp.alloc.snapshot()):
+        problems.append("allocator state differs")
+    problems += pool_problems(bench.eng, rp, 0, seqs, wl.block)
+    G = wl.Hq // wl.Hkv
+    starts = np.concatenate([[0], np.cumsum(wl.chunk_lens)])
+    rows = []
+    for i in seqs:
+        m = int(wl.chunk_lens[i])
+        pos = {0, 1, m // 2, m - 2, m - 1}
+        for b in (16, 64, 384 // G):
+            pos |= {b - 1, b}
+        rows += [(int(starts[i]) + t, h) for t in sorted(t for t in pos if 0 <= t < m) for h in range(wl.Hq)]
+    ref = OA.prefill(rp.pool, 0, rp.tables(), rp.lengths(), wl.chunk_lens, to_f64(_bits(bench.q[0]), wl.dtype),
+                     wl.Hq, window=bench.window, rows=set(rows))
+    got = bench.out[0].float().cpu().double().numpy()
+    g = np.stack([got[r, h] for r, h in rows])
+    r = np.stack([ref[r, h] for r, h in rows])
+    worst_abs = worst_rel = float("nan")
+    if not np.all(np.isfinite(g)):
+        problems.append("non-finite outputs")
+    else:
+        err = np.abs(g - r)
+        worst_abs = float(err.max())
+        worst_rel = float((err.max(axis=1) / np.maximum(np.abs(r).max(axis=1), 1e-300)).max())
+        if worst_abs > atol or worst_rel > row_rtol:
+            problems.append(f"outputs beyond tolerance: max_abs {worst_abs:.3e}, row_rel {worst_rel:.3e}")
+    record = {"checked": "first prefill step, before timing, against the oracle", "layers": [0],
+              "batch_rows": list(map(int, seqs)), "rows": len(rows), "max_abs": worst_abs, "row_rel": worst_rel,
+              "atol": atol, "row_rtol": row_rtol,
+              "allocator": "bit-exact" if "allocator state differs" not in problems else "differs",
+              "pool": "checked sequences' slots bit-exact" if not any("pool" in p for p in problems) else "differs",
+              "pass": not problems}
+    if problems:
+        log("VALIDATION FAILED: " + "; ".join(problems[:5]))
+        print(json.dumps({"metric": "paged prefill attention", "value": None, "parity": record,
+                          "errors": problems[:20]}), flush=True)
+        sys.exit(3)
+    log(f"validated the first prefill step on {len(rows)} (row, head) pairs: max_abs {worst_abs:.3e}, "
+        f"row_rel {worst_rel:.3e}")
     return record
 
 

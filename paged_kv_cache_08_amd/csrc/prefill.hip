@@ -364,11 +364,18 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16(PrefillParams p) {
         }
         // IEEE maximum (v_maximum3_f32): the scores are never NaN here (every
         // key the cores read is a cached token or zero), and unlike fmaxf it
-        // needs no canonicalisation of the matrix cores' results first.
-        float mx = fmax_ieee(fmax_ieee(fmax_ieee(x[0], x[1]), fmax_ieee(x[2], x[3])),
-                             fmax_ieee(fmax_ieee(x[4], x[5]), fmax_ieee(x[6], x[7])));
-        mx = max_over_rows_ieee(mx);
+        // needs no canonicalisation of the matrix cores' results first.  The
+        // eight scores take four three-input maxima when grouped this way.
+        // Each lane tests its own maximum against its row's threshold; the
+        // row maxima across the row's four lanes are formed only when some
+        // score exceeds it (the same maxima, so the same rescale): the
+        // softmax issue, not the matrix cores, sets this kernel's pace, and
+        // the common path saves the cross-lane steps.
+        const float m012 = fmax_ieee(fmax_ieee(x[0], x[1]), x[2]);
+        const float m345 = fmax_ieee(fmax_ieee(x[3], x[4]), x[5]);
+        float mx = fmax_ieee(fmax_ieee(fmax_ieee(m012, m345), x[6]), x[7]);
         if (__any(mx > thr[rb])) {
+          mx = max_over_rows_ieee(mx);
           // Rows of one block have different masks: a row whose maximum did
           // not grow keeps alpha = 1 (also with no key yet, m = -inf).
           const float m_new = fmax_ieee(m_run[rb], mx);
