@@ -823,19 +823,33 @@ def cpu_baseline(wl_name: str, seconds: float, window: int = 0):
         sample = "whole batch, one layer"
     if base != wl_name:
         wl = workloads.fp8_cache(wl)
+    from oracle.allocator import NoBlocks
     q, k, v = wl.tensors(0, device="cpu")
-    rp = Replay(wl, layers=1).run(wl.setup_ops, {0: (bits(k), bits(v))})
+    kv_bits = {0: (bits(k), bits(v))}
     g = torch.Generator().manual_seed(5)
     q64 = to_f64(bits(q), wl.dtype)
-    state = {"lengths": [int(n) - 1 for n in wl.lengths]}
+    state = {}
+
+    def restart():
+        # the set-up state again (outside the timing): a small pool runs out
+        # of free blocks after enough steps of growth
+        state["rp"] = Replay(wl, layers=1).run(wl.setup_ops, kv_bits)
+        state["lengths"] = [int(n) - 1 for n in wl.lengths]
+
+    restart()
 
     def run(budget):
         steps, kv, t = 0, 0, 0.0
         while t < budget or steps == 0:
             kn = torch.randn((wl.S, wl.Hkv, wl.d), generator=g).to(q.dtype)
             vn = torch.randn((wl.S, wl.Hkv, wl.d), generator=g).to(q.dtype)
+            rp = state["rp"]
             t0 = time.perf_counter()
-            slots, cow = rp.alloc.append(list(wl.seq_ids))
+            try:
+                slots, cow = rp.alloc.append(list(wl.seq_ids))
+            except NoBlocks:
+                restart()
+                continue
             for a, b in cow:
                 rp.pool.copy_block(a, b)
             rp.pool.scatter(0, slots, bits(kn), bits(vn))

@@ -54,3 +54,13 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_cpu_baseline_outlasts_a_small_pool():
+    """The oracle's timing leg keeps stepping a batch whose pool fills up: the
+    tiny batch's 32 blocks hold about a hundred steps of growth, and the leg
+    starts again from the set-up state instead of failing."""
+    r = bench.cpu_baseline("tiny", 1.0)
+    steps = int(r["sample"].split(";")[1].split()[0])
+    assert steps > 150, r["sample"]
+    assert r["value"] > 0 and r["kind"] == "oracle"
