@@ -232,14 +232,18 @@ class DecodeBench:
             del k, v
         torch.cuda.synchronize()
         self.ids = list(wl.seq_ids)
-        self.lengths = [int(n) - 1 for n in wl.lengths]        # current lengths
-        self.max_len = max(self.lengths) + steps_total
+        # numpy forms for the per-step host work, which a short step's kernels
+        # (about 70 us for 128 sequences) would otherwise wait for
+        self.ids_np = np.asarray(self.ids, dtype=np.int64)
+        self.lengths = np.asarray([int(n) - 1 for n in wl.lengths], dtype=np.int64)   # current lengths
+        self.max_len = int(self.lengths.max()) + steps_total
         self.max_blocks = -(-self.max_len // wl.block)
         self.tables = [torch.empty((len(self.ids), self.max_blocks), dtype=torch.int32, device=self.dev)
                        for _ in range(2)]
         self.lens = [torch.empty((len(self.ids),), dtype=torch.int32, device=self.dev) for _ in range(2)]
         self.eng.host_lens = np.zeros(len(self.ids), dtype=np.int32)
         self.main = torch.cuda.current_stream()
+        self.main_ptr = self.main.cuda_stream     # passed to each call: no stream query per launch
         # The side stream overlaps the upload with the previous step's layers, but the cross-stream wait
         # leaves a gap of about 11 us; in line the upload costs about 6 us.  One layer has nothing to
         # overlap it with.
@@ -293,24 +297,24 @@ class DecodeBench:
             self.done[b].wait_on(side)       # the step that last used these tables has finished
         if self.flush is not None:
             self.flush.fill_(j & 0xFF)
-        slots, cow = P.pkv_append_slots(self.eng.pool, self.ids)
-        for i in range(len(self.lengths)):
-            self.lengths[i] += 1
+        slots, cow = P.pkv_append_slots(self.eng.pool, self.ids_np)
+        self.lengths += 1
         if self.window:                  # a block that has just left the window goes back to the pool
             B = self.wl.block
-            for sid, n in zip(self.ids, self.lengths):
+            for sid, n in zip(self.ids, self.lengths.tolist()):
                 start = n - self.window
                 if start > 0 and start % B == 0:
                     P.pkv_seq_release_before(self.eng.pool, sid, start)
-        P.pkv_sync_tables(self.eng.pool, self.ids, self.tables[b], self.lens[b], self.eng.host_lens, side)
+        P.pkv_sync_tables(self.eng.pool, self.ids_np, self.tables[b], self.lens[b], self.eng.host_lens, side)
         if side is not self.main:
             self.ready[b].record(side)
             self.ready[b].wait_on(self.main)
         if self.flush is not None and record_events:
             s0 = Event(enable_timing=True)
             s0.record(self.main)
+        ms = self.main_ptr
         if cow:
-            P.pkv_copy_blocks(self.eng.pool, cow)
+            P.pkv_copy_blocks(self.eng.pool, cow, ms)
         # A timing event costs the stream about 5 us, so a step times one
         # partial-kernel launch (layers in turn); a one-layer step (well
         # under a millisecond) every fourth step.
@@ -325,16 +329,17 @@ class DecodeBench:
                 P.set_new_token(a, self.knew[l][j], self.vnew[l][j])
             else:                       # (the call would run the append kernel first: do it here,
                                         #  outside the timed partial launch)
-                P.pkv_kv_append_last(self.eng.pool, l, self.knew[l][j], self.vnew[l][j], self.tables[b], self.lens[b])
+                P.pkv_kv_append_last(self.eng.pool, l, self.knew[l][j], self.vnew[l][j], self.tables[b], self.lens[b],
+                                     stream=ms)
             if l == timed:
                 e0 = Event(enable_timing=True)
                 e1 = Event(enable_timing=True)
                 e0.record()
-            P.pkv_paged_decode_partial(a)
+            P.pkv_paged_decode_partial(a, ms)
             if l == timed:
                 e1.record()
                 self.events.append((e0, e1, self.attended_bytes(l)))
-            P.pkv_paged_decode_reduce(a)
+            P.pkv_paged_decode_reduce(a, ms)
         if side is not self.main:
             self.done[b].record(self.main)
         if self.flush is not None and record_events:
@@ -350,7 +355,7 @@ class DecodeBench:
         np = self.np
         B = self.wl.block
         slots = []
-        for sid, n in zip(self.ids, self.lengths):
+        for sid, n in zip(self.ids, self.lengths.tolist()):
             table = np.asarray(self.P.pkv_seq_table(self.eng.pool, sid), dtype=np.int64)
             t = np.arange(max(0, n - self.window) if self.window else 0, n)
             slots.append(table[t // B] * B + t % B)
@@ -360,7 +365,8 @@ class DecodeBench:
     def attended_bytes(self, layer: int) -> int:
         """KV bytes one layer's partial kernel reads at the current lengths."""
         wl = self.wl
-        attended = sum(min(n, self.window) if self.window else n for n in self.lengths)
+        n = self.lengths
+        attended = int((self.np.minimum(n, self.window) if self.window else n).sum())
         return attended * wl.Hkv * wl.kv_bytes_per_token_head()
 
 
