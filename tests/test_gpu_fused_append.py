@@ -2,8 +2,9 @@
 (pkv_decode_args.k_new / v_new).  It must leave the pool exactly as the
 separate kv_append_last would (bf16, fp32 and 8-bit pools, scales
 included), give the same output bits, and match the oracle.  Covers
-query-head groups above 16 and batches above 1024 (sequence, KV head)
-rows (there the call runs the append kernel first), a copy-on-write
+query-head groups above 16, batches above 1024 (sequence, KV head)
+rows (there the call runs the append kernel first) and above the work
+list's 512 sequences, a copy-on-write
 step, a sliding window, and launches with and without the host length
 hint."""
 import numpy as np
@@ -40,6 +41,9 @@ CASES = {
     "copy-on-write": _cow_batch,
     "1280 rows (append kernel first)": lambda: workloads.random_small(207, S=160, Hq=8, Hkv=8, d=64,
                                                                       dtype="bf16", max_len=150),
+    # more sequences than the launch's work list holds (512): a plain grid even with the hint
+    "600 sequences (no work list)": lambda: workloads.random_small(208, S=600, Hq=4, Hkv=2, d=64,
+                                                                   dtype="bf16", max_len=200),
 }
 
 
