@@ -335,7 +335,12 @@ typedef struct pkv_decode_args {
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t max_seq_len, int32_t partition);
 /* Partial kernel followed, when max_seq_len exceeds one partition, by the
- * reduce kernel; both on `stream`.                                        */
+ * reduce kernel; both on `stream`.  The call only launches kernels (no
+ * allocation, copy, memset or synchronisation), all reading their inputs
+ * through the pointers in `args`, so it can be captured in a HIP graph and
+ * replayed: each replay reads the buffers' contents at that time.  The
+ * launch plan (from host_seq_lens, when given) is fixed at capture; the
+ * results never depend on it.                                              */
 int pkv_paged_attention_decode(const pkv_decode_args* args, void* stream);
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, serving loops that must not allocate, harnesses that forbid it):
@@ -348,8 +353,10 @@ int pkv_paged_attention_decode(const pkv_decode_args* args, void* stream);
  * before any device work.  Every call on one device uses the same array:
  * calls that overlap on a device (other streams, other threads) race on it,
  * so the caller serialises them.  The workspace needs no clearing (every
- * partial result is written before the reduce reads it).  Other arguments,
- * errors and results are those of pkv_paged_attention_decode.             */
+ * partial result is written before the reduce reads it).  Under graph
+ * capture, make one call on the device outside the capture first (the
+ * address lookup).  Other arguments, errors and results are those of
+ * pkv_paged_attention_decode.                                              */
 int pkv_paged_attention_decode_static(const pkv_decode_args* args, void* stream);
 /* The partial kernel alone (single-partition sequences are finished here). */
 int pkv_paged_decode_partial(const pkv_decode_args* args, void* stream);
