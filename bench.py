@@ -411,9 +411,16 @@ class PrefillBench:
         qs = np.zeros(len(self.chunks) + 1, dtype=np.int32)
         qs[1:] = np.cumsum(self.chunks)
         self.query_start = torch.from_numpy(qs).to(self.dev)
+        ws = None
+        if self.eng.ks is not None:   # 8-bit cache: the call's bf16 copy of the blocks lives in a workspace
+            ws = self.eng.prefill_workspace(P.pkv_prefill_workspace_bytes(
+                wl.S, wl.Hkv, wl.d, wl.block, self.eng.tables.shape[1], wl.max_len, P.PKV_FP8_E4M3))
         self.args = [P.prefill_args(self.q[l], self.out[l], self.eng.k[l], self.eng.v[l], self.eng.tables,
                                     self.eng.lens, self.query_start, wl.Hkv, wl.num_blocks, wl.max_len,
-                                    max(self.chunks), window=window) for l in range(wl.layers)]
+                                    max(self.chunks), window=window,
+                                    k_scale=None if self.eng.ks is None else self.eng.ks[l],
+                                    v_scale=None if self.eng.vs is None else self.eng.vs[l], workspace=ws)
+                     for l in range(wl.layers)]
         torch.cuda.synchronize()
         self.events = []
 
@@ -447,6 +454,8 @@ def prefill_cpu_baseline(wl, seconds: float, window: int = 0):
 
     one = workloads.prefill_chunks(wl.lengths[:1] - wl.chunk_lens[:1], wl.chunk_lens[:1], wl.Hq, wl.Hkv, wl.d,
                                    wl.dtype, wl.seed)
+    if wl.cache_dtype == "fp8":
+        one = workloads.fp8_cache(one)
     q = one.prefill_queries()
     _, k, v = one.tensors()
     rp = Replay(one).run(one.setup_ops + one.step_ops, {0: (bits(k), bits(v))})
@@ -591,7 +600,7 @@ def run_prefill(args, wl):
         "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": wl.name, "description": wl.description, "layers": wl.layers, "S": wl.S,
                    "Hq": wl.Hq, "Hkv": wl.Hkv, "d": wl.d, "block": wl.block, "window": args.window,
-                   "chunk_mean": float(wl.chunk_lens.mean()), "length_mean": float(wl.lengths.mean())},
+                   "kv_cache": wl.cache_dtype, "chunk_mean": float(wl.chunk_lens.mean()), "length_mean": float(wl.lengths.mean())},
         "prefill_tokens_per_s": round(float(wl.chunk_lens.sum()) * args.steps / elapsed, 1),
         "roofline": {"bound": "mfma", "kernel": "prefill_bf16", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,

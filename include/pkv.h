@@ -415,7 +415,16 @@ int pkv_decode_plan(const pkv_decode_args* args, pkv_decode_plan_info* info, int
  * gathered through block_tables as for decode.  fp32 accumulation, bf16
  * output (nearest even).  Sequences with m > n, n > max_seq_len or a needed
  * block id outside the pool get NaN rows; m = 0 is allowed (no rows).
- * Supported: bf16 q/out/cache, block_size 16, head_dim 64 or 128.          */
+ * Supported: bf16 q/out, block_size 16, head_dim 64 or 128; a bf16 cache,
+ * or an 8-bit (PKV_FP8_E4M3) cache with its scales and a workspace of
+ * pkv_prefill_workspace_bytes() bytes («¿Cuánta memoria reservar para la
+ * caché KV?», "Reducir la precisión").  For the 8-bit cache the call first
+ * writes every block the sequences hold as bf16 (code × scale in fp32,
+ * rounded to nearest even) into the workspace, laid out as a bf16 pool
+ * with tables of its own, and attends over that copy: the same kernel and
+ * the same results as a bf16 cache holding those rounded values.  The
+ * workspace is scratch, overwritten by each call (calls sharing it must not
+ * overlap); it needs no clearing.                                          */
 typedef struct pkv_prefill_args {
   const void* q;              /* device [T][Hq][d] bf16, T = query_start[S] */
   void* out;                  /* device [T][Hq][d] bf16                     */
@@ -437,7 +446,19 @@ typedef struct pkv_prefill_args {
   float scale;                /* score scale, e.g. 1/sqrt(d); positive and  */
                               /*   finite (else PKV_ERR_INVALID)            */
   int32_t window;             /* > 0: sliding window; 0 = causal, full      */
+  /* 8-bit cache only (dtype PKV_FP8_E4M3; ignored for bf16):                */
+  const float* k_scale;       /* device per-slot K scales [num_blocks][Hkv][B] */
+  const float* v_scale;       /* device per-slot V scales, same shape        */
+  void* workspace;            /* device, 256-byte aligned                    */
+  size_t workspace_bytes;     /* >= pkv_prefill_workspace_bytes(...)         */
 } pkv_prefill_args;
+/* Workspace bytes pkv_paged_prefill needs: 0 for a bf16 cache; for an 8-bit
+ * cache the bf16 copy (num_seqs · ceil(max_seq_len / block_size) blocks of
+ * K and V) and its tables (num_seqs · max_blocks int32).  0 for sizes the
+ * call would reject.                                                       */
+size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t max_blocks, int32_t max_seq_len,
+                                   int32_t dtype);
 
 /* One kernel on `stream`; no workspace.                                    */
 int pkv_paged_prefill(const pkv_prefill_args* args, void* stream);

@@ -20,6 +20,7 @@
 
 #include "block_pool.hpp"
 #include "kernels.hpp"
+#include "prefill_stage.hpp"
 
 struct pkv_pool {
   pkv::BlockPool alloc;
@@ -318,7 +319,7 @@ const char* pkv_status_string(int status) {
 
 const char* pkv_last_error(void) { return g_error.c_str(); }
 
-int pkv_version(void) { return 200; }
+int pkv_version(void) { return 300; }
 
 int pkv_pool_create(const pkv_pool_desc* d, pkv_pool** out) {
   return guarded([&]() -> int {
@@ -839,9 +840,19 @@ int pkv_decode_plan(const pkv_decode_args* a, pkv_decode_plan_info* info, int32_
   return PKV_OK;
 }
 
+size_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int32_t max_blocks, int32_t max_seq_len, int32_t dtype) {
+  if (dtype != PKV_FP8_E4M3 || num_seqs < 1 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 ||
+      max_blocks < 1 || max_seq_len < 1)
+    return 0;
+  const int64_t nb = (static_cast<int64_t>(max_seq_len) + block_size - 1) / block_size;
+  return pkv::prefill_stage_bytes(num_seqs, num_kv_heads, head_dim, max_blocks, nb);
+}
+
 int pkv_paged_prefill(const pkv_prefill_args* a, void* stream) {
   if (!a) return fail(PKV_ERR_INVALID, "prefill: null args");
-  if (a->dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "prefill: bf16 only");
+  if (a->dtype != PKV_BF16 && a->dtype != PKV_FP8_E4M3)
+    return fail(PKV_ERR_UNSUPPORTED, "prefill: bf16 or 8-bit (E4M3) caches only");
   if (a->num_seqs < 1 || a->num_kv_heads < 1 || a->num_q_heads < 1 || a->head_dim < 1 || a->block_size < 1 ||
       a->num_blocks < 1 || a->max_blocks < 1 || a->max_seq_len < 1 || a->max_query_len < 0)
     return fail(PKV_ERR_INVALID, "prefill: sizes must be positive");
@@ -860,7 +871,21 @@ int pkv_paged_prefill(const pkv_prefill_args* a, void* stream) {
   const int64_t tiles = (static_cast<int64_t>(a->max_query_len) * G + 63) / 64;   // >= the real count
   if (tiles > 65535 || static_cast<int64_t>(a->num_seqs) * a->num_kv_heads > 0x7fffffffLL)
     return fail(PKV_ERR_INVALID, "prefill: grid too large");
+  const bool fp8 = a->dtype == PKV_FP8_E4M3;
+  const int64_t nb = (static_cast<int64_t>(a->max_seq_len) + a->block_size - 1) / a->block_size;
+  if (fp8) {
+    if (!a->k_scale || !a->v_scale) return fail(PKV_ERR_INVALID, "prefill: an 8-bit cache needs its scales");
+    const size_t need = pkv::prefill_stage_bytes(a->num_seqs, a->num_kv_heads, a->head_dim, a->max_blocks, nb);
+    if (!a->workspace || a->workspace_bytes < need)
+      return fail(PKV_ERR_INVALID, "prefill: an 8-bit cache needs a workspace of pkv_prefill_workspace_bytes() (" +
+                                       std::to_string(need) + " bytes)");
+    if (reinterpret_cast<uintptr_t>(a->workspace) % 256 != 0)
+      return fail(PKV_ERR_INVALID, "prefill: workspace must be 256-byte aligned");
+    if (static_cast<int64_t>(a->num_seqs) * nb > 0x7fffffffLL)
+      return fail(PKV_ERR_INVALID, "prefill: too many blocks for the 8-bit copy");
+  }
   if (a->max_query_len == 0) return PKV_OK;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
   pkv::PrefillParams p{};
   p.q = a->q;
   p.out = a->out;
@@ -880,7 +905,30 @@ int pkv_paged_prefill(const pkv_prefill_args* a, void* stream) {
   p.max_query_len = a->max_query_len;
   p.window = a->window;
   p.scale_log2 = a->scale * 1.4426950408889634f;
-  return from_hip(pkv::launch_prefill(p, static_cast<hipStream_t>(stream)), "prefill");
+  if (fp8) {                        // attend over a bf16 copy of the blocks the sequences hold
+    pkv::PrefillStageParams sp{};
+    sp.k_cache = static_cast<const uint8_t*>(a->k_cache);
+    sp.v_cache = static_cast<const uint8_t*>(a->v_cache);
+    sp.k_scale = a->k_scale;
+    sp.v_scale = a->v_scale;
+    sp.block_tables = a->block_tables;
+    sp.seq_lens = a->seq_lens;
+    sp.S = a->num_seqs;
+    sp.Hkv = a->num_kv_heads;
+    sp.d = a->head_dim;
+    sp.num_blocks = a->num_blocks;
+    sp.max_blocks = a->max_blocks;
+    sp.max_seq_len = a->max_seq_len;
+    sp.nb = static_cast<int32_t>(nb);
+    pkv::prefill_stage_layout(&sp, a->workspace);
+    const int rc = from_hip(pkv::launch_prefill_stage(sp, st), "prefill: 8-bit copy");
+    if (rc) return rc;
+    p.k_cache = sp.k_out;
+    p.v_cache = sp.v_out;
+    p.block_tables = sp.tables_out;
+    p.num_blocks = static_cast<int32_t>(static_cast<int64_t>(a->num_seqs) * nb);
+  }
+  return from_hip(pkv::launch_prefill(p, st), "prefill");
 }
 
 int pkv_read_tiles(const void* base, int64_t base_bytes, int32_t tile_bytes, const int32_t* order, int64_t n_tiles,

@@ -176,10 +176,25 @@ class PagedDecodeEngine:
         qs = np.zeros(len(chunk_lens) + 1, dtype=np.int32)
         qs[1:] = np.cumsum(chunk_lens)
         self.query_start = torch.from_numpy(qs).to(self.device)
+        ks = vs = ws = None
+        if self.ks is not None:       # 8-bit cache: its scales and the bf16 copy's workspace
+            ks, vs = self.ks[layer], self.vs[layer]
+            nbytes = P.pkv_prefill_workspace_bytes(len(chunk_lens), self.Hkv, self.d, self.B, self.tables.shape[1],
+                                                   max_seq_len, P.PKV_FP8_E4M3)
+            ws = self.prefill_workspace(nbytes)
         a = P.prefill_args(q, out, self.k[layer], self.v[layer], self.tables, self.lens, self.query_start,
-                           self.Hkv, self.N, max_seq_len, int(max(chunk_lens)), scale, window, self.B)
+                           self.Hkv, self.N, max_seq_len, int(max(chunk_lens)), scale, window, self.B,
+                           k_scale=ks, v_scale=vs, workspace=ws)
         P.pkv_paged_prefill(a, stream)
         return out
+
+    def prefill_workspace(self, nbytes: int) -> torch.Tensor:
+        """A device scratch buffer of at least nbytes (256-byte aligned by the
+        caching allocator), kept for later calls."""
+        ws = getattr(self, "_prefill_ws", None)
+        if ws is None or ws.numel() < nbytes:
+            ws = self._prefill_ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=self.device)
+        return ws
 
     def snapshot(self):
         return P.pkv_pool_snapshot(self.pool)

@@ -76,7 +76,8 @@ class pkv_prefill_args(ctypes.Structure):
                 ("num_seqs", _i32), ("num_q_heads", _i32), ("num_kv_heads", _i32),
                 ("head_dim", _i32), ("block_size", _i32), ("num_blocks", _i32),
                 ("max_blocks", _i32), ("max_seq_len", _i32), ("max_query_len", _i32),
-                ("dtype", _i32), ("scale", ctypes.c_float), ("window", _i32)]
+                ("dtype", _i32), ("scale", ctypes.c_float), ("window", _i32),
+                ("k_scale", _vp), ("v_scale", _vp), ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t)]
 
 
 _lib = None
@@ -117,6 +118,7 @@ SIGNATURES = [
     ("pkv_decode_fuses_append", ctypes.c_int, [_P(pkv_decode_args)]),
     ("pkv_decode_plan", ctypes.c_int, [_P(pkv_decode_args), _P(pkv_decode_plan_info), _P(_i32), _i64]),
     ("pkv_paged_prefill", ctypes.c_int, [_P(pkv_prefill_args), _vp]),
+    ("pkv_prefill_workspace_bytes", ctypes.c_size_t, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     ("pkv_read_tiles", ctypes.c_int, [_vp, _i64, _i32, _vp, _i64, _i32, _vp, _vp]),
 ]
 
@@ -497,9 +499,13 @@ def pkv_decode_plan(args: pkv_decode_args, with_cells: bool = True):
 
 def prefill_args(q, out, k_cache, v_cache, block_tables, seq_lens, query_start, num_kv_heads: int,
                  num_blocks: int, max_seq_len: int, max_query_len: int, scale: Optional[float] = None,
-                 window: int = 0, block_size: int = 16) -> pkv_prefill_args:
+                 window: int = 0, block_size: int = 16, k_scale=None, v_scale=None,
+                 workspace=None) -> pkv_prefill_args:
     """Pack a pkv_prefill_args from tensors: q/out [T][Hq][d] bf16,
-    query_start int32 [S + 1] (device), seq_lens int32 [S] (device)."""
+    query_start int32 [S + 1] (device), seq_lens int32 [S] (device).  An
+    8-bit cache (uint8 tensors) also takes its scales and a device
+    workspace of pkv_prefill_workspace_bytes() bytes (a uint8 tensor)."""
+    import torch
     T, Hq, d = q.shape
     a = pkv_prefill_args()
     a.q, a.out, a.k_cache, a.v_cache = _ptr(q), _ptr(out), _ptr(k_cache), _ptr(v_cache)
@@ -509,10 +515,19 @@ def prefill_args(q, out, k_cache, v_cache, block_tables, seq_lens, query_start, 
     a.block_size, a.num_blocks = block_size, num_blocks
     a.max_blocks = block_tables.shape[1]
     a.max_seq_len, a.max_query_len = max_seq_len, max_query_len
-    a.dtype = PKV_BF16
+    a.dtype = PKV_FP8_E4M3 if k_cache.dtype == torch.uint8 else PKV_BF16
     a.scale = 1.0 / math.sqrt(d) if scale is None else scale
     a.window = window
+    a.k_scale, a.v_scale = _ptr(k_scale), _ptr(v_scale)
+    if workspace is not None:
+        a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     return a
+
+
+def pkv_prefill_workspace_bytes(num_seqs: int, num_kv_heads: int, head_dim: int, block_size: int,
+                                max_blocks: int, max_seq_len: int, dtype: int) -> int:
+    return lib().pkv_prefill_workspace_bytes(num_seqs, num_kv_heads, head_dim, block_size, max_blocks,
+                                             max_seq_len, dtype)
 
 
 def pkv_paged_prefill(args: pkv_prefill_args, stream=None) -> None:

@@ -157,11 +157,27 @@ def _prefill_args(**kw):
     (dict(scale=float("nan")), P.PKV_ERR_INVALID),
     (dict(query_start=0), P.PKV_ERR_INVALID),
     (dict(q=8), P.PKV_ERR_INVALID),                # misaligned
+    # an 8-bit cache needs its scales and a 256-byte aligned workspace of the stated size
+    (dict(dtype=P.PKV_FP8_E4M3, workspace=256, workspace_bytes=1 << 30), P.PKV_ERR_INVALID),
+    (dict(dtype=P.PKV_FP8_E4M3, k_scale=16, v_scale=16), P.PKV_ERR_INVALID),
+    (dict(dtype=P.PKV_FP8_E4M3, k_scale=16, v_scale=16, workspace=256, workspace_bytes=1000), P.PKV_ERR_INVALID),
+    (dict(dtype=P.PKV_FP8_E4M3, k_scale=16, v_scale=16, workspace=16, workspace_bytes=1 << 30), P.PKV_ERR_INVALID),
 ])
 def test_prefill_argument_validation(bad, status):
     with pytest.raises(P.PkvError) as e:
         P.pkv_paged_prefill(_prefill_args(**bad), stream=0)
     assert e.value.status == status
+
+
+def test_prefill_workspace_bytes():
+    # bf16 needs none; 8-bit: int32 tables [S][max_blocks], then K and V bf16 copies of
+    # S * ceil(max_seq_len / B) blocks, each part rounded up to 256 bytes
+    assert P.pkv_prefill_workspace_bytes(2, 2, 128, 16, 4, 64, P.PKV_BF16) == 0
+    up = lambda x: -(-x // 256) * 256
+    S, Hkv, d, B, mb, msl = 3, 2, 128, 16, 7, 100
+    copy = up(S * (-(-msl // B)) * Hkv * B * d * 2)
+    assert P.pkv_prefill_workspace_bytes(S, Hkv, d, B, mb, msl, P.PKV_FP8_E4M3) == up(S * mb * 4) + 2 * copy
+    assert P.pkv_prefill_workspace_bytes(0, Hkv, d, B, mb, msl, P.PKV_FP8_E4M3) == 0
 
 
 @pytest.mark.parametrize("args", [

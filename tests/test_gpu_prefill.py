@@ -72,6 +72,36 @@ def test_prefill_parity(case):
     run_prefill_case(wl)
 
 
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}-{c[1]}-{c[2]}x{c[3]}x{c[4]}")
+def test_prefill_parity_8bit_cache(case):
+    """The same batches over an 8-bit (E4M3) cache: the call dequantises the
+    blocks the sequences hold into a bf16 copy, then attends; compared with
+    exact attention over the dequantised cache (codes and scales bit-exact
+    with the oracle's pool)."""
+    contexts, chunks, Hq, Hkv, d = case
+    wl = workloads.fp8_cache(workloads.prefill_chunks(contexts, chunks, Hq, Hkv, d, seed=sum(chunks) + Hq + 1))
+    run_prefill_case(wl)
+
+
+@pytest.mark.parametrize("window", [16, 65, 200])
+def test_prefill_window_8bit_cache(window):
+    wl = workloads.fp8_cache(workloads.prefill_chunks([0, 90, 500], [150, 70, 129], 16, 4, 128, seed=window + 1))
+    run_prefill_case(wl, window=window)
+
+
+def test_prefill_bad_block_gives_nan_rows_8bit_cache():
+    need_gpu()
+    wl = workloads.fp8_cache(workloads.prefill_chunks([64, 64], [40, 40], 8, 2, 128, seed=12))
+    _, k, v = wl.tensors(device="cuda")
+    q = wl.prefill_queries(device="cuda")
+    eng, _, _ = run_gpu(wl, {0: k}, {0: v})
+    eng.tables[1, 2] = wl.num_blocks              # sequence 1 reads a block outside the pool
+    out = eng.prefill(0, q, [40, 40], max_seq_len=wl.max_len)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[40:].float()).all()
+    assert torch.isfinite(out[:40].float()).all()
+
+
 @pytest.mark.parametrize("window", [1, 16, 63, 64, 65, 200])
 def test_prefill_window(window):
     wl = workloads.prefill_chunks([0, 90, 500], [150, 70, 129], 16, 4, 128, seed=window)
@@ -126,7 +156,7 @@ def test_prefill_bad_block_gives_nan_rows():
     assert torch.isfinite(out[:40].float()).all()
 
 
-@pytest.mark.parametrize("name", ["prefill_prompts", "prefill_chunked"])
+@pytest.mark.parametrize("name", ["prefill_prompts", "prefill_chunked", "prefill_chunked_fp8"])
 def test_prefill_configs(name):
     """The measured prefill batches at full size: every query head of every
     sequence at the query positions around the kernel's boundaries — both

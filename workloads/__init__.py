@@ -347,6 +347,8 @@ CONFIGS = {
     "full_step_fp8": lambda seed=4, **kw: fp8_cache(full_step(seed, **kw)),
     "prefill_prompts": prefill_prompts,
     "prefill_chunked": prefill_chunked,
+    "prefill_prompts_fp8": lambda seed=12, **kw: fp8_cache(prefill_prompts(seed, **kw)),
+    "prefill_chunked_fp8": lambda seed=13, **kw: fp8_cache(prefill_chunked(seed, **kw)),
 }
 
 
