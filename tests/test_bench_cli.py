@@ -32,6 +32,8 @@ def _args(*argv):
     ("tiny", 20),
     ("prefill_prompts", 20),
     ("prefill_chunked", 20),
+    ("prefill_prompts_fp8", 20),
+    ("prefill_chunked_fp8", 20),
 ])
 def test_default_steps_per_workload(config, steps):
     wl = workloads.CONFIGS[config]()
