@@ -103,3 +103,22 @@ def test_prefill_flops_count():
     # sequence 0: queries at 3, 4 see 4 + 5 keys; sequence 1: 1 + 2 + 3 + 4
     assert wl.prefill_flops() == 4 * 8 * 2 * (4 + 5 + 1 + 2 + 3 + 4)
     assert wl.prefill_flops(window=2) == 4 * 8 * 2 * (2 + 2 + 1 + 2 + 2 + 2)
+
+
+def _torch_dequantized(x: torch.Tensor) -> torch.Tensor:
+    """fp64 copy of bf16 rows [..][d] as an 8-bit cache holds them, through
+    torch: per-row fp32 scale amax/448, codes by torch's E4M3 conversion."""
+    x32 = x.to(torch.float32)
+    s = x32.abs().amax(dim=-1, keepdim=True) / torch.tensor(448.0, dtype=torch.float32)
+    y = torch.where(s > 0, x32 / torch.where(s > 0, s, torch.ones_like(s)), torch.zeros_like(x32))
+    return y.to(torch.float8_e4m3fn).to(torch.float64) * s.to(torch.float64)
+
+
+@pytest.mark.parametrize("window", [0, 7])
+def test_prefill_over_8bit_cache_matches_brute_force(window):
+    """The prefill oracle over an 8-bit pool is exact attention over the
+    dequantised cache: brute force on K/V quantised by torch."""
+    wl = workloads.fp8_cache(workloads.prefill_chunks([0, 5, 19], [9, 12, 6], Hq=4, Hkv=2, d=64, seed=4))
+    rp, q, k, v, out = run_prefill(wl, window)
+    ref = brute(wl, q, _torch_dequantized(k), _torch_dequantized(v), window)
+    assert np.max(np.abs(out - ref)) <= 1e-13
