@@ -913,6 +913,8 @@ int pkv_paged_prefill(const pkv_prefill_args* a, void* stream) {
     sp.v_scale = a->v_scale;
     sp.block_tables = a->block_tables;
     sp.seq_lens = a->seq_lens;
+    sp.query_start = a->query_start;
+    sp.window = a->window;
     sp.S = a->num_seqs;
     sp.Hkv = a->num_kv_heads;
     sp.d = a->head_dim;

@@ -6,7 +6,9 @@
 // prefill over an 8-bit cache every block a sequence holds is first written
 // as bf16 (code × scale in fp32, rounded to nearest even) into a copy laid
 // out as a bf16 pool: copy block s * nb + j holds block j of sequence s.
-// Slots past a sequence's length become zeros.  A block id outside the pool
+// Slots past a sequence's length become zeros; with a sliding window, blocks
+// that lie wholly before the first query's window are skipped (the prefill
+// reads neither them nor their table entries).  A block id outside the pool
 // becomes -1 in the copy's table, so the prefill writes NaN rows wherever it
 // would have read that block, as it does on a bf16 cache.
 #include <hip/hip_runtime.h>
@@ -48,6 +50,10 @@ __global__ __launch_bounds__(256) void prefill_stage_kernel(PrefillStageParams p
   const int g = blockIdx.y;
   const int n = p.seq_lens[s];
   if (n < 1 || n > p.max_seq_len || j * kTok >= n) return;     // a block the prefill never reads
+  if (p.window > 0) {            // nor one wholly before the first query's window (its entry stays unwritten)
+    const int first = n - (p.query_start[s + 1] - p.query_start[s]);
+    if ((j + 1) * kTok <= first - p.window + 1) return;
+  }
   const int32_t b = p.block_tables[static_cast<size_t>(s) * p.max_blocks + j];
   const bool ok = b >= 0 && b < p.num_blocks;
   if (g == 0 && threadIdx.x == 0) p.tables_out[static_cast<size_t>(s) * p.max_blocks + j] = ok ? x : -1;

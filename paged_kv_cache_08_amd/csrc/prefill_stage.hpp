@@ -18,6 +18,8 @@ struct PrefillStageParams {
   const float* v_scale;
   const int32_t* block_tables;   // [S][max_blocks]
   const int32_t* seq_lens;       // [S]
+  const int32_t* query_start;    // [S + 1]: with a window, blocks before every query's window are skipped
+  int32_t window;                // > 0: sliding window of the prefill
   int32_t S, Hkv, d;
   int32_t num_blocks, max_blocks, max_seq_len;
   int32_t nb;                    // copy blocks per sequence: ceil(max_seq_len / B)
